@@ -1,0 +1,200 @@
+"""Pins of the whole-layer oracle: a dense SwiGLU MLP (one expert, top-1),
+a per-token pure-Python evaluation on tiny inputs, identical-expert and
+token-order invariances, and agreement of the full and per-token paths."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+
+def _bank(spec, seed, same=False):
+    rng = np.random.default_rng(seed)
+    n = spec.E + spec.n_shared
+    w13 = [O.bf16_round((rng.standard_normal((2 * spec.I, spec.D)) / np.sqrt(spec.D)).astype(np.float32))
+           for _ in range(n)]
+    w2 = [O.bf16_round((rng.standard_normal((spec.D, spec.I)) / np.sqrt(spec.I)).astype(np.float32))
+          for _ in range(n)]
+    if same:
+        w13 = [w13[0]] * n
+        w2 = [w2[0]] * n
+    return O.ExpertBank(spec, lambda e: (w13[e], w2[e])), w13, w2
+
+
+def _x(T, D, seed):
+    return O.bf16_round(np.random.default_rng(seed).standard_normal((T, D)).astype(np.float32))
+
+
+def _torch_dense_swiglu(x, w13, w2, I, fp8):
+    """Dense MLP in torch (CPU, float64), quantizing with torch's float8 cast
+    when fp8 is set: y = down(silu(gate(x)) * up(x))."""
+    def q(m):                                   # per-row fp8 through torch's encoder
+        amax = m.abs().amax(dim=1).to(torch.float32)
+        inv = torch.where(amax == 0, torch.ones_like(amax), torch.full_like(amax, 448.0) / amax)
+        sc = torch.where(amax == 0, torch.ones_like(amax), amax / torch.full_like(amax, 448.0))
+        codes = (m.to(torch.float32) * inv[:, None]).to(torch.float8_e4m3fn)
+        return codes.to(torch.float64) * sc.to(torch.float64)[:, None]
+    xt = torch.from_numpy(x).to(torch.float64)
+    W13 = torch.from_numpy(w13).to(torch.float64)
+    W2 = torch.from_numpy(w2).to(torch.float64)
+    if fp8:
+        xt, W13, W2 = q(xt), q(W13), q(W2)
+    g = xt @ W13[:I].T
+    u = xt @ W13[I:].T
+    act = (torch.nn.functional.silu(g) * u).to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    if fp8:
+        act = q(act)
+    o = (act @ W2.T).to(torch.float32)
+    if fp8:
+        o = o.to(torch.bfloat16).to(torch.float32)
+    return o.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+@pytest.mark.parametrize("quant", ["bf16", "ptpc_fp8"])
+def test_one_expert_top1_is_dense_swiglu(quant):
+    spec = O.LayerSpec(D=64, I=48, E=1, top_k=1, quant=quant)
+    bank, w13, w2 = _bank(spec, 1)
+    x = _x(37, 64, 2)
+    logits = np.zeros((37, 1), np.float32)
+    out = O.moe_forward(spec, bank, x, logits, block_m=8)
+    ref = _torch_dense_swiglu(x, w13[0], w2[0], 48, quant != "bf16")
+    # both sides round act and y to bf16; their float64 sums may differ in the
+    # last fp64 bits, which can flip a rare rounding: allow 1 bf16 step there
+    d = np.abs(out["y"] - ref)
+    step = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert np.all(d <= step * 1.01)
+    assert np.mean(d > 0) < 0.01
+    assert O.relative_l2(out["y"], ref) < 1e-3
+
+
+def test_one_expert_block_fp8_is_dense_mlp_with_block_quant():
+    spec = O.LayerSpec(D=256, I=128, E=1, top_k=1, quant="block128_fp8")
+    bank, w13, w2 = _bank(spec, 3)
+    x = _x(20, 256, 4)
+    out = O.moe_forward(spec, bank, x, np.zeros((20, 1), np.float32), block_m=4)
+    # same MLP written with independent torch block quantization
+    def qrow(m, g):
+        m = m.reshape(m.shape[0], -1, g)
+        amax = m.abs().amax(dim=2).to(torch.float32)
+        inv = torch.where(amax == 0, torch.ones_like(amax), torch.full_like(amax, 448.0) / amax)
+        sc = torch.where(amax == 0, torch.ones_like(amax), amax / torch.full_like(amax, 448.0))
+        c = (m.to(torch.float32) * inv[..., None]).to(torch.float8_e4m3fn).to(torch.float64)
+        return (c * sc.to(torch.float64)[..., None]).reshape(m.shape[0], -1)
+    def qblk(w):
+        N, K = w.shape
+        t = w.reshape(N // 128, 128, K // 128, 128).permute(0, 2, 1, 3).reshape(-1, 128 * 128)
+        d = qrow(t, 128 * 128)
+        return d.reshape(N // 128, K // 128, 128, 128).permute(0, 2, 1, 3).reshape(N, K)
+    xt = qrow(torch.from_numpy(x), 128)
+    W13 = qblk(torch.from_numpy(w13[0]))
+    W2 = qblk(torch.from_numpy(w2[0]))
+    h = xt @ W13.T
+    act = (torch.nn.functional.silu(h[:, :128]) * h[:, 128:]).to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    o = (qrow(act, 128) @ W2.T).to(torch.float32).to(torch.bfloat16)
+    ref = o.to(torch.float32).numpy()
+    assert O.relative_l2(out["y"], ref) < 1e-3
+
+
+def _py_layer(spec, x, logits, w13, w2, sel_bias=None):
+    """Per-token evaluation with Python loops over d and i (tiny shapes),
+    straight from the layer's definition, no permutation involved."""
+    T = x.shape[0]
+    ids, w = (O.route_softmax_topk(logits, spec.top_k) if spec.scoring == "softmax" else
+              O.route_sigmoid_grouped(logits, spec.top_k, spec.n_groups, spec.topk_groups,
+                                      sel_bias, spec.route_scale))
+    y = np.zeros((T, spec.D), np.float32)
+    for t in range(T):
+        acc = [0.0] * spec.D
+        experts = [(int(e), float(wt)) for e, wt in zip(ids[t], w[t])]
+        if spec.n_shared:
+            experts.append((spec.E, 1.0))
+        for e, wt in experts:
+            act = []
+            for i in range(spec.I):
+                g = sum(float(x[t, d]) * float(w13[e][i, d]) for d in range(spec.D))
+                u = sum(float(x[t, d]) * float(w13[e][spec.I + i, d]) for d in range(spec.D))
+                act.append(float(O.bf16_round(np.float32(g / (1.0 + np.exp(-g)) * u))))
+            for d in range(spec.D):
+                o = float(np.float32(sum(act[i] * float(w2[e][d, i]) for i in range(spec.I))))
+                acc[d] += wt * o
+        y[t] = O.bf16_round(np.array(acc, np.float32))
+    return y
+
+
+def test_tiny_layer_vs_python_loops_softmax():
+    spec = O.LayerSpec(D=12, I=6, E=5, top_k=2)
+    bank, w13, w2 = _bank(spec, 5)
+    x = _x(9, 12, 6)
+    logits = np.random.default_rng(7).standard_normal((9, 5)).astype(np.float32)
+    out = O.moe_forward(spec, bank, x, logits, block_m=4)
+    ref = _py_layer(spec, x, logits, w13, w2)
+    assert O.relative_l2(out["y"], ref) < 1e-6
+
+
+def test_tiny_layer_vs_python_loops_grouped_shared():
+    spec = O.LayerSpec(D=10, I=4, E=8, top_k=3, n_shared=1, scoring="sigmoid_grouped",
+                       n_groups=4, topk_groups=2, route_scale=2.5)
+    bank, w13, w2 = _bank(spec, 8)
+    x = _x(11, 10, 9)
+    logits = np.random.default_rng(10).standard_normal((11, 8)).astype(np.float32)
+    bias = np.random.default_rng(11).standard_normal(8).astype(np.float32) * 0.1
+    out = O.moe_forward(spec, bank, x, logits, sel_bias=bias, block_m=2)
+    ref = _py_layer(spec, x, logits, w13, w2, bias)
+    assert O.relative_l2(out["y"], ref) < 1e-6
+
+
+@pytest.mark.parametrize("quant", ["bf16", "ptpc_fp8"])
+def test_identical_experts_give_dense_mlp(quant):
+    spec = O.LayerSpec(D=128, I=64, E=8, top_k=3, quant=quant)
+    bank, w13, w2 = _bank(spec, 12, same=True)
+    x = _x(30, 128, 13)
+    logits = np.random.default_rng(14).standard_normal((30, 8)).astype(np.float32)
+    out = O.moe_forward(spec, bank, x, logits, block_m=4)
+    one = O.LayerSpec(D=128, I=64, E=1, top_k=1, quant=quant)
+    dense = O.moe_forward(one, O.ExpertBank(one, lambda e: (w13[0], w2[0])), x,
+                          np.zeros((30, 1), np.float32), block_m=4)
+    # sum_j w_j = 1, so y = bf16(o) up to the fp32 weight sum and a rounding
+    assert O.relative_l2(out["y"], dense["y"]) < 3e-3
+
+
+def test_token_order_permutation_is_bitwise():
+    spec = O.LayerSpec(D=64, I=32, E=16, top_k=4, n_shared=1, scoring="sigmoid_grouped",
+                       n_groups=4, topk_groups=2, route_scale=2.5, quant="ptpc_fp8")
+    bank, _, _ = _bank(spec, 15)
+    x = _x(40, 64, 16)
+    logits = np.random.default_rng(17).standard_normal((40, 16)).astype(np.float32)
+    perm = np.random.default_rng(18).permutation(40)
+    a = O.moe_forward(spec, bank, x, logits, block_m=8)
+    b = O.moe_forward(spec, bank, x[perm], logits[perm], block_m=8)
+    assert np.array_equal(a["y"][perm].view(np.uint32), b["y"].view(np.uint32))
+
+
+@pytest.mark.parametrize("quant,block_m", [("bf16", 4), ("ptpc_fp8", 16), ("block128_fp8", 8)])
+def test_full_path_equals_per_token_path(quant, block_m):
+    spec = O.LayerSpec(D=256, I=128, E=6, top_k=2, n_shared=1 if quant == "block128_fp8" else 0,
+                       quant=quant)
+    bank, _, _ = _bank(spec, 19)
+    x = _x(25, 256, 20)
+    x[3] = 0.0
+    logits = np.random.default_rng(21).standard_normal((25, 6)).astype(np.float32)
+    a = O.moe_forward(spec, bank, x, logits, block_m=block_m)
+    b = O.moe_forward_tokens(spec, bank, x, logits)
+    assert np.array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32))
+    assert np.array_equal(a["ids"], b["ids"])
+
+
+def test_block_m_does_not_change_y():
+    spec = O.LayerSpec(D=128, I=64, E=8, top_k=2, quant="ptpc_fp8")
+    bank, _, _ = _bank(spec, 22)
+    x = _x(33, 128, 23)
+    logits = np.random.default_rng(24).standard_normal((33, 8)).astype(np.float32)
+    ys = [O.moe_forward(spec, bank, x, logits, block_m=b)["y"] for b in (1, 16, 64)]
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+
+
+def test_empty_batch():
+    spec = O.LayerSpec(D=128, I=64, E=8, top_k=2, quant="ptpc_fp8")
+    bank, _, _ = _bank(spec, 25)
+    out = O.moe_forward(spec, bank, np.zeros((0, 128), np.float32), np.zeros((0, 8), np.float32))
+    assert out["y"].shape == (0, 128)
