@@ -1,0 +1,272 @@
+"""Benchmark of the fused MoE layer forward on one MI355X.
+
+One step = one pass of the whole routed-expert path over one batch of
+synthetic input, resident in HBM: top-k routing -> permutation -> x
+quantization -> gate/up grouped GEMM with SwiGLU -> act quantization -> down
+grouped GEMM -> weighted combine (plus the router projection when the
+workload has one).  The timed loop calls the C-ABI step entries in the order
+moe_forward runs them, with HIP events around the two grouped GEMMs (the
+dominant kernels); the fused moe_forward entry is timed too as a cross-check.
+
+Prints ONE JSON line.  Default workload: the Qwen3-235B-A22B-shaped prefill
+layer (T=8192, D=4096, E=128, top-8, I=1536, PTPC-FP8).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer TFLOP/s (prefill) and expert-weight GB/s (decode), % of roofline"
+PEAK_TFLOPS = {"ptpc_fp8": 5000.0, "block128_fp8": 5000.0, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Steps:
+    """The path through the step entries, on buffers carved from the layer's
+    workspace (the same layout moe_forward uses)."""
+
+    def __init__(self, layer, w, x, logits, block_m):
+        import torch
+        from moe_layer_router_amd import _lib as L
+        self.L, self.lib, self.layer, self.w = L, L.lib(), layer, w
+        self.x, self.logits = x, logits
+        self.T = w.T
+        self.lay = layer.layout(w.T, block_m)
+        self.B = self.lay["block_m"]
+        self.ws = layer.workspace(w.T, block_m)
+        self.y = torch.empty((w.T, w.D), dtype=torch.bfloat16, device=x.device)
+        base = self.ws.data_ptr()
+        self.p = {k: (base + v if isinstance(v, int) and v >= 0 else None) for k, v in self.lay.items()}
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def run(self, ev=None):
+        L, lib, w, p, s = self.L, self.lib, self.w, self.p, self.stream
+        d = ctypes.byref(self.layer.desc)
+        fp8 = w.quant != "bf16"
+        group = 128 if w.quant == "block128_fp8" else 0
+        Ep = w.E + w.n_shared
+        lg = self.logits.data_ptr() if self.logits is not None else p["logits"]
+        if self.logits is None:
+            L.check("router", lib.moe_router_logits(self.x.data_ptr(), self.layer.weights.router_w.data_ptr(),
+                                                    self.T, w.D, w.E, lg, s))
+        sc = 0 if w.scoring == "softmax" else 1
+        L.check("route", lib.moe_route_topk(lg, self.T, w.E, w.k, sc, w.n_groups, w.topk_groups, None, 1,
+                                            w.route_scale, p["topk_ids"], p["topk_w"], s))
+        L.check("permute", lib.moe_permute_align(p["topk_ids"], self.T, w.k, w.E, w.n_shared, self.B, p["counts"],
+                                                 p["offsets"], p["sorted_ids"], p["block_expert"], p["inv_perm"],
+                                                 p["scratch"], s))
+        a, a_s = self.x.data_ptr(), None
+        if fp8:
+            L.check("quant x", lib.moe_quant_ptpc_fp8(self.x.data_ptr(), self.T, w.D, group, None, p["xq"], p["xs"], s))
+            a, a_s = p["xq"], p["xs"]
+        if ev is not None:
+            ev[0].record()
+        L.check("gateup", lib.moe_grouped_gemm_gateup_silu(d, a, a_s, self.T, self.B, p["sorted_ids"],
+                                                           p["block_expert"], p["offsets"], p["act"], s))
+        if ev is not None:
+            ev[1].record()
+        act, act_s = p["act"], None
+        if fp8:
+            L.check("quant act", lib.moe_quant_ptpc_fp8(p["act"], self.lay["max_rows"], w.I, group,
+                                                        p["offsets"] + 4 * Ep, p["aq"], p["as_"], s))
+            act, act_s = p["aq"], p["as_"]
+        if ev is not None:
+            ev[2].record()
+        L.check("down", lib.moe_grouped_gemm_down(d, act, act_s, self.T, self.B, p["block_expert"], p["offsets"],
+                                                  p["out_perm"], s))
+        if ev is not None:
+            ev[3].record()
+        L.check("combine", lib.moe_unpermute_combine(p["out_perm"], 1 if fp8 else 0, p["inv_perm"], p["topk_w"],
+                                                     self.T, w.k, w.n_shared, w.D, self.y.data_ptr(), s))
+
+
+def active_expert_bytes(w, ids_np):
+    """Weight bytes of the experts the batch routes to (codes + scales)."""
+    import numpy as np
+    used = len(np.unique(ids_np)) + w.n_shared
+    elem = 2 if w.quant == "bf16" else 1
+    per = 3 * w.I * w.D * elem
+    if w.quant == "ptpc_fp8":
+        per += 4 * (2 * w.I + w.D)
+    elif w.quant == "block128_fp8":
+        per += 4 * 3 * (w.I // 128) * (w.D // 128)
+    return used * per, used
+
+
+def time_decode(torch, mlr, synth, steps, warmup):
+    """Decode layer (T=32, Zipf-skewed routing): full forward, weights rotated
+    over copies so each step streams its experts from HBM."""
+    from tests.gpu_cases import build_case
+    w = synth.get("qwen3_235b_decode_ptpc")
+    c = build_case(w)
+    ncopy = 4
+    layers = [c.layer]
+    for _ in range(ncopy - 1):
+        wt = c.layer.weights
+        lw = mlr.LayerWeights(wt.w13.clone(), wt.w2.clone(), wt.w13_scale.clone(), wt.w2_scale.clone())
+        layers.append(mlr.MoELayer(D=w.D, I=w.I, E=w.E, top_k=w.k, weights=lw, quant=w.quant))
+    y = torch.empty((w.T, w.D), dtype=torch.bfloat16, device="cuda")
+    ws = layers[0].workspace(w.T)
+    for i in range(warmup):
+        layers[i % ncopy].forward(c.x, c.logits, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        layers[i % ncopy].forward(c.x, c.logits, y=y, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ids = layers[0].intermediates(w.T, 0, ws)["topk_ids"].cpu().numpy()
+    nbytes, used = active_expert_bytes(w, ids)
+    return dict(workload=w.name, us_per_step=round(ms * 1e3, 2), active_experts=int(used),
+                expert_weight_bytes=int(nbytes), GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+
+
+def cpu_baseline(case, y_gpu, tokens):
+    """The oracle as it stands, on the first `tokens` tokens of the workload
+    (routing, quantization of x and of the weights of every expert those
+    tokens use, expert GEMMs, combine), timed on this host's cores.  Its
+    output also gates the GPU number: the same tokens must match."""
+    import numpy as np
+    import oracle as O
+    from tests.gpu_cases import rel_l2, tol_of
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    w = case.w
+    x = case.x_np()[:tokens]
+    lg = case.logits_np()
+    rw = None if case.router_w is None else case.router_w.cpu().numpy()
+    lg = lg[:tokens] if lg is not None else None
+    bank = O.ExpertBank(case.spec, case.bank.master, cache=False)
+    t0 = time.perf_counter()
+    ref = O.moe_forward(case.spec, bank, x, lg, router_w=rw, block_m=16)
+    dt = time.perf_counter() - t0
+    flops = w.replace(T=tokens).flops()
+    err = rel_l2(y_gpu[:tokens].float().cpu().numpy(), ref["y"])
+    ok = err <= tol_of(w.quant)
+    used = len(np.unique(ref["ids"])) + w.n_shared
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"first {tokens} tokens of the {w.T}-token workload ({used} experts: the oracle "
+                       f"quantizes their weights, routes, runs the expert GEMMs in float64 and combines); "
+                       f"{dt:.1f} s", seconds=round(dt, 2)), ok, err
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_235b_prefill_ptpc")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (the layer holds every expert on one MI355X); "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_layer_router_amd as mlr
+    import synth
+    from tests.gpu_cases import build_case
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mlr.lib()
+    w = synth.get(args.workload)
+    log("building", w.name)
+    case = build_case(w)
+    st = Steps(case.layer, w, case.x, case.logits, args.block_m)
+    log("block_m", st.B, "max_rows", st.lay["max_rows"])
+
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        st.run(ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    gu_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    dn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    log(f"step {ms:.3f} ms  gate_up {gu_ms:.3f} ms  down {dn_ms:.3f} ms")
+
+    # the fused entry on the same inputs
+    y_fused = case.layer.forward(case.x, case.logits, block_m=args.block_m)
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.steps):
+        case.layer.forward(case.x, case.logits, block_m=args.block_m, y=y_fused)
+    f1.record()
+    torch.cuda.synchronize()
+    fused_ms = f0.elapsed_time(f1) / args.steps
+    same = bool(torch.equal(y_fused.view(torch.int16), st.y.view(torch.int16)))
+
+    rows = w.T * (w.k + w.n_shared)
+    flops = w.flops()
+    gu_flops = 2.0 * rows * 2 * w.I * w.D
+    dn_flops = 2.0 * rows * w.D * w.I
+    peak = PEAK_TFLOPS[w.quant]
+    tflops = flops / (ms * 1e-3) / 1e12
+    gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3" if w.quant != "bf16" else "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "top_k": w.k, "I": w.I,
+                   "n_shared": w.n_shared, "quant": w.quant, "scoring": w.scoring, "block_m": st.B},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_gateup_silu", "achieved": round(gu_tf, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(gu_tf / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(gu_ms, 4), "flops_per_launch": gu_flops},
+        "kernels": {"gateup_ms": round(gu_ms, 4), "down_ms": round(dn_ms, 4),
+                    "down_tflops": round(dn_flops / (dn_ms * 1e-3) / 1e12, 1),
+                    "gemms_frac_of_peak": round((gu_flops + dn_flops) / ((gu_ms + dn_ms) * 1e-3) / 1e12 / peak, 4),
+                    "rest_ms": round(ms - gu_ms - dn_ms, 4)},
+        "fused_ms_per_step": round(fused_ms, 4), "fused_equals_steps": same,
+        "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+    }
+    if not args.no_decode and w.name != "qwen3_235b_decode_ptpc":
+        log("decode leg")
+        out["decode"] = time_decode(torch, mlr, synth, max(args.steps, 20), args.warmup)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on", args.cpu_tokens, "tokens")
+        cb, ok, err = cpu_baseline(case, st.y, args.cpu_tokens)
+        out["cpu_baseline"] = cb
+        out["parity_sampled_rel_l2"] = err
+        if not ok:
+            log(f"PARITY FAILED on the sampled tokens: rel_l2 {err:.3e}")
+            out["value"] = None
+            print(json.dumps(out), flush=True)
+            sys.exit(1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

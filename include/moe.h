@@ -1,0 +1,269 @@
+/*
+ * moe.h -- C ABI of the fused Mixture-of-Experts layer forward for one
+ * AMD Instinct MI355X (gfx950) that holds every expert.
+ *
+ * The layer (pages it follows):
+ *   - "Systems engineering playbook: optimizing Qwen 3.5 397B MoE on Ironwood
+ *     TPU7x" (Google Developers Blog): a router gate scores each token against
+ *     the routed experts and keeps the top-k of a soft-max distribution, plus
+ *     one always-executed shared expert (model description, MoE paragraph);
+ *     routing metadata is a [tokens, k] array of expert ids and one of top-k
+ *     weights (expert-parallel routing item); token rows are gathered into a
+ *     contiguous per-expert buffer (SparseCore permutation item); a grouped
+ *     GEMM packs gate and up projections in one tile with SwiGLU fused and
+ *     processes each expert's variable token count in bounded slices (GMM V2
+ *     item); expert outputs are gathered back and reduced per token
+ *     (SparseCore unpermutation item).
+ *   - "Unleashing Computational Power: Ultimate Latency Optimization of Qwen3
+ *     and Qwen3-VL on AMD MI300X Series" (LMSYS blog), 2.1.1 "GEMM
+ *     Quantization Strategy", Figure 3: PTPC-FP8, a dynamic scale per token
+ *     for activations and a static scale per output channel for weights.
+ *   - "Win on TCO: How AMD Instinct MI355X Achieves Cost-Competitive
+ *     Distributed Inference Through SGLang with MoRI", "Hybrid FP4/FP8
+ *     quantized all-to-all": FP8 blockwise quantization with one fp32 scale
+ *     per 128 elements (used here for 1x128 activation groups and 128x128
+ *     weight blocks of the DeepSeek-R1-shaped layer, hidden 7168, top-8).
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless stated; the caller allocates and
+ *     owns every buffer and keeps it alive until the stream work completes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued asynchronously on it; no entry point allocates,
+ *     frees, synchronizes, or reads device memory from the host, so every
+ *     call can be captured in a HIP graph.
+ *   - Matrices are row-major.  GEMM operands are "NT": both the activation
+ *     rows and the weight rows are contiguous along the reduction dimension.
+ *   - bf16 data is passed as uint16 bit patterns (void*), FP8 as OCP e4m3fn
+ *     codes (uint8).  e4m3fn conversion rounds to nearest even, keeps
+ *     subnormals and the sign of zero, and saturates to +-448.
+ *   - Return value: a moe_status code.  Arguments are validated on the host
+ *     before anything is enqueued: an invalid call enqueues nothing.
+ *     MOE_ERR_HIP reports a launch failure (hipGetLastError after launch).
+ *     T = 0 (no tokens) is valid and enqueues nothing.
+ *   - The library keeps no state between calls and is thread-safe.
+ */
+#ifndef MOE_LAYER_ROUTER_AMD_MOE_H
+#define MOE_LAYER_ROUTER_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG  1  /* NULL pointer, non-positive size, k > E ... */
+#define MOE_ERR_UNSUPPORTED  2  /* valid but outside what the kernels cover  */
+#define MOE_ERR_WORKSPACE    3  /* workspace smaller than required          */
+#define MOE_ERR_HIP          4  /* a HIP launch reported an error            */
+
+/* router scoring */
+#define MOE_SCORING_SOFTMAX          0  /* soft-max over the logits, top-k        */
+#define MOE_SCORING_SIGMOID_GROUPED  1  /* sigmoid, group-limited top-k           */
+
+/* expert arithmetic */
+#define MOE_QUANT_NONE_BF16     0  /* bf16 operands, fp32 accumulate            */
+#define MOE_QUANT_PTPC_FP8      1  /* e4m3 per-token x per-output-channel       */
+#define MOE_QUANT_BLOCK128_FP8  2  /* e4m3 1x128 activations, 128x128 weights   */
+
+/* Limits of this build (MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS   1024  /* E + n_shared                                 */
+#define MOE_MAX_TOPK        16
+#define MOE_MAX_GROUPS      32
+#define MOE_MAX_ROUTER_D 16384  /* D of the router projection                  */
+
+/*
+ * Layer description (a host struct; its pointers are device pointers).
+ *   D hidden size, I expert intermediate size, E routed experts, top_k,
+ *   n_shared in {0,1}: the shared expert is expert index E, applied to every
+ *   token with weight 1 (not scaled by route_scale).
+ *   w13: [E+n_shared, 2I, D] -- rows 0..I-1 the gate projection, rows I..2I-1
+ *        the up projection of each expert; bf16 (quant 0) or e4m3 codes.
+ *   w13_scale: quant 1: [E+n_shared, 2I] fp32 per output channel;
+ *              quant 2: [E+n_shared, 2I/128, D/128] fp32 per 128x128 block;
+ *              quant 0: NULL.
+ *   w2: [E+n_shared, D, I]; w2_scale: [E+n_shared, D] or [.., D/128, I/128].
+ *   router_w: [E, D] fp32 router gate, used by moe_forward when it is given
+ *             no logits (may be NULL otherwise).
+ *   sel_bias: [E] fp32 selection-only bias of grouped-sigmoid routing or NULL.
+ */
+typedef struct moe_layer_desc {
+    int32_t D, I, E, top_k, n_shared;
+    int32_t scoring, n_groups, topk_groups, renormalize;
+    float route_scale;
+    int32_t quant;
+    const void* w13;
+    const float* w13_scale;
+    const void* w2;
+    const float* w2_scale;
+    const float* router_w;
+    const float* sel_bias;
+} moe_layer_desc;
+
+/* Byte offsets of the intermediates moe_forward keeps in its workspace
+ * (host struct; -1 when a buffer is not used by the layer's mode). */
+typedef struct moe_ws_layout {
+    int64_t logits, topk_ids, topk_w, counts, offsets, sorted_ids, block_expert,
+            inv_perm, xq, xs, act, aq, as, out_perm, scratch, total;
+    int64_t max_rows;   /* moe_permute_max_rows of the layer                 */
+    int32_t block_m;    /* the block_m the layout was computed for            */
+} moe_ws_layout;
+
+/* Text of a status code (static string, never NULL). */
+const char* moe_status_str(int32_t status);
+
+/*
+ * Router projection: logits[t, e] = sum_d x[t, d] * router_w[e, d]
+ * (router gate of the Qwen 3.5 MoE paragraph).  x: [T, D] bf16,
+ * router_w: [E, D] fp32, logits: [T, E] fp32.  Products and sums are formed
+ * in fp64 and rounded once to fp32.  D <= MOE_MAX_ROUTER_D.
+ */
+int32_t moe_router_logits(const void* x_bf16, const float* router_w, int32_t T, int32_t D,
+                          int32_t E, float* logits, void* stream);
+
+/*
+ * Top-k routing (router gate + top-k of the Qwen 3.5 MoE paragraph; the
+ * grouped-sigmoid form is the DeepSeek-R1 layer's).  logits: [T, E] fp32,
+ * finite.  Outputs topk_ids [T, k] int32 and topk_w [T, k] fp32, each row in
+ * descending key order, ties to the lower expert index (+0 == -0).
+ *   scoring 0: key = logit.  renormalize != 0: w = soft-max over the k
+ *     selected logits; else w = the full soft-max probability.  n_groups,
+ *     topk_groups, sel_bias, route_scale are ignored (pass 1, 1, NULL, 1).
+ *   scoring 1: s = sigmoid(logit) (fp32); key = s + sel_bias[e] (NULL = 0);
+ *     group score = sum of the two largest keys of each of n_groups equal
+ *     groups; only the topk_groups best groups are eligible (ties to the
+ *     lower group); w = s / sum(s of the picks) * route_scale (renormalize)
+ *     or s * route_scale.
+ * Weights are formed in fp64 and rounded once to fp32.
+ * Limits: 1 <= k <= MOE_MAX_TOPK, k <= E <= MOE_MAX_EXPERTS, E % n_groups ==
+ * 0, n_groups <= MOE_MAX_GROUPS, 1 <= topk_groups <= n_groups, and k not
+ * above the experts of the eligible groups.
+ */
+int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t scoring,
+                       int32_t n_groups, int32_t topk_groups, const float* sel_bias,
+                       int32_t renormalize, float route_scale, int32_t* topk_ids, float* topk_w,
+                       void* stream);
+
+/*
+ * Host-only: rows of the padded permuted buffer, an upper bound valid for any
+ * routing: block_m * min(floor((A' + E'(block_m-1)) / block_m), A') with
+ * A' = T(k + n_shared), E' = E + n_shared.  Returns -1 on invalid input.
+ */
+int64_t moe_permute_max_rows(int32_t T, int32_t k, int32_t E, int32_t n_shared, int32_t block_m);
+
+/*
+ * Stable permutation of the routed rows by expert (SparseCore permutation and
+ * GMM V2 bounded slices of the Qwen 3.5 page).  Routed row (t, j) has flat
+ * index t*k + j; with n_shared = 1 the shared-expert rows are expert E with
+ * flat index T*k + t.  Within an expert rows keep ascending flat order; each
+ * expert's segment is padded to a multiple of block_m with the sentinel
+ * T*(k + n_shared).
+ * Outputs (sizes with E' = E + n_shared, R = moe_permute_max_rows(...)):
+ *   expert_counts [E'], expert_offsets [E'+1] (padded exclusive prefix; the
+ *   last entry is the padded total), sorted_ids [R] (flat indices; sentinel
+ *   in pads and past the total), block_expert [R / block_m] (expert of each
+ *   block, -1 past the total), inv_perm [T*(k+n_shared)] (flat -> row).
+ * Ids outside [0, E) get no row (inv_perm = -1).  block_m in [1, 1024].
+ * `scratch` is device memory of moe_permute_scratch_bytes(T, k, n_shared, E)
+ * bytes (contents need not be initialised).
+ */
+size_t moe_permute_scratch_bytes(int32_t T, int32_t k, int32_t n_shared, int32_t E);
+int32_t moe_permute_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                          int32_t n_shared, int32_t block_m, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* sorted_ids, int32_t* block_expert,
+                          int32_t* inv_perm, void* scratch, void* stream);
+
+/*
+ * PTPC / 1x128 FP8 quantization of bf16 rows (PTPC-FP8 of the Qwen3 MI300X
+ * page, 2.1.1; the 1x128 blockwise form of the MI355X MoRI page).
+ * x: [M, K] bf16.  group 0: one scale per row; group 128: one scale per 128
+ * consecutive elements (K % 128 == 0).  For each group:
+ *   amax = max|x|; scale = amax / 448; q = e4m3(x * (448 / amax)),
+ * both divisions IEEE fp32, one fp32 multiply; amax = 0 gives scale 1.
+ * Outputs q [M, K] uint8 and scale [M] or [M, K/128] fp32.
+ * valid_rows: device int32 scalar or NULL; rows >= *valid_rows are left
+ * untouched (used for the data-dependent row count of the permuted buffer).
+ * Limits: K % 8 == 0, K <= 65536.
+ */
+int32_t moe_quant_ptpc_fp8(const void* x_bf16, int64_t M, int32_t K, int32_t group,
+                           const int32_t* valid_rows, uint8_t* q, float* scale, void* stream);
+
+/*
+ * Offline FP8 quantization of bf16 weights [n_mats, N, K] (row n of a matrix
+ * is output channel n).  quant 1 (PTPC): one scale per row, scale
+ * [n_mats, N]; quant 2: one scale per 128x128 block, scale
+ * [n_mats, N/128, K/128] (N, K multiples of 128).  Same arithmetic as
+ * moe_quant_ptpc_fp8.
+ */
+int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int32_t K,
+                             int32_t quant, uint8_t* q, float* scale, void* stream);
+
+/*
+ * Grouped GEMM gate/up with fused SwiGLU (GMM V2 item of the Qwen 3.5 page).
+ * For every valid row r of the permuted buffer, with e = block_expert[r/block_m]
+ * and token t of sorted_ids[r] (t = f / k for f < T*k, else f - T*k):
+ *   [g | u] = A[t] . W13[e]^T (fp32 accumulate, dequantized by the row's
+ *   activation scale and the weight scales), act[r] = bf16(silu(g) * u).
+ * a: quant 0: x bf16 [T, D]; quant 1/2: codes [T, D] with a_scale [T] or
+ * [T, D/128].  act: [R, I] bf16 where R = moe_permute_max_rows(...).
+ * Pad rows (sentinel) get act = 0; rows at or past expert_offsets[E'] are not
+ * written.  block_m must be one of 16, 32, 64, 128 for this entry and
+ * moe_grouped_gemm_down, and equal to the block_m of moe_permute_align.
+ * I % 64 == 0 and D % 128 == 0 (FP8) or D % 64 == 0 (bf16).
+ */
+int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
+                                     const float* a_scale, int32_t T, int32_t block_m,
+                                     const int32_t* sorted_ids, const int32_t* block_expert,
+                                     const int32_t* expert_offsets, void* act_bf16,
+                                     void* stream);
+
+/*
+ * Grouped GEMM down: out_perm[r] = act[r] . W2[e]^T for the valid rows
+ * (dequantized by the row scale(s) and the weight scales).  act: quant 0:
+ * bf16 [R, I]; quant 1/2: codes [R, I] with act_scale [R] or [R, I/128].
+ * out_perm [R, D]: fp32 for quant 0, bf16 for quant 1/2.
+ */
+int32_t moe_grouped_gemm_down(const moe_layer_desc* L, const void* act, const float* act_scale,
+                              int32_t T, int32_t block_m, const int32_t* block_expert,
+                              const int32_t* expert_offsets, void* out_perm, void* stream);
+
+/*
+ * Unpermute and weighted combine (SparseCore unpermutation item of the
+ * Qwen 3.5 page): y[t] = bf16( sum_{j<k} w[t,j] * out_perm[inv_perm[t*k+j]]
+ * + out_perm[inv_perm[T*k+t]] (shared, when n_shared = 1) ), accumulated in
+ * fp32 in that order.  out_dtype 0: out_perm fp32; 1: bf16.  Rows with
+ * inv_perm = -1 contribute nothing.  y: [T, D] bf16.
+ */
+int32_t moe_unpermute_combine(const void* out_perm, int32_t out_dtype, const int32_t* inv_perm,
+                              const float* topk_w, int32_t T, int32_t k, int32_t n_shared,
+                              int32_t D, void* y_bf16, void* stream);
+
+/*
+ * block_m that moe_forward uses for block_m = 0 (chosen from T and the layer).
+ */
+int32_t moe_default_block_m(const moe_layer_desc* L, int32_t T);
+
+/* Workspace bytes of moe_forward and where each intermediate lives in it. */
+size_t moe_forward_workspace_size(const moe_layer_desc* L, int32_t T, int32_t block_m);
+int32_t moe_workspace_layout(const moe_layer_desc* L, int32_t T, int32_t block_m,
+                             moe_ws_layout* out);
+
+/*
+ * The whole layer: [router projection when logits == NULL] -> top-k ->
+ * permute -> [quantize x] -> gate/up + SwiGLU -> [quantize act] -> down ->
+ * combine.  x: [T, D] bf16; logits: [T, E] fp32 or NULL (then L->router_w is
+ * required); y: [T, D] bf16.  block_m 0 picks moe_default_block_m.  The
+ * workspace (>= moe_forward_workspace_size bytes, 256-byte aligned) holds
+ * every intermediate at the offsets of moe_workspace_layout.
+ */
+int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* logits_or_null,
+                    int32_t T, int32_t block_m, void* y_bf16, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_ROUTER_AMD_MOE_H */

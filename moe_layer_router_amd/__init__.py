@@ -1,0 +1,9 @@
+"""Fused Mixture-of-Experts layer forward for AMD Instinct MI355X (gfx950).
+
+Every step runs in the hand-written HIP kernels of ``libmoe.so`` behind the C
+ABI in ``include/moe.h``; this package only marshals torch tensors to it.
+"""
+
+from ._lib import MoEError, lib  # noqa: F401
+from .ops import (LayerWeights, MoELayer, permute_align, permute_max_rows,  # noqa: F401
+                  quant_ptpc_fp8, quant_weight_fp8, route_topk, router_logits, unpermute_combine)

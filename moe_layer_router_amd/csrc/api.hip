@@ -1,0 +1,343 @@
+// C ABI: argument validation, workspace carving and the fused forward.
+// Every check runs on the host before anything is enqueued.
+#include "common.h"
+
+namespace moe {
+int32_t route_topk_launch(const float* logits, int T, int E, int k, int scoring, int n_groups, int topk_groups,
+                          const float* sel_bias, int renormalize, float route_scale, int* ids, float* w,
+                          hipStream_t s);
+int32_t router_logits_launch(const uint16_t* x, const float* wr, int T, int D, int E, float* logits,
+                             hipStream_t s);
+size_t permute_scratch_bytes(int T, int k, int n_shared, int E);
+int32_t permute_align_launch(const int* ids, int T, int k, int E, int n_shared, int block_m, int max_rows,
+                             int* counts, int* offsets, int* sorted_ids, int* block_expert, int* inv_perm,
+                             void* scratch, hipStream_t s);
+int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const int* valid_rows, uint8_t* q,
+                          float* scale, hipStream_t s);
+int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, uint8_t* q, float* scale,
+                            hipStream_t s);
+int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T, int block_m,
+                           int64_t max_rows, const int* sorted_ids, const int* block_expert, void* act,
+                           hipStream_t s);
+int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int block_m,
+                         int64_t max_rows, const int* block_expert, void* out_perm, hipStream_t s);
+int32_t combine_launch(const void* out_perm, int out_dtype, const int* inv_perm, const float* topk_w, int T,
+                       int k, int n_shared, int D, uint16_t* y, hipStream_t s);
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int64_t max_rows_of(int64_t T, int64_t k, int64_t E, int64_t n_sh, int64_t B) {
+    const int64_t A = T * (k + n_sh);
+    const int64_t Ep = E + n_sh;
+    int64_t blocks = (A + Ep * (B - 1)) / B;
+    if (blocks > A) blocks = A;
+    return blocks * B;
+}
+
+bool block_m_ok(int quant, int block_m) {
+    if (block_m == 32 || block_m == 64) return true;
+    return block_m == 128 && quant != MOE_QUANT_BLOCK128_FP8;
+}
+
+int32_t check_routing(int E, int k, int scoring, int n_groups, int topk_groups) {
+    MOE_CHECK_ARG(E > 0 && k > 0 && k <= E);
+    MOE_CHECK_ARG(scoring == MOE_SCORING_SOFTMAX || scoring == MOE_SCORING_SIGMOID_GROUPED);
+    MOE_CHECK_SUP(k <= MOE_MAX_TOPK && E <= MOE_MAX_EXPERTS);
+    if (scoring == MOE_SCORING_SIGMOID_GROUPED) {
+        MOE_CHECK_ARG(n_groups > 0 && E % n_groups == 0 && topk_groups > 0 && topk_groups <= n_groups);
+        MOE_CHECK_ARG(k <= topk_groups * (E / n_groups));
+        MOE_CHECK_SUP(n_groups <= MOE_MAX_GROUPS);
+    }
+    return MOE_OK;
+}
+
+// Shapes the layer's kernels cover.
+int32_t check_layer(const moe_layer_desc* L) {
+    MOE_CHECK_ARG(L != nullptr);
+    MOE_CHECK_ARG(L->D > 0 && L->I > 0 && L->E > 0 && (L->n_shared == 0 || L->n_shared == 1));
+    int32_t st = check_routing(L->E, L->top_k, L->scoring, L->n_groups, L->topk_groups);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_SUP(L->E + L->n_shared <= MOE_MAX_EXPERTS);
+    MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || L->quant == MOE_QUANT_PTPC_FP8 ||
+                  L->quant == MOE_QUANT_BLOCK128_FP8);
+    MOE_CHECK_ARG(L->w13 != nullptr && L->w2 != nullptr);
+    if (L->quant != MOE_QUANT_NONE_BF16) MOE_CHECK_ARG(L->w13_scale != nullptr && L->w2_scale != nullptr);
+    MOE_CHECK_SUP(L->I % 128 == 0 && L->D % 256 == 0);
+    MOE_CHECK_SUP(L->D <= 16384 && L->I <= 16384);
+    return MOE_OK;
+}
+
+struct Carver {
+    int64_t off = 0;
+    int64_t take(int64_t bytes) {
+        const int64_t at = off;
+        off += (bytes + kAlign - 1) / kAlign * kAlign;
+        return at;
+    }
+};
+
+void layout_of(const moe_layer_desc* L, int T, int B, moe_ws_layout* o) {
+    const int64_t k = L->top_k, E = L->E, Ep = E + L->n_shared, D = L->D, I = L->I;
+    const int64_t A = static_cast<int64_t>(T) * (k + L->n_shared);
+    const int64_t R = max_rows_of(T, k, E, L->n_shared, B);
+    const bool fp8 = L->quant != MOE_QUANT_NONE_BF16;
+    const bool blk = L->quant == MOE_QUANT_BLOCK128_FP8;
+    Carver c;
+    o->logits = c.take(static_cast<int64_t>(T) * E * 4);
+    o->topk_ids = c.take(T * k * 4);
+    o->topk_w = c.take(T * k * 4);
+    o->counts = c.take(Ep * 4);
+    o->offsets = c.take((Ep + 1) * 4);
+    o->sorted_ids = c.take(R * 4);
+    o->block_expert = c.take(R / B * 4);
+    o->inv_perm = c.take(A * 4);
+    o->xq = fp8 ? c.take(static_cast<int64_t>(T) * D) : -1;
+    o->xs = fp8 ? c.take(static_cast<int64_t>(T) * (blk ? D / 128 : 1) * 4) : -1;
+    o->act = c.take(R * I * 2);
+    o->aq = fp8 ? c.take(R * I) : -1;
+    o->as = fp8 ? c.take(R * (blk ? I / 128 : 1) * 4) : -1;
+    o->out_perm = c.take(R * D * (fp8 ? 2 : 4));
+    o->scratch = c.take(static_cast<int64_t>(permute_scratch_bytes(T, static_cast<int>(k), L->n_shared,
+                                                                    static_cast<int>(E))));
+    o->total = c.off;
+    o->max_rows = R;
+    o->block_m = B;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int32_t s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or mode";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int32_t moe_router_logits(const void* x_bf16, const float* router_w, int32_t T, int32_t D, int32_t E,
+                          float* logits, void* stream) {
+    MOE_CHECK_ARG(T >= 0 && D > 0 && E > 0);
+    MOE_CHECK_SUP(D <= MOE_MAX_ROUTER_D);
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(x_bf16 && router_w && logits);
+    return router_logits_launch(static_cast<const uint16_t*>(x_bf16), router_w, T, D, E, logits,
+                                as_stream(stream));
+}
+
+int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t scoring, int32_t n_groups,
+                       int32_t topk_groups, const float* sel_bias, int32_t renormalize, float route_scale,
+                       int32_t* topk_ids, float* topk_w, void* stream) {
+    MOE_CHECK_ARG(T >= 0);
+    const int32_t st = check_routing(E, k, scoring, n_groups, topk_groups);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(logits && topk_ids && topk_w);
+    return route_topk_launch(logits, T, E, k, scoring, n_groups, topk_groups, sel_bias, renormalize, route_scale,
+                             topk_ids, topk_w, as_stream(stream));
+}
+
+int64_t moe_permute_max_rows(int32_t T, int32_t k, int32_t E, int32_t n_shared, int32_t block_m) {
+    if (T < 0 || k <= 0 || E <= 0 || n_shared < 0 || n_shared > 1 || block_m <= 0) return -1;
+    return max_rows_of(T, k, E, n_shared, block_m);
+}
+
+size_t moe_permute_scratch_bytes(int32_t T, int32_t k, int32_t n_shared, int32_t E) {
+    if (T < 0 || k <= 0 || E <= 0 || n_shared < 0 || n_shared > 1) return 0;
+    return permute_scratch_bytes(T, k, n_shared, E);
+}
+
+int32_t moe_permute_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t n_shared,
+                          int32_t block_m, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_ids,
+                          int32_t* block_expert, int32_t* inv_perm, void* scratch, void* stream) {
+    MOE_CHECK_ARG(T >= 0 && k > 0 && E > 0 && (n_shared == 0 || n_shared == 1));
+    MOE_CHECK_ARG(block_m >= 1 && block_m <= 1024);
+    MOE_CHECK_SUP(E + n_shared <= MOE_MAX_EXPERTS);
+    const int64_t R = max_rows_of(T, k, E, n_shared, block_m);
+    MOE_CHECK_SUP(static_cast<int64_t>(T) * (k + n_shared) < (1LL << 30) && R < (1LL << 30));
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(topk_ids && expert_counts && expert_offsets && sorted_ids && block_expert && inv_perm && scratch);
+    return permute_align_launch(topk_ids, T, k, E, n_shared, block_m, static_cast<int>(R), expert_counts,
+                                expert_offsets, sorted_ids, block_expert, inv_perm, scratch, as_stream(stream));
+}
+
+int32_t moe_quant_ptpc_fp8(const void* x_bf16, int64_t M, int32_t K, int32_t group, const int32_t* valid_rows,
+                           uint8_t* q, float* scale, void* stream) {
+    MOE_CHECK_ARG(M >= 0 && K > 0 && (group == 0 || group == 128));
+    MOE_CHECK_SUP(K % 8 == 0 && K <= 16384 && (group == 0 || K % 128 == 0));
+    MOE_CHECK_SUP(M < (1LL << 31) * 4);
+    if (M == 0) return MOE_OK;
+    MOE_CHECK_ARG(x_bf16 && q && scale);
+    return quant_rows_launch(static_cast<const uint16_t*>(x_bf16), M, K, group, valid_rows, q, scale,
+                             as_stream(stream));
+}
+
+int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int32_t K, int32_t quant, uint8_t* q,
+                             float* scale, void* stream) {
+    MOE_CHECK_ARG(n_mats >= 0 && N > 0 && K > 0);
+    MOE_CHECK_ARG(quant == MOE_QUANT_PTPC_FP8 || quant == MOE_QUANT_BLOCK128_FP8);
+    if (n_mats == 0) return MOE_OK;
+    MOE_CHECK_ARG(w_bf16 && q && scale);
+    if (quant == MOE_QUANT_PTPC_FP8) {
+        MOE_CHECK_SUP(K % 8 == 0 && K <= 16384);
+        return quant_rows_launch(static_cast<const uint16_t*>(w_bf16), n_mats * N, K, 0, nullptr, q, scale,
+                                 as_stream(stream));
+    }
+    MOE_CHECK_SUP(N % 128 == 0 && K % 128 == 0);
+    MOE_CHECK_SUP(n_mats * (N / 128) * (K / 128) < (1LL << 31));
+    return quant_wblock_launch(static_cast<const uint16_t*>(w_bf16), n_mats, N, K, q, scale, as_stream(stream));
+}
+
+int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a, const float* a_scale, int32_t T,
+                                     int32_t block_m, const int32_t* sorted_ids, const int32_t* block_expert,
+                                     const int32_t* expert_offsets, void* act_bf16, void* stream) {
+    int32_t st = check_layer(L);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(T >= 0);
+    MOE_CHECK_SUP(block_m_ok(L->quant, block_m));
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(a && sorted_ids && block_expert && expert_offsets && act_bf16);
+    MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || a_scale);
+    const int64_t R = max_rows_of(T, L->top_k, L->E, L->n_shared, block_m);
+    return gemm_gateup_launch(L, a, a_scale, T, block_m, R, sorted_ids, block_expert, act_bf16, as_stream(stream));
+}
+
+int32_t moe_grouped_gemm_down(const moe_layer_desc* L, const void* act, const float* act_scale, int32_t T,
+                              int32_t block_m, const int32_t* block_expert, const int32_t* expert_offsets,
+                              void* out_perm, void* stream) {
+    int32_t st = check_layer(L);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(T >= 0);
+    MOE_CHECK_SUP(block_m_ok(L->quant, block_m));
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(act && block_expert && expert_offsets && out_perm);
+    MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || act_scale);
+    const int64_t R = max_rows_of(T, L->top_k, L->E, L->n_shared, block_m);
+    return gemm_down_launch(L, act, act_scale, block_m, R, block_expert, out_perm, as_stream(stream));
+}
+
+int32_t moe_unpermute_combine(const void* out_perm, int32_t out_dtype, const int32_t* inv_perm,
+                              const float* topk_w, int32_t T, int32_t k, int32_t n_shared, int32_t D,
+                              void* y_bf16, void* stream) {
+    MOE_CHECK_ARG(T >= 0 && k > 0 && D > 0 && (n_shared == 0 || n_shared == 1));
+    MOE_CHECK_ARG(out_dtype == 0 || out_dtype == 1);
+    MOE_CHECK_SUP(D % 8 == 0);
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(out_perm && inv_perm && topk_w && y_bf16);
+    return combine_launch(out_perm, out_dtype, inv_perm, topk_w, T, k, n_shared, D, static_cast<uint16_t*>(y_bf16),
+                          as_stream(stream));
+}
+
+int32_t moe_default_block_m(const moe_layer_desc* L, int32_t T) {
+    if (!L || L->E <= 0 || T < 0) return 64;
+    const int64_t rows = static_cast<int64_t>(T) * (L->top_k + L->n_shared);
+    const int64_t per_expert = rows / (L->E + L->n_shared);
+    if (L->quant == MOE_QUANT_BLOCK128_FP8) return per_expert >= 48 ? 64 : 32;
+    if (per_expert >= 96) return 128;
+    if (per_expert >= 48) return 64;
+    return 32;
+}
+
+size_t moe_forward_workspace_size(const moe_layer_desc* L, int32_t T, int32_t block_m) {
+    if (check_layer(L) != MOE_OK || T < 0) return 0;
+    if (block_m == 0) block_m = moe_default_block_m(L, T);
+    if (!block_m_ok(L->quant, block_m)) return 0;
+    moe_ws_layout o;
+    layout_of(L, T, block_m, &o);
+    return static_cast<size_t>(o.total);
+}
+
+int32_t moe_workspace_layout(const moe_layer_desc* L, int32_t T, int32_t block_m, moe_ws_layout* out) {
+    int32_t st = check_layer(L);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(T >= 0 && out);
+    if (block_m == 0) block_m = moe_default_block_m(L, T);
+    MOE_CHECK_SUP(block_m_ok(L->quant, block_m));
+    layout_of(L, T, block_m, out);
+    return MOE_OK;
+}
+
+int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* logits_or_null, int32_t T,
+                    int32_t block_m, void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t st = check_layer(L);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(T >= 0);
+    if (block_m == 0) block_m = moe_default_block_m(L, T);
+    MOE_CHECK_SUP(block_m_ok(L->quant, block_m));
+    const int64_t A = static_cast<int64_t>(T) * (L->top_k + L->n_shared);
+    MOE_CHECK_SUP(A < (1LL << 30));
+    if (T == 0) return MOE_OK;
+    if (!logits_or_null) {
+        MOE_CHECK_ARG(L->router_w != nullptr);
+        MOE_CHECK_SUP(L->D <= MOE_MAX_ROUTER_D);
+    }
+    MOE_CHECK_ARG(x_bf16 && y_bf16 && workspace);
+    MOE_CHECK_ARG(reinterpret_cast<uintptr_t>(workspace) % kAlign == 0);
+    moe_ws_layout o;
+    layout_of(L, T, block_m, &o);
+    if (static_cast<int64_t>(workspace_bytes) < o.total) return MOE_ERR_WORKSPACE;
+
+    hipStream_t s = as_stream(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    auto at = [&](int64_t off) { return static_cast<void*>(ws + off); };
+    const int k = L->top_k, E = L->E, Ep = E + L->n_shared;
+    const bool fp8 = L->quant != MOE_QUANT_NONE_BF16;
+    const int group = L->quant == MOE_QUANT_BLOCK128_FP8 ? 128 : 0;
+
+    const float* logits = logits_or_null;
+    if (!logits) {
+        float* lg = static_cast<float*>(at(o.logits));
+        if ((st = router_logits_launch(static_cast<const uint16_t*>(x_bf16), L->router_w, T, L->D, E, lg, s)) != MOE_OK)
+            return st;
+        logits = lg;
+    }
+    int* ids = static_cast<int*>(at(o.topk_ids));
+    float* w = static_cast<float*>(at(o.topk_w));
+    if ((st = route_topk_launch(logits, T, E, k, L->scoring, L->n_groups, L->topk_groups, L->sel_bias,
+                                L->renormalize, L->route_scale, ids, w, s)) != MOE_OK)
+        return st;
+    int* offsets = static_cast<int*>(at(o.offsets));
+    int* sorted = static_cast<int*>(at(o.sorted_ids));
+    int* bexp = static_cast<int*>(at(o.block_expert));
+    int* inv = static_cast<int*>(at(o.inv_perm));
+    if ((st = permute_align_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
+                                   static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, at(o.scratch), s)) !=
+        MOE_OK)
+        return st;
+    const void* a = x_bf16;
+    const float* a_scale = nullptr;
+    if (fp8) {
+        if ((st = quant_rows_launch(static_cast<const uint16_t*>(x_bf16), T, L->D, group, nullptr,
+                                    static_cast<uint8_t*>(at(o.xq)), static_cast<float*>(at(o.xs)), s)) != MOE_OK)
+            return st;
+        a = at(o.xq);
+        a_scale = static_cast<float*>(at(o.xs));
+    }
+    void* act = at(o.act);
+    if ((st = gemm_gateup_launch(L, a, a_scale, T, block_m, o.max_rows, sorted, bexp, act, s)) != MOE_OK) return st;
+    const void* act_in = act;
+    const float* act_scale = nullptr;
+    if (fp8) {
+        if ((st = quant_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, group, offsets + Ep,
+                                    static_cast<uint8_t*>(at(o.aq)), static_cast<float*>(at(o.as)), s)) != MOE_OK)
+            return st;
+        act_in = at(o.aq);
+        act_scale = static_cast<float*>(at(o.as));
+    }
+    void* outp = at(o.out_perm);
+    if ((st = gemm_down_launch(L, act_in, act_scale, block_m, o.max_rows, bexp, outp, s)) != MOE_OK) return st;
+    return combine_launch(outp, fp8 ? 1 : 0, inv, w, T, k, L->n_shared, L->D, static_cast<uint16_t*>(y_bf16), s);
+}
+
+}  // extern "C"

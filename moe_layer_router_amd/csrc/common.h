@@ -1,0 +1,93 @@
+// Device helpers shared by the MoE kernels: number-format conversions, wave
+// reductions and launch plumbing.  gfx950 only (wave64, CDNA4 MFMA).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round-to-nearest-even fp32 -> bf16 (inputs are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------- e4m3fn
+// OCP e4m3fn: bias 7, 3 mantissa bits, subnormals m * 2^-9, max 448 (0x7E),
+// 0x7F/0xFF NaN (never produced).  Round to nearest even, keep the sign of
+// zero, saturate magnitudes above 448.  Written from the format definition
+// with integer rounding so the result does not depend on a hardware mode.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fminf(fabsf(y), 448.0f);
+    if (a < 0.015625f) {                       // below 2^-6: subnormal codes 0..8
+        const float s = a * 512.0f;            // exact scaling by 2^9
+        return sign | static_cast<uint32_t>(__builtin_rintf(s));   // ties to even
+    }
+    const uint32_t ua = __float_as_uint(a);
+    const uint32_t e = (ua >> 23) - 120u;      // (exp - 127) + 7, in 1..15
+    uint32_t keep = (ua >> 20) & 7u;           // top 3 mantissa bits
+    const uint32_t rest = ua & 0xFFFFFu;       // 20 dropped bits
+    keep += (rest > 0x80000u) | ((rest == 0x80000u) & (keep & 1u));
+    uint32_t code = (e << 3) + keep;           // a carry of keep moves into e
+    code = code > 0x7Eu ? 0x7Eu : code;
+    return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    float v = e == 0 ? static_cast<float>(m) * 0.001953125f
+                     : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -v : v;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+        int t = __shfl_up(v, o, MOE_WAVE);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace moe
+
+// ---------------------------------------------------------------- host side
+#define MOE_CHECK_ARG(c)            \
+    do {                            \
+        if (!(c)) return MOE_ERR_INVALID_ARG; \
+    } while (0)
+#define MOE_CHECK_SUP(c)            \
+    do {                            \
+        if (!(c)) return MOE_ERR_UNSUPPORTED; \
+    } while (0)
+
+static inline int32_t moe_launch_status() {
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}

@@ -1,0 +1,153 @@
+// PTPC / blockwise FP8 quantization.
+//
+// PTPC-FP8 (Qwen3 MI300X page, 2.1.1 and Figure 3) gives every activation row
+// (token) its own dynamic scale and every weight output channel its own
+// static scale; the MI355X MoRI page's blockwise FP8 uses one fp32 scale per
+// 128 elements.  Per group: amax = max|x|, scale = amax/448,
+// q = e4m3(x * (448/amax)), IEEE fp32 divisions and one fp32 multiply.
+//
+// HBM-bound: one wave per row reads 16 B per lane per step (1 KB coalesced
+// per wave instruction), keeps the row in registers, reduces amax with
+// cross-lane shuffles (16-lane segments for 1x128 groups), then writes 8 B of
+// codes per lane.  No LDS, no block barrier.
+#include "common.h"
+
+namespace moe {
+
+struct alignas(16) bf16x8 { uint16_t v[8]; };
+
+__device__ __forceinline__ uint2 quant8(const bf16x8& x, float inv) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(bf16_to_f32(x.v[i]) * inv) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(bf16_to_f32(x.v[4 + i]) * inv) << (8 * i);
+    return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ float amax8(const bf16x8& x) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(bf16_to_f32(x.v[i])));
+    return m;
+}
+
+__device__ __forceinline__ void scale_pair(float amax, float& scale, float& inv) {
+    if (amax == 0.0f) { scale = 1.0f; inv = 1.0f; }
+    else { scale = amax / 448.0f; inv = 448.0f / amax; }
+}
+
+// NV: vectors of 8 per lane (K = 512 * NV at most).  GROUP: 0 (row) or 128.
+template <int NV, int GROUP>
+__global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
+                                                         const int* __restrict__ valid_rows,
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    if (valid_rows && row >= *valid_rows) return;
+    const int nvec = K >> 3;
+    const bf16x8* xr = reinterpret_cast<const bf16x8*>(x + row * K);
+    bf16x8 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nvec) v[i] = xr[c];
+    }
+    uint2* qr = reinterpret_cast<uint2*>(q + row * K);
+    if (GROUP == 0) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (lane + 64 * i < nvec) m = fmaxf(m, amax8(v[i]));
+        m = wave_max(m);
+        float sc, inv;
+        scale_pair(m, sc, inv);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nvec) qr[c] = quant8(v[i], inv);
+        }
+        if (lane == 0) scale[row] = sc;
+    } else {
+        // vector c covers elements 8c..8c+7; group g = c / 16 spans 16 lanes
+        const int ngroups = K / GROUP;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = lane + 64 * i;
+            float m = c < nvec ? amax8(v[i]) : 0.0f;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            float sc, inv;
+            scale_pair(m, sc, inv);
+            if (c < nvec) {
+                qr[c] = quant8(v[i], inv);
+                if ((lane & 15) == 0) scale[row * ngroups + (c >> 4)] = sc;
+            }
+        }
+    }
+}
+
+// One 128x128 weight block per workgroup: 256 threads x 8 vectors of 8.
+__global__ void __launch_bounds__(256) quant_wblock_kernel(const uint16_t* __restrict__ w, int N, int K,
+                                                           uint8_t* __restrict__ q, float* __restrict__ scale) {
+    __shared__ float s_max[4];
+    const int nbk = K / 128, nbn = N / 128;
+    const int64_t blk = blockIdx.x;
+    const int64_t mat = blk / (static_cast<int64_t>(nbn) * nbk);
+    const int bn = static_cast<int>((blk / nbk) % nbn), bk = static_cast<int>(blk % nbk);
+    const int64_t base = mat * N * K + static_cast<int64_t>(bn) * 128 * K + static_cast<int64_t>(bk) * 128;
+    const int tid = threadIdx.x;
+    bf16x8 v[8];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = (tid >> 4) + 16 * i, c = tid & 15;
+        v[i] = *reinterpret_cast<const bf16x8*>(w + base + static_cast<int64_t>(r) * K + 8 * c);
+        m = fmaxf(m, amax8(v[i]));
+    }
+    m = wave_max(m);
+    if ((tid & 63) == 0) s_max[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    float sc, inv;
+    scale_pair(m, sc, inv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = (tid >> 4) + 16 * i, c = tid & 15;
+        *reinterpret_cast<uint2*>(q + base + static_cast<int64_t>(r) * K + 8 * c) = quant8(v[i], inv);
+    }
+    if (tid == 0) scale[blk] = sc;
+}
+
+template <int GROUP>
+static void launch_rows(int nv, dim3 g, hipStream_t s, const uint16_t* x, int64_t M, int K, const int* valid,
+                        uint8_t* q, float* sc) {
+    const dim3 b(256);
+    if (nv <= 1) hipLaunchKernelGGL((quant_rows_kernel<1, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
+    else if (nv <= 2) hipLaunchKernelGGL((quant_rows_kernel<2, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
+    else if (nv <= 4) hipLaunchKernelGGL((quant_rows_kernel<4, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
+    else if (nv <= 8) hipLaunchKernelGGL((quant_rows_kernel<8, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
+    else if (nv <= 16) hipLaunchKernelGGL((quant_rows_kernel<16, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
+    else hipLaunchKernelGGL((quant_rows_kernel<32, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
+}
+
+int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const int* valid_rows, uint8_t* q,
+                          float* scale, hipStream_t s) {
+    if (M == 0) return MOE_OK;
+    const int nv = static_cast<int>(ceil_div(K / 8, 64));
+    const dim3 g(static_cast<unsigned>(ceil_div(M, 4)));
+    if (group == 0) launch_rows<0>(nv, g, s, x, M, K, valid_rows, q, scale);
+    else launch_rows<128>(nv, g, s, x, M, K, valid_rows, q, scale);
+    return moe_launch_status();
+}
+
+int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, uint8_t* q, float* scale,
+                            hipStream_t s) {
+    const int64_t nblk = n_mats * (N / 128) * (K / 128);
+    if (nblk == 0) return MOE_OK;
+    hipLaunchKernelGGL(quant_wblock_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, w, N, K, q, scale);
+    return moe_launch_status();
+}
+
+}  // namespace moe

@@ -1,0 +1,91 @@
+"""Shared set-up of the GPU parity tests and the bench: a workload's seeded
+inputs on the GPU, the HIP layer built from them, and the oracle's view of
+the same data (host copies, fetched per expert on demand)."""
+
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle as O
+import synth
+
+# Reduced shapes with the recipes of the full workloads: several M tiles per
+# expert, ragged tails, and every mode.  Full sizes are in synth.WORKLOADS.
+REDUCED = {
+    "tiny_bf16": synth.get("tiny_bf16"),
+    "qwen3_30b_a3b_ptpc": synth.get("qwen3_30b_a3b_ptpc"),
+    "qwen3_235b_prefill_ptpc_r": synth.get("qwen3_235b_prefill_ptpc").replace(T=1000, D=1024, I=512, E=32),
+    "qwen3_235b_decode_ptpc": synth.get("qwen3_235b_decode_ptpc"),
+    "deepseek_r1_block_fp8_r": synth.get("deepseek_r1_block_fp8").replace(T=300, D=1024, I=256, E=32),
+    "bf16_multi_tile_r": synth.get("tiny_bf16").replace(T=700, D=512, I=256, E=16, k=4),
+}
+
+
+def say(*a) -> None:
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def spec_of(w: synth.Workload) -> O.LayerSpec:
+    return O.LayerSpec(D=w.D, I=w.I, E=w.E, top_k=w.k, n_shared=w.n_shared, scoring=w.scoring,
+                       n_groups=w.n_groups, topk_groups=w.topk_groups, route_scale=w.route_scale, quant=w.quant)
+
+
+@dataclass
+class Case:
+    w: synth.Workload
+    layer: object                 # moe_layer_router_amd.MoELayer
+    x: torch.Tensor               # [T, D] bf16 on the GPU
+    logits: Optional[torch.Tensor]
+    router_w: Optional[torch.Tensor]
+    w13: torch.Tensor             # bf16 masters on the GPU
+    w2: torch.Tensor
+    spec: O.LayerSpec
+    bank: O.ExpertBank
+
+    def x_np(self) -> np.ndarray:
+        return synth.bf16_to_f32_np(self.x)
+
+    def logits_np(self) -> Optional[np.ndarray]:
+        return None if self.logits is None else self.logits.cpu().numpy()
+
+
+def build_case(w: synth.Workload, device="cuda", cache_experts: bool = True, keep_masters: bool = True) -> Case:
+    import moe_layer_router_amd as mlr
+    x = synth.gen_x(w, device)
+    logits = synth.gen_logits(w, device)
+    router_w = synth.gen_router_w(w, device) if w.router == "gemm" else None
+    w13, w2 = synth.gen_masters(w, device)
+    layer = mlr.MoELayer.from_masters(w13, w2, w.quant, router_w=router_w, E=w.E, top_k=w.k,
+                                      n_shared=w.n_shared, scoring=w.scoring, n_groups=w.n_groups,
+                                      topk_groups=w.topk_groups, route_scale=w.route_scale)
+    spec = spec_of(w)
+
+    def master(e):
+        return synth.bf16_to_f32_np(w13[e]), synth.bf16_to_f32_np(w2[e])
+    bank = O.ExpertBank(spec, master, cache=cache_experts)
+    if not keep_masters and w.quant != "bf16":
+        # the layer holds its own quantized copies; free the masters early
+        # (the oracle then needs them again: regenerate per expert)
+        def master_regen(e):
+            a, b = synth.gen_expert_master(w, e, device)
+            return synth.bf16_to_f32_np(a), synth.bf16_to_f32_np(b)
+        bank = O.ExpertBank(spec, master_regen, cache=cache_experts)
+        del w13, w2
+        torch.cuda.empty_cache()
+        w13 = w2 = None
+    return Case(w, layer, x, logits, router_w, w13, w2, spec, bank)
+
+
+def rel_l2(a, b) -> float:
+    return O.relative_l2(np.asarray(a, np.float64), np.asarray(b, np.float64))
+
+
+def tol_of(quant: str) -> float:
+    """Relative L2 bound on y: 2e-3 for the bf16 path, 1e-2 for the FP8 paths."""
+    return 2e-3 if quant == "bf16" else 1e-2

@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/moe.h declares, and its host-only functions and
+argument validation behave as documented."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.conftest import ROOT
+
+mlr = pytest.importorskip("moe_layer_router_amd")
+from moe_layer_router_amd import _lib as L  # noqa: E402
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int32_t|int64_t|size_t|char\s*\*|const char\s*\*)\s*\*?\s*"
+                                 r"(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 14, names
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
+
+
+def test_status_strings():
+    for s in range(5):
+        assert L.status_str(s)
+    assert L.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("T,k,E,ns,B", [(0, 8, 128, 0, 32), (1, 1, 1, 0, 1), (64, 2, 8, 0, 32),
+                                        (8192, 8, 128, 0, 128), (32, 8, 128, 0, 32), (4096, 8, 256, 1, 64),
+                                        (8192, 10, 512, 0, 1)])
+def test_max_rows_matches_oracle(T, k, E, ns, B):
+    assert L.lib().moe_permute_max_rows(T, k, E, ns, B) == O.permute_max_rows(T, k, E, ns, B)
+
+
+def test_max_rows_rejects_bad_input():
+    assert L.lib().moe_permute_max_rows(-1, 8, 128, 0, 32) == -1
+    assert L.lib().moe_permute_max_rows(4, 8, 128, 2, 32) == -1
+
+
+def _desc(**kw):
+    d = dict(D=512, I=256, E=16, top_k=4, n_shared=0, scoring=0, n_groups=1, topk_groups=1, renormalize=1,
+             route_scale=1.0, quant=1, w13=1 << 20, w13_scale=1 << 21, w2=1 << 22, w2_scale=1 << 23,
+             router_w=None, sel_bias=None)
+    d.update(kw)
+    return L.LayerDesc(**d)
+
+
+def test_validation_happens_before_any_launch():
+    lib = L.lib()
+    bad = ctypes.c_void_p(0)
+    # NULL device pointers with T > 0 -> invalid argument, nothing enqueued
+    assert lib.moe_route_topk(None, 4, 8, 2, 0, 1, 1, None, 1, 1.0, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk(None, 4, 8, 9, 0, 1, 1, None, 1, 1.0, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk(None, 4, 8, 17, 0, 1, 1, None, 1, 1.0, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk(None, 4, 2048, 8, 0, 1, 1, None, 1, 1.0, None, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk(None, 4, 64, 8, 1, 7, 2, None, 1, 1.0, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk(None, 4, 64, 8, 1, 8, 1, None, 1, 1.0, None, None, None) == L.MOE_ERR_INVALID_ARG
+    # T = 0 is a valid no-op even with NULL buffers
+    assert lib.moe_route_topk(None, 0, 8, 2, 0, 1, 1, None, 1, 1.0, None, None, None) == L.MOE_OK
+    assert lib.moe_quant_ptpc_fp8(None, 0, 256, 0, None, None, None, None) == L.MOE_OK
+    assert lib.moe_quant_ptpc_fp8(None, 4, 256, 64, None, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quant_ptpc_fp8(None, 4, 200, 128, None, None, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_align(None, 4, 2, 8, 0, 0, None, None, None, None, None, None, None) \
+        == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_unpermute_combine(None, 2, None, None, 4, 2, 0, 256, None, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_layer_validation_and_workspace():
+    lib = L.lib()
+    d = _desc()
+    assert lib.moe_forward_workspace_size(ctypes.byref(d), 100, 64) > 0
+    # unsupported shapes / block sizes
+    assert lib.moe_forward_workspace_size(ctypes.byref(_desc(I=200)), 100, 64) == 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(d), 100, 48) == 0
+    assert lib.moe_forward(ctypes.byref(_desc(I=200)), None, None, 4, 0, None, None, 0, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_forward(ctypes.byref(_desc(w13=None)), None, None, 4, 0, None, None, 0, None) \
+        == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(ctypes.byref(_desc(quant=7)), None, None, 4, 0, None, None, 0, None) \
+        == L.MOE_ERR_INVALID_ARG
+    # no logits and no router weight
+    assert lib.moe_forward(ctypes.byref(d), 1 << 24, None, 4, 0, 1 << 25, 1 << 26, 1 << 30, None) \
+        == L.MOE_ERR_INVALID_ARG
+    # workspace too small is reported before anything runs
+    need = lib.moe_forward_workspace_size(ctypes.byref(d), 4, 0)
+    assert lib.moe_forward(ctypes.byref(d), 1 << 24, 1 << 27, 4, 0, 1 << 25, 1 << 26, need - 1, None) \
+        == L.MOE_ERR_WORKSPACE
+    # misaligned workspace
+    assert lib.moe_forward(ctypes.byref(d), 1 << 24, 1 << 27, 4, 0, 1 << 25, (1 << 26) + 8, need, None) \
+        == L.MOE_ERR_INVALID_ARG
+    # T = 0: no-op
+    assert lib.moe_forward(ctypes.byref(d), None, None, 0, 0, None, None, 0, None) == L.MOE_OK
+
+
+def test_workspace_layout_is_disjoint_and_aligned():
+    lib = L.lib()
+    for d, T in [(_desc(), 300), (_desc(quant=0, w13_scale=None, w2_scale=None), 64),
+                 (_desc(quant=2, n_shared=1, scoring=1, n_groups=4, topk_groups=2, route_scale=2.5), 77)]:
+        lay = L.WsLayout()
+        assert lib.moe_workspace_layout(ctypes.byref(d), T, 0, ctypes.byref(lay)) == L.MOE_OK
+        offs = sorted(getattr(lay, n) for n, _ in L.WsLayout._fields_[:15] if getattr(lay, n) >= 0)
+        assert all(o % 256 == 0 for o in offs)
+        assert len(set(offs)) == len(offs)
+        assert lay.total == lib.moe_forward_workspace_size(ctypes.byref(d), T, 0)
+        assert lay.max_rows == O.permute_max_rows(T, d.top_k, d.E, d.n_shared, lay.block_m)
