@@ -176,9 +176,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_235b_prefill_ptpc")
     ap.add_argument("--block-m", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="launch one device-to-device copy of this many MiB (a known-size kernel for "
+                         "calibrating HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -198,6 +201,12 @@ def main():
     w = synth.get(args.workload)
     log("building", w.name)
     case = build_case(w)
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     st = Steps(case.layer, w, case.x, case.logits, args.block_m)
     log("block_m", st.B, "max_rows", st.lay["max_rows"])
 

@@ -45,8 +45,8 @@ def test_route_softmax_full_size(name):
 
 def test_route_softmax_not_renormalized_and_k_equals_e():
     say("route_softmax variants")
-    logits = synth.gen_normal_f32((300, 64), 2.0, 99, "cuda")
-    for k, renorm in [(64, True), (8, False), (1, True)]:
+    logits = synth.gen_normal_f32((300, 16), 2.0, 99, "cuda")
+    for k, renorm in [(16, True), (8, False), (1, True)]:
         ids, wt = mlr.route_topk(logits, k, renormalize=renorm)
         torch.cuda.synchronize()
         rid, rw = O.route_softmax_topk(logits.cpu().numpy(), k, renorm)
@@ -304,7 +304,11 @@ def test_combine_entry(T, k, ns, D, dt):
     o_sh = opn[inv[T * k:]] if ns else None
     ref = O.combine(o_rows, wt.cpu().numpy(), o_sh)
     got = y.float().cpu().numpy()
-    # fp32 vs fp64 accumulation: at most one bf16 step apart, and rarely
+    # fp32 vs fp64 accumulation: the fp32 sum is within (k+1) * 2^-24 of the
+    # summed term magnitudes; after that one bf16 step of the larger result
+    mag = np.abs(wt.cpu().numpy())[:, :, None] * np.abs(o_rows)
+    S = mag.sum(axis=1) + (np.abs(o_sh) if ns else 0.0)
     diff = np.abs(got - ref)
-    assert np.all(diff <= np.abs(ref) * 2.0 ** -7 + 1e-30)
+    bound = np.maximum(np.abs(got), np.abs(ref)) * 2.0 ** -7 + (k + 2) * 2.0 ** -24 * S + 1e-30
+    assert np.all(diff <= bound)
     assert (diff > 0).mean() < 0.01
