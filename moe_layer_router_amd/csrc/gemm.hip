@@ -7,23 +7,28 @@
 // DeepSeek-R1 layer's blockwise FP8 (MI355X MoRI page) uses 1x128 activation
 // and 128x128 weight scales.
 //
-// Layout of one workgroup (256 threads, 4 waves):
-//   - a tile of BM permuted rows (one expert: the permutation pads every
-//     expert to a multiple of BM, so block_expert gives the expert) times 256
-//     weight rows (gate_up: 128 gate + the matching 128 up rows, giving 128
-//     act columns; down: 256 output columns);
-//   - K advances 128 bytes per step (128 e4m3 or 64 bf16 elements); A and B
-//     tiles are staged through LDS, double buffered, one barrier per step;
-//     rows are padded to 144 B so the 32 lanes that read one MFMA operand hit
-//     distinct banks;
-//   - waves split the tile 2x2 (BM = 128) or 1x4 (BM <= 64); each wave runs
-//     32x32 MFMAs (v_mfma_f32_32x32x64_f8f6f4 or v_mfma_f32_32x32x16_bf16);
-//   - A and B operands take the same lane -> K mapping, so the reduction is
-//     exact whatever order the matrix core sums K in;
+// Layout of one workgroup (256 threads, 4 waves, one workgroup per CU):
+//   - a tile of BM permuted rows of one expert (the permutation pads every
+//     expert to a multiple of BM) times 256 weight rows (gate_up: 128 gate
+//     rows and the matching 128 up rows, giving 128 act columns; down: 256
+//     output columns);
+//   - K advances 128 bytes per step (128 e4m3 or 64 bf16 elements; one
+//     128-element scale block in the blockwise mode).  Global loads run three
+//     steps ahead through a ring of three register stages; LDS holds two
+//     stages of 128-byte rows whose 16-byte chunks are XOR-swizzled by row, so
+//     the 16 lanes of an MFMA operand read hit distinct banks; one barrier
+//     per step; the steady-state loop has no data-dependent branch;
+//   - waves split the tile 2x2 (BM = 128) or 1x4 (BM <= 64) and run 32x32
+//     MFMAs (v_mfma_f32_32x32x64_f8f6f4 or v_mfma_f32_32x32x16_bf16); A and B
+//     operands take the same lane -> K mapping, so the reduction pairs
+//     matching K whatever order the matrix core sums in;
+//   - pad rows read a real row and are zeroed by a row mask in the epilogue;
+//   - tiles are ordered expert by expert, weight tile by weight tile, row
+//     block fastest, and each XCD (workgroup id mod 8) takes a contiguous
+//     range of that order: the row blocks of one expert that share a weight
+//     tile run together on one XCD and share it through its L2;
 //   - the epilogue dequantizes (row scale x channel scale), applies
-//     silu(g) * u for gate_up, rounds to bf16 and stores;
-//   - workgroup ids are remapped so consecutive tiles (same rows, adjacent
-//     weight columns) land on the same XCD and share its L2.
+//     silu(g) * u for gate_up, rounds to bf16 and stores.
 #include "common.h"
 
 namespace moe {
@@ -33,8 +38,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBKB = 128;      // K bytes per step
-constexpr int kLdsRow = 144;   // padded LDS row (bytes)
+constexpr int kBK = 128;       // K bytes per step
 constexpr int kBRows = 256;    // weight rows per tile
 
 struct GemmArgs {
@@ -45,6 +49,7 @@ struct GemmArgs {
     const int* sorted_ids;     // gate_up: flat id per permuted row (NULL: rows are direct)
     int topk, TK, sentinel;
     const int* block_expert;
+    const int* offsets;        // [E'+1] padded expert offsets
     const uint8_t* w;          // [E', Nw, K] weights
     int64_t w_expert_bytes;
     const float* w_scale;      // PTPC: [E', Nw]; block: [E', Nw/128, K/128]
@@ -57,26 +62,15 @@ struct GemmArgs {
     int n_ntiles, n_tiles;
 };
 
-template <int MODE>
-__device__ __forceinline__ void mfma_step(const uint8_t* a_lds, const uint8_t* b_lds, v16f& acc) {
-    if constexpr (MODE == MOE_QUANT_NONE_BF16) {
-        const v8bf a = *reinterpret_cast<const v8bf*>(a_lds);
-        const v8bf b = *reinterpret_cast<const v8bf*>(b_lds);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-    } else {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(a_lds), a1 = *reinterpret_cast<const u32x4*>(a_lds + 16);
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(b_lds), b1 = *reinterpret_cast<const u32x4*>(b_lds + 16);
-        const v8i a = __builtin_bit_cast(v8i, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        const v8i b = __builtin_bit_cast(v8i, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-        // e4m3 x e4m3 (format selectors 0, 0), no block scaling
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
-    }
-}
+// byte offset of (row, logical 16-byte chunk c) in a 128-byte-row LDS stage
+__device__ __forceinline__ int lds_off(int row, int c) { return row * kBK + ((c ^ ((row >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ u32x4 lds16(const uint8_t* L, int off) { return *reinterpret_cast<const u32x4*>(L + off); }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 template <int MODE, bool GATEUP, int BM>
-__global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmArgs p) {
+__global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) {
     constexpr int ELEM = MODE == MOE_QUANT_NONE_BF16 ? 2 : 1;
     constexpr int WM = BM >= 128 ? 2 : 1;
     constexpr int WN = 4 / WM;
@@ -85,97 +79,96 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmArgs p) {
     constexpr int WCOLS = kBRows / WN;       // weight rows per wave
     constexpr int TN = WCOLS / 32;
     constexpr int G = 128 / WN;              // gate_up: gate (and up) rows per wave
-    constexpr int A_LD = BM * 8 / 256;       // 16-B chunks of A per thread per step
-    constexpr int KSUB = MODE == MOE_QUANT_NONE_BF16 ? 4 : 2;   // MFMAs per 128-B step
-    constexpr int SUBB = kBKB / KSUB;        // bytes per MFMA K-substep
-    constexpr int LANEB = SUBB / 2;          // bytes per lane per operand
+    constexpr int A_CH = BM * 8 / 256;       // 16-byte A chunks per thread per step
+    constexpr int B_CH = kBRows * 8 / 256;   // 16-byte B chunks per thread per step
     constexpr int TILE_N = GATEUP ? 128 : kBRows;
     constexpr bool BLOCKQ = MODE == MOE_QUANT_BLOCK128_FP8;
-    static_assert(TM >= 1 && TN >= 2, "tile shape");
+    constexpr int STAGE = (BM + kBRows) * kBK;
+    constexpr int kRing = BLOCKQ ? 2 : 3;    // register stages (loads in flight ahead of use)
+    static_assert(TM >= 1 && TN >= 2 && A_CH >= 1, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + kBRows) * kLdsRow];
-    __shared__ float s_rowscale[BM];
-    __shared__ float s_ascale[2][BM];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    __shared__ float s_rowscale[BM];          // PTPC: row scale; other modes: row mask (pad rows 0)
+    __shared__ float s_ascale[2][BM];         // block mode: row scale of the stage's K block
     __shared__ int s_tok[BM];
 
-    // XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
-    // contiguous range of tiles.
+    // tile order: expert-major, weight tile, then row block; XCD-contiguous
     const int per = (p.n_tiles + 7) >> 3;
     const int lt = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (lt >= p.n_tiles) return;
-    const int mb = lt / p.n_ntiles, nt = lt - mb * p.n_ntiles;
-    const int e = p.block_expert[mb];
+    const int e = p.block_expert[lt / p.n_ntiles];
     if (e < 0) return;
+    const int bs = p.offsets[e] / BM, nb = p.offsets[e + 1] / BM - bs;
+    const int local = lt - bs * p.n_ntiles;
+    const int nt = local / nb, mb = bs + local % nb;
     const int m0 = mb * BM;
     const int n0 = nt * TILE_N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    // rows of this tile -> activation row (token for gate_up)
     if (tid < BM) {
-        int tok;
+        int tok = m0 + tid;
+        float rs = 1.0f;
         if (p.sorted_ids) {
             const int f = p.sorted_ids[m0 + tid];
-            tok = f == p.sentinel ? -1 : (f < p.TK ? f / p.topk : f - p.TK);
-        } else {
-            tok = m0 + tid;
+            const bool pad = f == p.sentinel;
+            tok = pad ? 0 : (f < p.TK ? f / p.topk : f - p.TK);
+            rs = pad ? 0.0f : 1.0f;
         }
         s_tok[tid] = tok;
-        if constexpr (MODE == MOE_QUANT_PTPC_FP8) s_rowscale[tid] = tok >= 0 ? p.a_scale[tok] : 0.0f;
+        if constexpr (MODE == MOE_QUANT_PTPC_FP8) rs = rs == 0.0f ? 0.0f : p.a_scale[tok];
+        s_rowscale[tid] = rs;
     }
     __syncthreads();
 
-    const uint8_t* a_src[A_LD];
+    // global sources and LDS slots of this thread's chunks (same every step)
+    const uint8_t* a_src[A_CH];
+    int a_dst[A_CH];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int c = tid + 256 * i;
-        const int tok = s_tok[c >> 3];
-        a_src[i] = tok >= 0 ? p.a + tok * p.a_ld + (c & 7) * 16 : nullptr;
+    for (int i = 0; i < A_CH; ++i) {
+        const int q = tid + 256 * i;
+        const int r = q >> 3, c = q & 7;
+        a_src[i] = p.a + static_cast<int64_t>(s_tok[r]) * p.a_ld + c * 16;
+        a_dst[i] = lds_off(r, c);
     }
     const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
     const int64_t wrow_bytes = static_cast<int64_t>(p.K) * ELEM;
-    const uint8_t* b_src[8];
+    uint32_t b_src[B_CH];                                   // byte offsets within the expert
+    int b_dst[B_CH];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int c = tid + 256 * i;
-        const int r = c >> 3;
+    for (int i = 0; i < B_CH; ++i) {
+        const int q = tid + 256 * i;
+        const int r = q >> 3, c = q & 7;
         const int wr = GATEUP ? (r < 128 ? n0 + r : p.I + n0 + r - 128) : n0 + r;
-        b_src[i] = wexp + wr * wrow_bytes + (c & 7) * 16;
+        b_src[i] = static_cast<uint32_t>(wr * wrow_bytes + c * 16);
+        b_dst[i] = lds_off(BM + r, c);
     }
-    const int nk = static_cast<int>(wrow_bytes / kBKB);
+    const int nk = static_cast<int>(wrow_bytes / kBK);
+    int ras_tok = -1;
+    if constexpr (BLOCKQ) ras_tok = tid < BM ? (s_rowscale[tid] == 0.0f ? -1 : s_tok[tid]) : -1;
 
-    u32x4 ra[A_LD], rb[8];
-    float ras = 0.0f;
-#define MOE_GLOAD(S)                                                                                     \
-    do {                                                                                                 \
-        const int64_t koff_ = static_cast<int64_t>(S) * kBKB;                                            \
-        _Pragma("unroll") for (int i = 0; i < A_LD; ++i) ra[i] =                                         \
-            a_src[i] ? *reinterpret_cast<const u32x4*>(a_src[i] + koff_) : u32x4{0, 0, 0, 0};      \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + koff_); \
-        if constexpr (BLOCKQ) {                                                                          \
-            if (tid < BM) {                                                                              \
-                const int tok_ = s_tok[tid];                                                             \
-                ras = tok_ >= 0 ? p.a_scale[static_cast<int64_t>(tok_) * p.a_scale_ld + (S)] : 0.0f;     \
-            }                                                                                            \
-        }                                                                                                \
+    u32x4 ra[kRing][A_CH], rb[kRing][B_CH];
+    float ras[kRing];
+#define MOE_GLOAD(J, S)                                                                                   \
+    do {                                                                                                  \
+        const int64_t ko_ = static_cast<int64_t>(S) * kBK;                                                \
+        _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[J][i] = *reinterpret_cast<const u32x4*>(a_src[i] + ko_); \
+        _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[J][i] = *reinterpret_cast<const u32x4*>(wexp + b_src[i] + ko_); \
+        if constexpr (BLOCKQ) {                                                                           \
+            ras[J] = ras_tok >= 0 ? p.a_scale[static_cast<int64_t>(ras_tok) * p.a_scale_ld + (S)] : 0.0f; \
+        }                                                                                                 \
     } while (0)
-#define MOE_LSTORE(BUF)                                                                                  \
-    do {                                                                                                 \
-        uint8_t* L_ = lds[BUF];                                                                          \
-        _Pragma("unroll") for (int i = 0; i < A_LD; ++i) {                                               \
-            const int c_ = tid + 256 * i;                                                                \
-            *reinterpret_cast<u32x4*>(L_ + (c_ >> 3) * kLdsRow + (c_ & 7) * 16) = ra[i];                 \
-        }                                                                                                \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                  \
-            const int c_ = tid + 256 * i;                                                                \
-            *reinterpret_cast<u32x4*>(L_ + (BM + (c_ >> 3)) * kLdsRow + (c_ & 7) * 16) = rb[i];          \
-        }                                                                                                \
-        if constexpr (BLOCKQ) {                                                                          \
-            if (tid < BM) s_ascale[BUF][tid] = ras;                                                      \
-        }                                                                                                \
+#define MOE_LSTORE(J, BUF)                                                                                \
+    do {                                                                                                  \
+        uint8_t* L_ = lds + (BUF) * STAGE;                                                                \
+        _Pragma("unroll") for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4*>(L_ + a_dst[i]) = ra[J][i]; \
+        _Pragma("unroll") for (int i = 0; i < B_CH; ++i) *reinterpret_cast<u32x4*>(L_ + b_dst[i]) = rb[J][i]; \
+        if constexpr (BLOCKQ) {                                                                           \
+            if (tid < BM) s_ascale[BUF][tid] = ras[J];                                                    \
+        }                                                                                                 \
     } while (0)
 
-    // LDS row of this lane's operand rows
+    // LDS rows of this lane's operands
     int a_row[TM], b_row[TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) a_row[tm] = wm * WROWS + tm * 32 + (lane & 31);
@@ -186,7 +179,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmArgs p) {
         else r = wn * WCOLS + tn * 32;
         b_row[tn] = BM + r + (lane & 31);
     }
-    const int lane_k = (lane >> 5) * LANEB;
+    const int h = lane >> 5;
 
     v16f acc[TM][TN];
 #pragma unroll
@@ -194,60 +187,109 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmArgs p) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16f{};
 
-    MOE_GLOAD(0);
-    MOE_LSTORE(0);
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nk) MOE_GLOAD(s + 1);
-        const uint8_t* L = lds[buf];
-        if constexpr (!BLOCKQ) {
+    // one 128-byte K step on LDS stage `buf`
+    auto step = [&](int buf, int s) {
+        const uint8_t* L = lds + buf * STAGE;
+        if constexpr (MODE == MOE_QUANT_NONE_BF16) {
 #pragma unroll
-            for (int kk = 0; kk < KSUB; ++kk)
+            for (int kk = 0; kk < 4; ++kk) {
+                v8bf av[TM];
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm)
+                for (int tm = 0; tm < TM; ++tm) av[tm] = __builtin_bit_cast(v8bf, lds16(L, lds_off(a_row[tm], 2 * kk + h)));
 #pragma unroll
-                    for (int tn = 0; tn < TN; ++tn)
-                        mfma_step<MODE>(L + a_row[tm] * kLdsRow + kk * SUBB + lane_k,
-                                        L + b_row[tn] * kLdsRow + kk * SUBB + lane_k, acc[tm][tn]);
+                for (int tn = 0; tn < TN; ++tn) {
+                    const v8bf bv = __builtin_bit_cast(v8bf, lds16(L, lds_off(b_row[tn], 2 * kk + h)));
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm)
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv, acc[tm][tn], 0, 0, 0);
+                }
+            }
         } else {
-            // one 128-element K step is one scale block: partial sums, then
-            // acc += partial * a_scale(row, kb) * w_scale(n-block, kb)
-            v16f part[TM][TN];
+            v8i av[2][TM];
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn) part[tm][tn] = v16f{};
-#pragma unroll
-            for (int kk = 0; kk < KSUB; ++kk)
+                for (int tm = 0; tm < TM; ++tm) {
+                    const u32x4 lo = lds16(L, lds_off(a_row[tm], 4 * kk + 2 * h));
+                    const u32x4 hi = lds16(L, lds_off(a_row[tm], 4 * kk + 2 * h + 1));
+                    av[kk][tm] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            float as[BLOCKQ ? TM : 1][BLOCKQ ? 16 : 1];
+            if constexpr (BLOCKQ) {
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                    for (int tn = 0; tn < TN; ++tn)
-                        mfma_step<MODE>(L + a_row[tm] * kLdsRow + kk * SUBB + lane_k,
-                                        L + b_row[tn] * kLdsRow + kk * SUBB + lane_k, part[tm][tn]);
-            float wsc[TN];
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const int wr0 = b_row[tn] - BM - (lane & 31);              // tile-local weight row
-                const int wr = GATEUP ? (wr0 < 128 ? n0 + wr0 : p.I + n0 + wr0 - 128) : n0 + wr0;
-                wsc[tn] = p.w_scale[e * p.ws_expert + (wr >> 7) * p.ws_ld + s];
+                    for (int i = 0; i < 16; ++i)
+                        as[tm][i] = s_ascale[buf][wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
             }
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
+            for (int tn = 0; tn < TN; ++tn) {
+                v8i bv[2];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                    const float as = s_ascale[buf][row];
+                for (int kk = 0; kk < 2; ++kk) {
+                    const u32x4 lo = lds16(L, lds_off(b_row[tn], 4 * kk + 2 * h));
+                    const u32x4 hi = lds16(L, lds_off(b_row[tn], 4 * kk + 2 * h + 1));
+                    bv[kk] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+                if constexpr (!BLOCKQ) {
 #pragma unroll
-                    for (int tn = 0; tn < TN; ++tn) acc[tm][tn][i] += part[tm][tn][i] * (as * wsc[tn]);
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int tm = 0; tm < TM; ++tm)
+                            // e4m3 x e4m3 (format selectors 0, 0), no block scaling
+                            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[kk][tm], bv[kk], acc[tm][tn],
+                                                                                          0, 0, 0, 0, 0, 0);
+                } else {
+                    // the step is one 128-element scale block:
+                    // acc += part * a_scale(row, kb) * w_scale(n-block, kb)
+                    const int wr0 = b_row[tn] - BM - (lane & 31);
+                    const int wr = GATEUP ? (wr0 < 128 ? n0 + wr0 : p.I + n0 + wr0 - 128) : n0 + wr0;
+                    const float wsc = p.w_scale[e * p.ws_expert + (wr >> 7) * p.ws_ld + s];
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm) {
+                        v16f part = v16f{};
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk)
+                            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[kk][tm], bv[kk], part, 0, 0, 0, 0,
+                                                                                   0, 0);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[tm][tn][i] += part[i] * (as[tm][i] * wsc);
+                    }
                 }
             }
         }
-        if (s + 1 < nk) MOE_LSTORE(buf ^ 1);
-        __syncthreads();
-    }
+    };
 
+    // prologue: stages 0..2 in flight, stage 0 into LDS buffer 0
+#pragma unroll
+    for (int j = 0; j < kRing; ++j)
+        if (j < nk) MOE_GLOAD(j, j);
+    MOE_LSTORE(0, 0);
+    __syncthreads();
+    int s = 0;
+    // steady state, kRing steps per trip; step s uses LDS buffer s & 1 and
+    // register stage s % kRing (refilled with step s + kRing right away)
+    for (; s + 2 * kRing <= nk; s += kRing) {
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+            const int buf = (s + j) & 1;
+            MOE_GLOAD(j, s + j + kRing);
+            step(buf, s + j);
+            MOE_LSTORE((j + 1) % kRing, buf ^ 1);
+            __syncthreads();
+        }
+    }
+    // tail: fewer than 2 * kRing steps remain
+#pragma unroll
+    for (int j = 0; j < 2 * kRing; ++j) {
+        const int t = s + j;
+        if (t < nk) {
+            if (j < kRing && t + kRing < nk) MOE_GLOAD(j, t + kRing);
+            step(t & 1, t);
+            if (t + 1 < nk) MOE_LSTORE((j + 1) % kRing, (t + 1) & 1);
+            __syncthreads();
+        }
+    }
 #undef MOE_GLOAD
 #undef MOE_LSTORE
 
@@ -269,7 +311,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmArgs p) {
                 for (int i = 0; i < 16; ++i) {
                     const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                     float g = acc[tm][tg][i], u = acc[tm][tg + TN / 2][i];
-                    if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
+                    if constexpr (!BLOCKQ) {
                         const float rs = s_rowscale[row];
                         g = g * rs * swg;
                         u = u * rs * swu;
@@ -290,7 +332,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmArgs p) {
                 for (int i = 0; i < 16; ++i) {
                     const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                     float v = acc[tm][tn][i];
-                    if constexpr (MODE == MOE_QUANT_PTPC_FP8) v = v * s_rowscale[row] * sw;
+                    if constexpr (!BLOCKQ) v = v * s_rowscale[row] * sw;
                     const int64_t o = static_cast<int64_t>(m0 + row) * p.out_ld + n0 + col;
                     if constexpr (MODE == MOE_QUANT_NONE_BF16) static_cast<float*>(p.out)[o] = v;
                     else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
@@ -303,16 +345,23 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmArgs p) {
 template <int MODE, bool GATEUP>
 static int32_t launch_bm(int block_m, const GemmArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(ceil_div(a.n_tiles, 8) * 8)), block(256);
-    switch (block_m) {
-        case 32: hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 32>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 64>), grid, block, 0, s, a); break;
-        case 128:
-            if constexpr (MODE == MOE_QUANT_BLOCK128_FP8) return MOE_ERR_UNSUPPORTED;
-            else hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 128>), grid, block, 0, s, a);
-            break;
-        default: return MOE_ERR_UNSUPPORTED;
+    if (block_m == 32) {
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 32>), grid, block, 0, s, a);
+        return moe_launch_status();
     }
-    return moe_launch_status();
+    // the blockwise mode keeps its partial sums and scales in registers: row
+    // blocks above 32 would spill
+    if constexpr (MODE != MOE_QUANT_BLOCK128_FP8) {
+        if (block_m == 64) {
+            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 64>), grid, block, 0, s, a);
+            return moe_launch_status();
+        }
+        if (block_m == 128) {
+            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 128>), grid, block, 0, s, a);
+            return moe_launch_status();
+        }
+    }
+    return MOE_ERR_UNSUPPORTED;
 }
 
 template <bool GATEUP>
@@ -326,11 +375,18 @@ static int32_t launch_mode(int quant, int block_m, const GemmArgs& a, hipStream_
     return MOE_ERR_UNSUPPORTED;
 }
 
+int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
+                             const int* sorted_ids, const int* offsets, void* act, hipStream_t s);
+int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T,
+                           const int* offsets, void* out_perm, hipStream_t s);
+
 int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T, int block_m,
-                           int64_t max_rows, const int* sorted_ids, const int* block_expert, void* act,
-                           hipStream_t s) {
+                           int64_t max_rows, const int* sorted_ids, const int* block_expert, const int* offsets,
+                           void* act, hipStream_t s) {
+    if (block_m == 16) return stream_gateup_launch(L, a, a_scale, T, sorted_ids, offsets, act, s);
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     GemmArgs g{};
+    g.offsets = offsets;
     g.a = static_cast<const uint8_t*>(a);
     g.a_ld = static_cast<int64_t>(L->D) * elem;
     g.a_scale = a_scale;
@@ -355,10 +411,13 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
     return launch_mode<true>(L->quant, block_m, g, s);
 }
 
-int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int block_m,
-                         int64_t max_rows, const int* block_expert, void* out_perm, hipStream_t s) {
+int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T, int block_m,
+                         int64_t max_rows, const int* block_expert, const int* offsets, void* out_perm,
+                         hipStream_t s) {
+    if (block_m == 16) return stream_down_launch(L, act, act_scale, T, offsets, out_perm, s);
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     GemmArgs g{};
+    g.offsets = offsets;
     g.a = static_cast<const uint8_t*>(act);
     g.a_ld = static_cast<int64_t>(L->I) * elem;
     g.a_scale = act_scale;

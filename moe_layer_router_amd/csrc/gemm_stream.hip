@@ -1,0 +1,329 @@
+// Weight-streaming grouped GEMMs for small batches (decode).
+//
+// With few tokens per expert the expert GEMMs are bound by reading the
+// weights of the active experts once from HBM (the Qwen3 MI300X page, 2.1.2,
+// finds MoE inference memory-bound; its 2.1.4 tunes CU-level load balance at
+// low concurrency; the MI355X MoRI page notes that small-batch TP decode
+// gives tall-skinny expert GEMMs).  Design:
+//   - one workgroup = one expert x a slice of weight rows; the expert's rows
+//     (at most 16*MT, every expert holds at most T rows) are all handled by
+//     the wave that streams a weight slice, so each weight byte is read once;
+//   - no LDS: each lane streams 32 B of a weight row per 128-byte K step
+//     straight into MFMA operand registers (v_mfma_f32_16x16x128_f8f6f4, or
+//     two v_mfma_f32_16x16x32_bf16), the next step's loads in flight while
+//     the current step multiplies;
+//   - activation rows are tiny and stay in L2;
+//   - workgroups of experts without rows exit at once.
+#include "common.h"
+
+namespace moe {
+
+typedef int v8i_s __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf_s __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_s __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
+
+struct StreamArgs {
+    const uint8_t* a;          // gate_up: x / xq [T, K]; down: act / aq [R, K]
+    int64_t a_ld;              // bytes per row
+    const float* a_scale;      // PTPC: per row; block: [rows, K/128]
+    int a_scale_ld;
+    const int* sorted_ids;     // gate_up: flat ids; down: NULL (rows direct)
+    int topk, TK, sentinel;
+    const int* offsets;        // [E'+1] padded (multiples of 16)
+    const uint8_t* w;
+    int64_t w_expert_bytes;
+    const float* w_scale;
+    int64_t ws_expert;
+    int ws_ld;
+    int K;                     // elements
+    int I;                     // gate_up act columns
+    void* out;
+    int64_t out_ld;
+};
+
+template <int MODE>
+__device__ __forceinline__ void mfma16(const u32x8& a, const u32x8& b, v4f& acc) {
+    if constexpr (MODE == MOE_QUANT_NONE_BF16) {
+        const u32x4_s a0 = __builtin_shufflevector(a, a, 0, 1, 2, 3), a1 = __builtin_shufflevector(a, a, 4, 5, 6, 7);
+        const u32x4_s b0 = __builtin_shufflevector(b, b, 0, 1, 2, 3), b1 = __builtin_shufflevector(b, b, 4, 5, 6, 7);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_s, a0), __builtin_bit_cast(v8bf_s, b0),
+                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_s, a1), __builtin_bit_cast(v8bf_s, b1),
+                                                      acc, 0, 0, 0);
+    } else {
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_bit_cast(v8i_s, a), __builtin_bit_cast(v8i_s, b),
+                                                               acc, 0, 0, 0, 0, 0, 0);
+    }
+}
+
+// A lane's 32 operand bytes of one 128-byte K step: bytes [16q, 16q+16) and
+// [64+16q, 64+16q+16) with q = lane / 16, so each of the two load
+// instructions covers 64 contiguous bytes of every row it touches.  Activation
+// and weight operands use the same mapping, so the MFMA pairs matching K.
+__device__ __forceinline__ u32x8 ld32(const uint8_t* p) {
+#ifdef MOE_STREAM_NT
+    const u32x4_s lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4_s*>(p));
+    const u32x4_s hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4_s*>(p + 64));
+#else
+    const u32x4_s lo = *reinterpret_cast<const u32x4_s*>(p);
+    const u32x4_s hi = *reinterpret_cast<const u32x4_s*>(p + 64);
+#endif
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float silu_mul_s(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+__device__ __forceinline__ int src_row(const StreamArgs& p, bool gateup, int row, bool& valid) {
+    if (!gateup) { valid = true; return row; }
+    const int f = p.sorted_ids[row];
+    valid = f != p.sentinel;
+    return valid ? (f < p.TK ? f / p.topk : f - p.TK) : 0;
+}
+
+// TN: 16-row weight tiles per wave (gate_up: TN/2 gate + TN/2 up tiles).
+// MT: 16-row activation tiles (rows per expert <= 16*MT).  PF: K steps in
+// flight.  The steady-state loop has no data-dependent branch, so the
+// compiler can wait for exactly the step it is about to use.
+template <int MODE, bool GATEUP, int TN, int MT, int PF>
+__global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
+    constexpr bool BLOCKQ = MODE == MOE_QUANT_BLOCK128_FP8;
+    constexpr int COLS_W = GATEUP ? TN / 2 * 16 : TN * 16;     // output columns per wave
+    const int e = blockIdx.y;
+    const int row0 = p.offsets[e];
+    const int cnt = p.offsets[e + 1] - row0;                    // padded rows of this expert
+    if (cnt == 0) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c0 = (blockIdx.x * 4 + wave) * COLS_W;            // first output column of this wave
+    const int r16 = lane & 15, kq = (lane >> 4) * 16;
+
+    const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
+    const int64_t wrow = static_cast<int64_t>(p.K) * (MODE == MOE_QUANT_NONE_BF16 ? 2 : 1);
+    const uint8_t* bp[TN];
+    int wn0[TN];                                                  // first weight row of each tile
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        wn0[t] = GATEUP ? (t < TN / 2 ? c0 + t * 16 : p.I + c0 + (t - TN / 2) * 16) : c0 + t * 16;
+        bp[t] = wexp + (wn0[t] + r16) * wrow + kq;
+    }
+    // operand rows: row r16 of each M tile; rows past the segment or on a pad
+    // slot read a valid row and are zeroed by the epilogue's row mask
+    const uint8_t* ap[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int r = m * 16 + r16;
+        bool v = false;
+        const int src = r < cnt ? src_row(p, GATEUP, row0 + r, v) : 0;
+        ap[m] = p.a + static_cast<int64_t>(v ? src : (GATEUP ? 0 : row0)) * p.a_ld + kq;
+    }
+    // accumulator rows: (lane / 16) * 4 + i of each tile
+    int esrc[MT][4];
+    float emask[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = m * 16 + (lane >> 4) * 4 + i;
+            bool v = false;
+            const int src = r < cnt ? src_row(p, GATEUP, row0 + r, v) : 0;
+            esrc[m][i] = v ? src : (GATEUP ? 0 : row0);
+            emask[m][i] = v ? 1.0f : 0.0f;
+        }
+
+    v4f acc[MT][TN];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[m][t] = v4f{0, 0, 0, 0};
+
+    const int nk = static_cast<int>(wrow / 128);
+    // Each wave starts its K sweep at its own step (wrapping around), so the
+    // waves spread over the byte offsets of the weight rows.  The K order of a
+    // wave is fixed by its position: results stay deterministic.
+    const int kbeg = ((blockIdx.x * 4 + wave) * 5 + e * 3) % nk;
+
+    u32x8 bq[PF][TN], aqr[PF][MT];
+    float asq[PF][MT][4];
+    auto fill = [&](int j, int s) {
+        int ks = s + kbeg;
+        ks = ks >= nk ? ks - nk : ks;
+        const int64_t ko = static_cast<int64_t>(ks) * 128;
+#pragma unroll
+        for (int t = 0; t < TN; ++t) bq[j][t] = ld32(bp[t] + ko);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) aqr[j][m] = ld32(ap[m] + ko);
+        if constexpr (BLOCKQ) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) asq[j][m][i] = p.a_scale[static_cast<int64_t>(esrc[m][i]) * p.a_scale_ld + ks];
+        }
+    };
+    auto compute = [&](int j, int s) {
+        if constexpr (!BLOCKQ) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int t = 0; t < TN; ++t) mfma16<MODE>(aqr[j][m], bq[j][t], acc[m][t]);
+        } else {
+            int ks = s + kbeg;
+            ks = ks >= nk ? ks - nk : ks;
+            float wsc[TN];
+#pragma unroll
+            for (int t = 0; t < TN; ++t) wsc[t] = p.w_scale[e * p.ws_expert + (wn0[t] >> 7) * p.ws_ld + ks];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int t = 0; t < TN; ++t) {
+                    v4f part = v4f{0, 0, 0, 0};
+                    mfma16<MODE>(aqr[j][m], bq[j][t], part);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[m][t][i] += part[i] * (asq[j][m][i] * wsc[t]);
+                }
+        }
+    };
+
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+        if (j < nk) fill(j, j);
+    int s0 = 0;
+    // steady state: every refill targets a step < nk
+    for (; s0 + 2 * PF <= nk; s0 += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            compute(j, s0 + j);
+            fill(j, s0 + j + PF);
+        }
+    }
+    // tail: the last PF .. 2PF-1 steps
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        if (s0 + j < nk) {
+            compute(j, s0 + j);
+            if (s0 + j + PF < nk) fill(j, s0 + j + PF);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+        if (s0 + PF + j < nk) compute(j, s0 + PF + j);
+
+    // epilogue: lane holds column (lane & 15) and rows (lane / 16) * 4 + i of each tile
+    const int mtiles = cnt >> 4;
+    const float* wsx = MODE == MOE_QUANT_PTPC_FP8 ? p.w_scale + e * p.ws_expert : nullptr;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        if (m >= mtiles) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = m * 16 + (lane >> 4) * 4 + i;       // row within the expert segment
+            float rs = emask[m][i];
+            if constexpr (MODE == MOE_QUANT_PTPC_FP8) rs *= p.a_scale[esrc[m][i]];
+            const int64_t orow = static_cast<int64_t>(row0 + r) * p.out_ld;
+            if constexpr (GATEUP) {
+#pragma unroll
+                for (int t = 0; t < TN / 2; ++t) {
+                    const int col = c0 + t * 16 + (lane & 15);
+                    float g = acc[m][t][i] * rs, u = acc[m][t + TN / 2][i] * rs;
+                    if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
+                        g *= wsx[col];
+                        u *= wsx[p.I + col];
+                    }
+                    static_cast<uint16_t*>(p.out)[orow + col] = f32_to_bf16(silu_mul_s(g, u));
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < TN; ++t) {
+                    const int col = c0 + t * 16 + (lane & 15);
+                    float v = acc[m][t][i] * rs;
+                    if constexpr (MODE == MOE_QUANT_PTPC_FP8) v *= wsx[col];
+                    if constexpr (MODE == MOE_QUANT_NONE_BF16) static_cast<float*>(p.out)[orow + col] = v;
+                    else static_cast<uint16_t*>(p.out)[orow + col] = f32_to_bf16(v);
+                }
+            }
+        }
+    }
+}
+
+#ifndef MOE_STREAM_TN
+#define MOE_STREAM_TN 2
+#endif
+#ifndef MOE_STREAM_PF
+#define MOE_STREAM_PF 4
+#endif
+constexpr int kStreamTN = MOE_STREAM_TN;     // 16-row weight tiles per wave
+constexpr int kStreamPF = MOE_STREAM_PF;     // K steps in flight per wave
+
+template <int MODE, bool GATEUP>
+static int32_t stream_launch_mode(const StreamArgs& a, int Ep, int ncols, int T, hipStream_t s) {
+    constexpr int COLS_W = GATEUP ? kStreamTN / 2 * 16 : kStreamTN * 16;
+    const dim3 grid(static_cast<unsigned>(ncols / (4 * COLS_W)), static_cast<unsigned>(Ep)), block(256);
+    if (T <= 16) hipLaunchKernelGGL((stream_gemm_kernel<MODE, GATEUP, kStreamTN, 1, kStreamPF>), grid, block, 0, s, a);
+    else if (T <= 32) hipLaunchKernelGGL((stream_gemm_kernel<MODE, GATEUP, kStreamTN, 2, kStreamPF>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stream_gemm_kernel<MODE, GATEUP, kStreamTN, 4, kStreamPF>), grid, block, 0, s, a);
+    return moe_launch_status();
+}
+
+template <bool GATEUP>
+static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, int T, hipStream_t s) {
+    switch (quant) {
+        case MOE_QUANT_NONE_BF16: return stream_launch_mode<MOE_QUANT_NONE_BF16, GATEUP>(a, Ep, ncols, T, s);
+        case MOE_QUANT_PTPC_FP8: return stream_launch_mode<MOE_QUANT_PTPC_FP8, GATEUP>(a, Ep, ncols, T, s);
+        case MOE_QUANT_BLOCK128_FP8: return stream_launch_mode<MOE_QUANT_BLOCK128_FP8, GATEUP>(a, Ep, ncols, T, s);
+    }
+    return MOE_ERR_UNSUPPORTED;
+}
+
+// Columns per workgroup: gate_up 128 act columns, down 256 output columns.
+int stream_cols_per_block(bool gateup) { return gateup ? 4 * (kStreamTN / 2) * 16 : 4 * kStreamTN * 16; }
+
+int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
+                             const int* sorted_ids, const int* offsets, void* act, hipStream_t s) {
+    const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    StreamArgs g{};
+    g.a = static_cast<const uint8_t*>(a);
+    g.a_ld = static_cast<int64_t>(L->D) * elem;
+    g.a_scale = a_scale;
+    g.a_scale_ld = L->D / 128;
+    g.sorted_ids = sorted_ids;
+    g.topk = L->top_k;
+    g.TK = T * L->top_k;
+    g.sentinel = T * (L->top_k + L->n_shared);
+    g.offsets = offsets;
+    g.w = static_cast<const uint8_t*>(L->w13);
+    g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
+    g.w_scale = L->w13_scale;
+    g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? 2LL * L->I
+                                                  : static_cast<int64_t>(2 * L->I / 128) * (L->D / 128);
+    g.ws_ld = L->D / 128;
+    g.K = L->D;
+    g.I = L->I;
+    g.out = act;
+    g.out_ld = L->I;
+    return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s);
+}
+
+int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T,
+                           const int* offsets, void* out_perm, hipStream_t s) {
+    const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    StreamArgs g{};
+    g.a = static_cast<const uint8_t*>(act);
+    g.a_ld = static_cast<int64_t>(L->I) * elem;
+    g.a_scale = act_scale;
+    g.a_scale_ld = L->I / 128;
+    g.sorted_ids = nullptr;
+    g.offsets = offsets;
+    g.w = static_cast<const uint8_t*>(L->w2);
+    g.w_expert_bytes = static_cast<int64_t>(L->D) * L->I * elem;
+    g.w_scale = L->w2_scale;
+    g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? static_cast<int64_t>(L->D)
+                                                  : static_cast<int64_t>(L->D / 128) * (L->I / 128);
+    g.ws_ld = L->I / 128;
+    g.K = L->I;
+    g.I = L->I;
+    g.out = out_perm;
+    g.out_ld = L->D;
+    return stream_launch<false>(L->quant, g, L->E + L->n_shared, L->D, T, s);
+}
+
+}  // namespace moe

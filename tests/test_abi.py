@@ -85,6 +85,9 @@ def test_layer_validation_and_workspace():
     # unsupported shapes / block sizes
     assert lib.moe_forward_workspace_size(ctypes.byref(_desc(I=200)), 100, 64) == 0
     assert lib.moe_forward_workspace_size(ctypes.byref(d), 100, 48) == 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(_desc(quant=2)), 100, 64) == 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(d), 100, 16) == 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(d), 64, 16) > 0
     assert lib.moe_forward(ctypes.byref(_desc(I=200)), None, None, 4, 0, None, None, 0, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_forward(ctypes.byref(_desc(w13=None)), None, None, 4, 0, None, None, 0, None) \
         == L.MOE_ERR_INVALID_ARG

@@ -210,7 +210,9 @@ def test_quant_weights(quant):
 
 @pytest.mark.parametrize("name,block_m", [("tiny_bf16", 32), ("bf16_multi_tile_r", 64), ("qwen3_30b_a3b_ptpc", 32),
                                           ("qwen3_235b_prefill_ptpc_r", 128), ("qwen3_235b_prefill_ptpc_r", 64),
-                                          ("deepseek_r1_block_fp8_r", 64), ("deepseek_r1_block_fp8_r", 32)])
+                                          ("deepseek_r1_block_fp8_r", 32),
+                                          ("tiny_bf16", 16), ("bf16_small_t20", 16), ("qwen3_235b_decode_ptpc", 16),
+                                          ("qwen3_235b_decode_ptpc_t64", 16), ("deepseek_r1_block_fp8_small", 16)])
 def test_gateup_silu_entry(name, block_m):
     """act rows of the gate/up GEMM vs the oracle's, from the same x, routing
     and weights (routing and x codes are bit-exact upstream)."""
@@ -244,7 +246,9 @@ def test_gateup_silu_entry(name, block_m):
 
 
 @pytest.mark.parametrize("name,block_m", [("tiny_bf16", 32), ("qwen3_235b_prefill_ptpc_r", 128),
-                                          ("qwen3_30b_a3b_ptpc", 64), ("deepseek_r1_block_fp8_r", 64)])
+                                          ("qwen3_30b_a3b_ptpc", 64), ("deepseek_r1_block_fp8_r", 32),
+                                          ("tiny_bf16", 16), ("qwen3_235b_decode_ptpc", 16),
+                                          ("qwen3_235b_decode_ptpc_t64", 16), ("deepseek_r1_block_fp8_small", 16)])
 def test_down_entry(name, block_m):
     """out_perm of the down GEMM on a synthetic act buffer (same values on both
     sides), quantized per row / 1x128 by each side."""
