@@ -34,6 +34,28 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+    counter record, or None when the kernel source changed since (or the
+    record is for another workload)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "grouped_gemm_gateup_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.strip() and not line.startswith("#") and ":" in line:
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    src = os.path.join(ROOT, rec.get("kernel_source", ""))
+    if rec.get("workload") != workload or not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        return None
+    kib = float(rec["fetch_kib"]) * float(rec["fetch_factor"]) + float(rec["write_kib"]) * float(rec["write_factor"])
+    return int(kib * 1024)
+
+
 class Steps:
     """The path through the step entries, on buffers carved from the layer's
     workspace (the same layout moe_forward uses)."""
@@ -202,9 +224,11 @@ def main():
     log("building", w.name)
     case = build_case(w)
     if args.copy_probe_mib:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        # one elementwise kernel that reads and writes exactly copy_probe_mib MiB
+        src = torch.ones((args.copy_probe_mib << 20) // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
     st = Steps(case.layer, w, case.x, case.logits, args.block_m)
@@ -252,7 +276,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "top_k": w.k, "I": w.I,
                    "n_shared": w.n_shared, "quant": w.quant, "scoring": w.scoring, "block_m": st.B},
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm_gateup_silu", "achieved": round(gu_tf, 1),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(gu_tf / peak, 4), "traffic": None,
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(gu_tf / peak, 4), "traffic": measured_traffic(w.name),
                      "avg_launch_ms": round(gu_ms, 4), "flops_per_launch": gu_flops},
         "kernels": {"gateup_ms": round(gu_ms, 4), "down_ms": round(dn_ms, 4),
                     "down_tflops": round(dn_flops / (dn_ms * 1e-3) / 1e12, 1),

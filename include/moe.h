@@ -185,7 +185,7 @@ int32_t moe_permute_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t
  * Outputs q [M, K] uint8 and scale [M] or [M, K/128] fp32.
  * valid_rows: device int32 scalar or NULL; rows >= *valid_rows are left
  * untouched (used for the data-dependent row count of the permuted buffer).
- * Limits: K % 8 == 0, K <= 65536.
+ * Limits: K % 8 == 0, K <= 16384.
  */
 int32_t moe_quant_ptpc_fp8(const void* x_bf16, int64_t M, int32_t K, int32_t group,
                            const int32_t* valid_rows, uint8_t* q, float* scale, void* stream);
@@ -209,9 +209,11 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
  * a: quant 0: x bf16 [T, D]; quant 1/2: codes [T, D] with a_scale [T] or
  * [T, D/128].  act: [R, I] bf16 where R = moe_permute_max_rows(...).
  * Pad rows (sentinel) get act = 0; rows at or past expert_offsets[E'] are not
- * written.  block_m must be one of 16, 32, 64, 128 for this entry and
- * moe_grouped_gemm_down, and equal to the block_m of moe_permute_align.
- * I % 64 == 0 and D % 128 == 0 (FP8) or D % 64 == 0 (bf16).
+ * written.  block_m must equal the block_m of moe_permute_align and be one
+ * of: 16 (weight-streaming kernels for small batches; requires T <= 64 and
+ * at most T rows per expert, which holds when each token's k ids are
+ * distinct), 32, 64 or 128 (LDS-tiled kernels; the blockwise FP8 mode
+ * supports 16 and 32 only).  Shapes: I % 128 == 0 and D % 256 == 0.
  */
 int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
                                      const float* a_scale, int32_t T, int32_t block_m,
@@ -221,7 +223,9 @@ int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
 
 /*
  * Grouped GEMM down: out_perm[r] = act[r] . W2[e]^T for the valid rows
- * (dequantized by the row scale(s) and the weight scales).  act: quant 0:
+ * (dequantized by the row scale(s) and the weight scales).  Same block_m and
+ * shape rules as moe_grouped_gemm_gateup_silu; pad rows of act must hold
+ * zeros (moe_grouped_gemm_gateup_silu writes them so).  act: quant 0:
  * bf16 [R, I]; quant 1/2: codes [R, I] with act_scale [R] or [R, I/128].
  * out_perm [R, D]: fp32 for quant 0, bf16 for quant 1/2.
  */

@@ -75,6 +75,7 @@ int32_t check_layer(const moe_layer_desc* L) {
                   L->quant == MOE_QUANT_BLOCK128_FP8);
     MOE_CHECK_ARG(L->w13 != nullptr && L->w2 != nullptr);
     if (L->quant != MOE_QUANT_NONE_BF16) MOE_CHECK_ARG(L->w13_scale != nullptr && L->w2_scale != nullptr);
+    // column tiles of the grouped GEMMs: 128 act columns, 256 output columns
     MOE_CHECK_SUP(L->I % 128 == 0 && L->D % 256 == 0);
     MOE_CHECK_SUP(L->D <= 16384 && L->I <= 16384);
     return MOE_OK;
