@@ -13,11 +13,14 @@
 //     rows and the matching 128 up rows, giving 128 act columns; down: 256
 //     output columns);
 //   - K advances 128 bytes per step (128 e4m3 or 64 bf16 elements; one
-//     128-element scale block in the blockwise mode).  Global loads run three
-//     steps ahead through a ring of three register stages; LDS holds two
-//     stages of 128-byte rows whose 16-byte chunks are XOR-swizzled by row, so
-//     the 16 lanes of an MFMA operand read hit distinct banks; one barrier
-//     per step; the steady-state loop has no data-dependent branch;
+//     128-element scale block in the blockwise mode).  Tiles move from global
+//     memory straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes
+//     land at M0 + 16*lane, no register staging), two steps ahead, into three
+//     LDS stages of 128-byte rows whose 16-byte chunks are XOR-swizzled by row
+//     (the swizzle is applied on the global side, so the 16 lanes of an MFMA
+//     operand read hit distinct banks); each wave waits for its own copies
+//     with an explicit vmcnt, then one barrier per step; all MFMA operands of
+//     a step are read from LDS before its MFMAs issue;
 //   - waves split the tile 2x2 (BM = 128) or 1x4 (BM <= 64) and run 32x32
 //     MFMAs (v_mfma_f32_32x32x64_f8f6f4 or v_mfma_f32_32x32x16_bf16); A and B
 //     operands take the same lane -> K mapping, so the reduction pairs
@@ -67,7 +70,29 @@ __device__ __forceinline__ int lds_off(int row, int c) { return row * kBK + ((c 
 
 __device__ __forceinline__ u32x4 lds16(const uint8_t* L, int off) { return *reinterpret_cast<const u32x4*>(L + off); }
 
+__device__ __forceinline__ v8i cat8(u32x4 lo, u32x4 hi) {
+    return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Global -> LDS copies.  Each lane's bytes land at M0 + size * lane; M0 must
+// be wave-uniform.  Issued as inline asm so that the only waits on them are
+// the explicit vmcnt_wait below (the compiler would otherwise drain every
+// outstanding copy before each LDS read).  The main loop issues no other
+// vector-memory instruction, so vmcnt counts exactly these copies.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int MODE, bool GATEUP, int BM>
 __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) {
@@ -84,12 +109,16 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
     constexpr int TILE_N = GATEUP ? 128 : kBRows;
     constexpr bool BLOCKQ = MODE == MOE_QUANT_BLOCK128_FP8;
     constexpr int STAGE = (BM + kBRows) * kBK;
-    constexpr int kRing = BLOCKQ ? 2 : 3;    // register stages (loads in flight ahead of use)
     static_assert(TM >= 1 && TN >= 2 && A_CH >= 1, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    constexpr int NSTAGE = 3;
+    constexpr int A_IN = BM / 32;              // 1 KB copies (8 rows) of A per wave per step
+    constexpr int B_IN = kBRows / 32;          // 1 KB copies of B per wave per step
+    constexpr int SC_IN = BLOCKQ ? 1 : 0;      // blockwise: one 4-byte-lane copy of row scales
+    constexpr int N_IN = A_IN + B_IN + SC_IN;  // copies per wave per step (vmcnt units)
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NSTAGE * STAGE];
     __shared__ float s_rowscale[BM];          // PTPC: row scale; other modes: row mask (pad rows 0)
-    __shared__ float s_ascale[2][BM];         // block mode: row scale of the stage's K block
+    __shared__ __attribute__((aligned(16))) float s_ascale[NSTAGE][256];   // blockwise: row scales of a stage
     __shared__ int s_tok[BM];
 
     // tile order: expert-major, weight tile, then row block; XCD-contiguous
@@ -121,52 +150,50 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
     }
     __syncthreads();
 
-    // global sources and LDS slots of this thread's chunks (same every step)
-    const uint8_t* a_src[A_CH];
-    int a_dst[A_CH];
+    // Copy j of a wave fills 8 LDS rows: lane i writes row 8j' + i/8 (j' the
+    // wave's j-th block of 8 rows), physical chunk i%8, which must hold the
+    // logical chunk (i%8) ^ swizzle(row) of that row.
+    const int crow = lane >> 3, cphys = lane & 7;
+    const uint8_t* a_src[A_IN];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int q = tid + 256 * i;
-        const int r = q >> 3, c = q & 7;
-        a_src[i] = p.a + static_cast<int64_t>(s_tok[r]) * p.a_ld + c * 16;
-        a_dst[i] = lds_off(r, c);
+    for (int j = 0; j < A_IN; ++j) {
+        const int r = (wave + 4 * j) * 8 + crow;
+        const int c = cphys ^ ((r >> 1) & 7);
+        a_src[j] = p.a + static_cast<int64_t>(s_tok[r]) * p.a_ld + c * 16;
     }
     const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
     const int64_t wrow_bytes = static_cast<int64_t>(p.K) * ELEM;
-    uint32_t b_src[B_CH];                                   // byte offsets within the expert
-    int b_dst[B_CH];
+    uint32_t b_src[B_IN];                                   // byte offsets within the expert
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int q = tid + 256 * i;
-        const int r = q >> 3, c = q & 7;
+    for (int j = 0; j < B_IN; ++j) {
+        const int r = (wave + 4 * j) * 8 + crow;             // weight tile row
+        const int c = cphys ^ (((BM + r) >> 1) & 7);
         const int wr = GATEUP ? (r < 128 ? n0 + r : p.I + n0 + r - 128) : n0 + r;
-        b_src[i] = static_cast<uint32_t>(wr * wrow_bytes + c * 16);
-        b_dst[i] = lds_off(BM + r, c);
+        b_src[j] = static_cast<uint32_t>(wr * wrow_bytes + c * 16);
+    }
+    // blockwise: wave w copies the scales of rows 64w .. 64w+63 (rows past BM
+    // read row 0 into unused slots)
+    const float* sc_src = nullptr;
+    if constexpr (BLOCKQ) {
+        const int r = wave * 64 + lane;
+        sc_src = p.a_scale + static_cast<int64_t>(s_tok[r < BM ? r : 0]) * p.a_scale_ld;
     }
     const int nk = static_cast<int>(wrow_bytes / kBK);
-    int ras_tok = -1;
-    if constexpr (BLOCKQ) ras_tok = tid < BM ? (s_rowscale[tid] == 0.0f ? -1 : s_tok[tid]) : -1;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+    const uint32_t sc0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_ascale[0][0]));
 
-    u32x4 ra[kRing][A_CH], rb[kRing][B_CH];
-    float ras[kRing];
-#define MOE_GLOAD(J, S)                                                                                   \
-    do {                                                                                                  \
-        const int64_t ko_ = static_cast<int64_t>(S) * kBK;                                                \
-        _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[J][i] = *reinterpret_cast<const u32x4*>(a_src[i] + ko_); \
-        _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[J][i] = *reinterpret_cast<const u32x4*>(wexp + b_src[i] + ko_); \
-        if constexpr (BLOCKQ) {                                                                           \
-            ras[J] = ras_tok >= 0 ? p.a_scale[static_cast<int64_t>(ras_tok) * p.a_scale_ld + (S)] : 0.0f; \
-        }                                                                                                 \
-    } while (0)
-#define MOE_LSTORE(J, BUF)                                                                                \
-    do {                                                                                                  \
-        uint8_t* L_ = lds + (BUF) * STAGE;                                                                \
-        _Pragma("unroll") for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4*>(L_ + a_dst[i]) = ra[J][i]; \
-        _Pragma("unroll") for (int i = 0; i < B_CH; ++i) *reinterpret_cast<u32x4*>(L_ + b_dst[i]) = rb[J][i]; \
-        if constexpr (BLOCKQ) {                                                                           \
-            if (tid < BM) s_ascale[BUF][tid] = ras[J];                                                    \
-        }                                                                                                 \
-    } while (0)
+    // issue the copies of K step S into LDS stage BUF (uniform M0 per copy)
+    auto issue = [&](int S, int buf) {
+        const int64_t ko = static_cast<int64_t>(S) * kBK;
+        const uint32_t st = lds0 + buf * STAGE;
+#pragma unroll
+        for (int j = 0; j < A_IN; ++j)
+            dma16(a_src[j] + ko, __builtin_amdgcn_readfirstlane(st + (wave + 4 * j) * 8 * kBK));
+#pragma unroll
+        for (int j = 0; j < B_IN; ++j)
+            dma16(wexp + b_src[j] + ko, __builtin_amdgcn_readfirstlane(st + (BM + (wave + 4 * j) * 8) * kBK));
+        if constexpr (BLOCKQ) dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 256 + wave * 64) * 4));
+    };
 
     // LDS rows of this lane's operands
     int a_row[TM], b_row[TN];
@@ -187,61 +214,51 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16f{};
 
-    // one 128-byte K step on LDS stage `buf`
+    // one 128-byte K step on LDS stage `buf`: all operand fragments first, then the MFMAs
     auto step = [&](int buf, int s) {
         const uint8_t* L = lds + buf * STAGE;
         if constexpr (MODE == MOE_QUANT_NONE_BF16) {
+            v8bf av[4][TM], bv[4][TN];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                v8bf av[TM];
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm) av[tm] = __builtin_bit_cast(v8bf, lds16(L, lds_off(a_row[tm], 2 * kk + h)));
+                for (int tm = 0; tm < TM; ++tm) av[kk][tm] = __builtin_bit_cast(v8bf, lds16(L, lds_off(a_row[tm], 2 * kk + h)));
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    const v8bf bv = __builtin_bit_cast(v8bf, lds16(L, lds_off(b_row[tn], 2 * kk + h)));
+                for (int tn = 0; tn < TN; ++tn) bv[kk][tn] = __builtin_bit_cast(v8bf, lds16(L, lds_off(b_row[tn], 2 * kk + h)));
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
                     for (int tm = 0; tm < TM; ++tm)
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv, acc[tm][tn], 0, 0, 0);
-                }
-            }
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][tm], bv[kk][tn], acc[tm][tn], 0, 0, 0);
         } else {
-            v8i av[2][TM];
+            v8i av[2][TM], bv[2][TN];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const u32x4 lo = lds16(L, lds_off(a_row[tm], 4 * kk + 2 * h));
-                    const u32x4 hi = lds16(L, lds_off(a_row[tm], 4 * kk + 2 * h + 1));
-                    av[kk][tm] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                }
-            float as[BLOCKQ ? TM : 1][BLOCKQ ? 16 : 1];
-            if constexpr (BLOCKQ) {
+            for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
+                    av[kk][tm] = cat8(lds16(L, lds_off(a_row[tm], 4 * kk + 2 * h)), lds16(L, lds_off(a_row[tm], 4 * kk + 2 * h + 1)));
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        as[tm][i] = s_ascale[buf][wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
+                for (int tn = 0; tn < TN; ++tn)
+                    bv[kk][tn] = cat8(lds16(L, lds_off(b_row[tn], 4 * kk + 2 * h)), lds16(L, lds_off(b_row[tn], 4 * kk + 2 * h + 1)));
             }
+            if constexpr (!BLOCKQ) {
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                v8i bv[2];
+                for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const u32x4 lo = lds16(L, lds_off(b_row[tn], 4 * kk + 2 * h));
-                    const u32x4 hi = lds16(L, lds_off(b_row[tn], 4 * kk + 2 * h + 1));
-                    bv[kk] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                }
-                if constexpr (!BLOCKQ) {
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
+                    for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
                         for (int tm = 0; tm < TM; ++tm)
                             // e4m3 x e4m3 (format selectors 0, 0), no block scaling
-                            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[kk][tm], bv[kk], acc[tm][tn],
+                            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[kk][tm], bv[kk][tn], acc[tm][tn],
                                                                                           0, 0, 0, 0, 0, 0);
-                } else {
-                    // the step is one 128-element scale block:
-                    // acc += part * a_scale(row, kb) * w_scale(n-block, kb)
+            } else {
+                // the step is one 128-element scale block:
+                // acc += part * a_scale(row, kb) * w_scale(n-block, kb)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
                     const int wr0 = b_row[tn] - BM - (lane & 31);
                     const int wr = GATEUP ? (wr0 < 128 ? n0 + wr0 : p.I + n0 + wr0 - 128) : n0 + wr0;
                     const float wsc = p.w_scale[e * p.ws_expert + (wr >> 7) * p.ws_ld + s];
@@ -250,48 +267,44 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
                         v16f part = v16f{};
 #pragma unroll
                         for (int kk = 0; kk < 2; ++kk)
-                            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[kk][tm], bv[kk], part, 0, 0, 0, 0,
-                                                                                   0, 0);
+                            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[kk][tm], bv[kk][tn], part, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) acc[tm][tn][i] += part[i] * (as[tm][i] * wsc);
+                        for (int i = 0; i < 16; ++i) {
+                            const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                            acc[tm][tn][i] += part[i] * (s_ascale[buf][row] * wsc);
+                        }
                     }
                 }
             }
         }
     };
 
-    // prologue: stages 0..2 in flight, stage 0 into LDS buffer 0
-#pragma unroll
-    for (int j = 0; j < kRing; ++j)
-        if (j < nk) MOE_GLOAD(j, j);
-    MOE_LSTORE(0, 0);
+    // prologue: steps 0 and 1 in flight; wait for step 0
+    issue(0, 0);
+    if (nk > 1) {
+        issue(1, 1);
+        vmcnt_wait<N_IN>();
+    } else {
+        vmcnt_wait<0>();
+    }
     __syncthreads();
     int s = 0;
-    // steady state, kRing steps per trip; step s uses LDS buffer s & 1 and
-    // register stage s % kRing (refilled with step s + kRing right away)
-    for (; s + 2 * kRing <= nk; s += kRing) {
-#pragma unroll
-        for (int j = 0; j < kRing; ++j) {
-            const int buf = (s + j) & 1;
-            MOE_GLOAD(j, s + j + kRing);
-            step(buf, s + j);
-            MOE_LSTORE((j + 1) % kRing, buf ^ 1);
-            __syncthreads();
-        }
+    // steady state: the copies of step s + 2 go out, step s computes, then
+    // this wave's copies of step s + 1 are waited for (those of s + 2 may
+    // stay in flight) and the barrier publishes them and frees stage s
+    for (; s + 2 < nk; ++s) {
+        const int b = s % NSTAGE;
+        issue(s + 2, (s + 2) % NSTAGE);
+        step(b, s);
+        vmcnt_wait<N_IN>();
+        __syncthreads();
     }
-    // tail: fewer than 2 * kRing steps remain
-#pragma unroll
-    for (int j = 0; j < 2 * kRing; ++j) {
-        const int t = s + j;
-        if (t < nk) {
-            if (j < kRing && t + kRing < nk) MOE_GLOAD(j, t + kRing);
-            step(t & 1, t);
-            if (t + 1 < nk) MOE_LSTORE((j + 1) % kRing, (t + 1) & 1);
-            __syncthreads();
-        }
+    // last two steps (step nk-1 may already be the only one left)
+    for (; s < nk; ++s) {
+        step(s % NSTAGE, s);
+        vmcnt_wait<0>();
+        __syncthreads();
     }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
 
     // ------------------------------------------------------------ epilogue
     const float* wsx = (MODE == MOE_QUANT_PTPC_FP8) ? p.w_scale + e * p.ws_expert : nullptr;
@@ -311,11 +324,9 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
                 for (int i = 0; i < 16; ++i) {
                     const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                     float g = acc[tm][tg][i], u = acc[tm][tg + TN / 2][i];
-                    if constexpr (!BLOCKQ) {
-                        const float rs = s_rowscale[row];
-                        g = g * rs * swg;
-                        u = u * rs * swu;
-                    }
+                    const float rs = s_rowscale[row];
+                    g = g * rs * swg;
+                    u = u * rs * swu;
                     out[static_cast<int64_t>(m0 + row) * p.out_ld + n0 + col] = f32_to_bf16(silu_mul(g, u));
                 }
             }
@@ -331,8 +342,7 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                    float v = acc[tm][tn][i];
-                    if constexpr (!BLOCKQ) v = v * s_rowscale[row] * sw;
+                    const float v = acc[tm][tn][i] * s_rowscale[row] * sw;
                     const int64_t o = static_cast<int64_t>(m0 + row) * p.out_ld + n0 + col;
                     if constexpr (MODE == MOE_QUANT_NONE_BF16) static_cast<float*>(p.out)[o] = v;
                     else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
