@@ -212,8 +212,8 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
  * written.  block_m must equal the block_m of moe_permute_align and be one
  * of: 16 (weight-streaming kernels for small batches; requires T <= 64 and
  * at most T rows per expert, which holds when each token's k ids are
- * distinct), 32, 64 or 128 (LDS-tiled kernels; the blockwise FP8 mode
- * supports 16 and 32 only).  Shapes: I % 128 == 0 and D % 256 == 0.
+ * distinct), 32, 64, 128 or 256 (LDS-tiled kernels; the blockwise FP8
+ * mode supports 16 and 32 only).  Shapes: I % 128 == 0 and D % 256 == 0.
  */
 int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
                                      const float* a_scale, int32_t T, int32_t block_m,

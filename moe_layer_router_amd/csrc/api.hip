@@ -49,7 +49,7 @@ constexpr int kStreamMaxT = 64;
 bool block_m_ok(int quant, int block_m, int T) {
     if (block_m == 16) return T <= kStreamMaxT;
     if (block_m == 32) return true;
-    return (block_m == 64 || block_m == 128) && quant != MOE_QUANT_BLOCK128_FP8;
+    return (block_m == 64 || block_m == 128 || block_m == 256) && quant != MOE_QUANT_BLOCK128_FP8;
 }
 
 int32_t check_routing(int E, int k, int scoring, int n_groups, int topk_groups) {

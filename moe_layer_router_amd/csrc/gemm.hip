@@ -7,32 +7,44 @@
 // DeepSeek-R1 layer's blockwise FP8 (MI355X MoRI page) uses 1x128 activation
 // and 128x128 weight scales.
 //
-// Layout of one workgroup (256 threads, 4 waves, one workgroup per CU):
-//   - a tile of BM permuted rows of one expert (the permutation pads every
-//     expert to a multiple of BM) times 256 weight rows (gate_up: 128 gate
-//     rows and the matching 128 up rows, giving 128 act columns; down: 256
-//     output columns);
-//   - K advances 128 bytes per step (128 e4m3 or 64 bf16 elements; one
-//     128-element scale block in the blockwise mode).  Tiles move from global
-//     memory straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes
-//     land at M0 + 16*lane, no register staging), two steps ahead, into three
-//     LDS stages of 128-byte rows whose 16-byte chunks are XOR-swizzled by row
-//     (the swizzle is applied on the global side, so the 16 lanes of an MFMA
-//     operand read hit distinct banks); each wave waits for its own copies
-//     with an explicit vmcnt, then one barrier per step; all MFMA operands of
-//     a step are read from LDS before its MFMAs issue;
-//   - waves split the tile 2x2 (BM = 128) or 1x4 (BM <= 64) and run 32x32
-//     MFMAs (v_mfma_f32_32x32x64_f8f6f4 or v_mfma_f32_32x32x16_bf16); A and B
-//     operands take the same lane -> K mapping, so the reduction pairs
-//     matching K whatever order the matrix core sums in;
-//   - pad rows read a real row and are zeroed by a row mask in the epilogue;
-//   - tiles are ordered expert by expert, weight tile by weight tile, row
-//     block fastest, and each XCD (workgroup id mod 8) takes a contiguous
-//     range of that order: the row blocks of one expert that share a weight
-//     tile run together on one XCD and share it through its L2;
-//   - the epilogue dequantizes (row scale x channel scale), applies
-//     silu(g) * u for gate_up, rounds to bf16 and stores.
+// One workgroup per CU (256 threads, 4 waves in a WM x WN grid) computes a
+// tile of BM permuted rows of one expert (the permutation pads every expert
+// to a multiple of BM) times WN x 32*TN weight rows.  Wave (wm, wn) owns
+// BM/WM rows and 32*TN weight rows (gate_up: 16*TN gate rows and the
+// matching up rows, so gate and up of an act column meet in one wave).
+//
+// Data movement.  K advances in 128-byte steps (128 e4m3 or 64 bf16
+// elements; one step is one 128-element scale block in the blockwise mode).
+// Operand rows move from global memory straight into LDS with
+// global_load_lds_dwordx4 (lane i's 16 bytes land at M0 + 16 i): one copy
+// instruction moves 8 rows x 128 contiguous bytes, so every L1-to-L2 request
+// carries a whole 128-byte line; the number of such requests, not bytes, is
+// what bounds the copy rate per CU.  LDS rows are 128 bytes with their
+// 16-byte chunks XOR-swizzled by row (applied on the global side) so that the
+// MFMA operand reads are free of bank conflicts.  NS (2 or 3) LDS stages form
+// a ring; the copies of step S + NS - 1 go out while step S is computed.
+//
+// Compute.  Each 128-byte step is two 64-byte half-steps of 32x32 MFMAs
+// (v_mfma_f32_32x32x64_f8f6f4 or two v_mfma_f32_32x32x16_bf16).  Lane l
+// supplies row (l mod 32) and bytes [32q, 32q + 32) of a half-step (q = l/32)
+// for both operands, so the reduction pairs matching K whatever order the
+// matrix core sums in.  Operand fragments are double-buffered in registers:
+// while the MFMAs of one half-step run, the fragments of the next are read
+// from LDS, and the MFMAs, LDS reads and copies are interleaved one by one
+// (pinned with scheduling barriers) so that a memory instruction stalled at
+// issue overlaps a running MFMA.  One wait + barrier per 128-byte step.
+//
+// Pad rows read a real row and are zeroed by a row mask in the epilogue.
+// Tiles are ordered expert by expert, weight tile by weight tile, row block
+// fastest, and each XCD (workgroup id mod 8) takes a contiguous range of
+// that order, so the row blocks of one expert that share a weight tile run
+// together on one XCD and share it through its L2.  The epilogue
+// dequantizes (row scale x channel scale), applies silu(g) * u for gate_up,
+// rounds to bf16 and stores through a buffer resource.
 #include "common.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace moe {
 
@@ -41,8 +53,25 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 128;       // K bytes per step
-constexpr int kBRows = 256;    // weight rows per tile
+constexpr int kRow = 128;          // K bytes per step = LDS row width
+constexpr int kLdsBudget = 150 * 1024;
+
+// Waves per workgroup and their grid.  One wave per SIMD cannot keep enough
+// LDS reads in flight to feed its MFMAs from the 128 x 256 tile below 256
+// rows; the 256-row tile runs 8 waves (2 per SIMD, 2 x 4, each 128 x 64),
+// which doubles the LDS read rate the CU sustains.  Row tiles of 128 use a
+// 2 x 2 grid of 4 waves, smaller ones 1 x 4.
+constexpr int nw_of(int bm) { return bm == 256 ? 8 : 4; }
+constexpr int wm_of(int bm) { return bm >= 128 ? 2 : 1; }
+
+// 32-row weight tiles per wave: 4 for PTPC where the weight rows divide into
+// WN x 128 (gate_up: 2I rows as WN waves x (64 gate + 64 up)); else 2 (the
+// bf16 and blockwise modes keep more live registers per tile, and the
+// 8-wave tile holds 128 x 64 per wave)
+static int tn_of(int mode, int weight_rows, int bm) {
+    if (bm == 256) return 2;
+    return mode == MOE_QUANT_PTPC_FP8 && weight_rows % ((4 / wm_of(bm)) * 128) == 0 ? 4 : 2;
+}
 
 struct GemmArgs {
     const uint8_t* a;          // activation rows (bf16 or e4m3)
@@ -62,11 +91,12 @@ struct GemmArgs {
     int I;                     // gate_up: act columns; weight rows 2I
     void* out;
     int64_t out_ld;            // elements per output row
-    int n_ntiles, n_tiles;
+    int n_ntiles, n_tiles;     // weight tiles per row block; tiles the grid covers (row blocks of max_rows)
+    int n_exp;                 // E' = E + n_shared: offsets[n_exp] is the padded row total
 };
 
 // byte offset of (row, logical 16-byte chunk c) in a 128-byte-row LDS stage
-__device__ __forceinline__ int lds_off(int row, int c) { return row * kBK + ((c ^ ((row >> 1) & 7)) << 4); }
+__device__ __forceinline__ int lds_off(int row, int c) { return row * kRow + ((c ^ ((row >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ u32x4 lds16(const uint8_t* L, int off) { return *reinterpret_cast<const u32x4*>(L + off); }
 
@@ -94,37 +124,59 @@ __device__ __forceinline__ void vmcnt_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int MODE, bool GATEUP, int BM>
-__global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) {
+// compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>)
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Raw buffer resource over one output tile (stride 0, byte-range checked;
+// the offsets of one tile always fit in 32 bits)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), 0x7fffffff, 0x00020000);
+}
+
+template <int MODE, bool GATEUP, int BM, int TN>
+__global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const GemmArgs p) {
     constexpr int ELEM = MODE == MOE_QUANT_NONE_BF16 ? 2 : 1;
-    constexpr int WM = BM >= 128 ? 2 : 1;
-    constexpr int WN = 4 / WM;
-    constexpr int WROWS = BM / WM;          // rows per wave
-    constexpr int TM = WROWS / 32;
-    constexpr int WCOLS = kBRows / WN;       // weight rows per wave
-    constexpr int TN = WCOLS / 32;
-    constexpr int G = 128 / WN;              // gate_up: gate (and up) rows per wave
-    constexpr int A_CH = BM * 8 / 256;       // 16-byte A chunks per thread per step
-    constexpr int B_CH = kBRows * 8 / 256;   // 16-byte B chunks per thread per step
-    constexpr int TILE_N = GATEUP ? 128 : kBRows;
+    constexpr int NW = nw_of(BM), NT = NW * 64;
+    constexpr int WM = wm_of(BM), WN = NW / WM;
+    constexpr int TM = BM / (32 * WM);
+    constexpr int WCOLS = TN * 32;              // weight rows per wave
+    constexpr int NROWS = WN * WCOLS;           // weight rows per workgroup
+    constexpr int HALF = WCOLS / 2;             // gate_up: gate (and up) rows per wave
+    constexpr int TILE_N = GATEUP ? WN * HALF : NROWS;   // output columns per workgroup
     constexpr bool BLOCKQ = MODE == MOE_QUANT_BLOCK128_FP8;
-    constexpr int STAGE = (BM + kBRows) * kBK;
-    static_assert(TM >= 1 && TN >= 2 && A_CH >= 1, "tile shape");
+    constexpr int STAGE = (BM + NROWS) * kRow;
+    // LDS stages: 2 where that lets two workgroups share a CU (one's
+    // prologue and epilogue then overlap the other's main loop), else 3 if
+    // they fit
+    constexpr int NS = 2 * STAGE + 4096 <= 80 * 1024 ? 2 : (3 * STAGE <= kLdsBudget ? 3 : 2);
+    constexpr int A_IN = BM / (8 * NW);         // copies (8 rows x 128 B) of A per wave per step
+    constexpr int B_IN = NROWS / (8 * NW);      // copies of B per wave per step
+    constexpr int N_BIG = A_IN + B_IN + (BLOCKQ ? 1 : 0);   // copies per wave per step
+    constexpr int NB1 = N_BIG / 2, NB2 = N_BIG - NB1;       // issued in the two half-steps
+    static_assert(TM >= 1 && A_IN >= 1 && B_IN >= 1 && BM % (8 * NW) == 0 && NROWS % (8 * NW) == 0 && BM <= 256 &&
+                      2 * STAGE <= kLdsBudget && (!BLOCKQ || NW == 4),
+                  "tile shape");
 
-    constexpr int NSTAGE = 3;
-    constexpr int A_IN = BM / 32;              // 1 KB copies (8 rows) of A per wave per step
-    constexpr int B_IN = kBRows / 32;          // 1 KB copies of B per wave per step
-    constexpr int SC_IN = BLOCKQ ? 1 : 0;      // blockwise: one 4-byte-lane copy of row scales
-    constexpr int N_IN = A_IN + B_IN + SC_IN;  // copies per wave per step (vmcnt units)
-    __shared__ __attribute__((aligned(16))) uint8_t lds[NSTAGE * STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE];
     __shared__ float s_rowscale[BM];          // PTPC: row scale; other modes: row mask (pad rows 0)
-    __shared__ __attribute__((aligned(16))) float s_ascale[NSTAGE][256];   // blockwise: row scales of a stage
+    __shared__ __attribute__((aligned(16))) float s_ascale[BLOCKQ ? NS : 1][256];   // blockwise: row scales of a stage
     __shared__ int s_tok[BM];
+    __shared__ float s_wscale[BLOCKQ ? WN * TN : 1][BLOCKQ ? 128 : 1];   // blockwise: weight scales of the tile
 
-    // tile order: expert-major, weight tile, then row block; XCD-contiguous
-    const int per = (p.n_tiles + 7) >> 3;
+    // tile order: expert-major, weight tile, then row block; each XCD takes
+    // a contiguous eighth of the tiles that hold rows (the grid covers the
+    // worst case; workgroups past the real count exit at once)
+    const int n_valid = p.offsets[p.n_exp] / BM * p.n_ntiles;
+    const int per = (n_valid + 7) >> 3;
     const int lt = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (lt >= p.n_tiles) return;
+    if (blockIdx.x >> 3 >= per || lt >= n_valid) return;
     const int e = p.block_expert[lt / p.n_ntiles];
     if (e < 0) return;
     const int bs = p.offsets[e] / BM, nb = p.offsets[e + 1] / BM - bs;
@@ -134,6 +186,8 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
     const int n0 = nt * TILE_N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
+    const int q = lane >> 5, r32 = lane & 31;
+    const int arow = wm * TM * 32;            // first tile row of this wave
 
     if (tid < BM) {
         int tok = m0 + tid;
@@ -150,25 +204,28 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
     }
     __syncthreads();
 
-    // Copy j of a wave fills 8 LDS rows: lane i writes row 8j' + i/8 (j' the
-    // wave's j-th block of 8 rows), physical chunk i%8, which must hold the
-    // logical chunk (i%8) ^ swizzle(row) of that row.
+    // Copy j of a wave fills 8 LDS rows of block wave + NW*j: lane i writes
+    // row 8*blk + i/8, physical chunk i%8, which holds logical chunk
+    // (i%8) ^ swizzle(row) of that row.
     const int crow = lane >> 3, cphys = lane & 7;
     const uint8_t* a_src[A_IN];
 #pragma unroll
     for (int j = 0; j < A_IN; ++j) {
-        const int r = (wave + 4 * j) * 8 + crow;
+        const int r = (wave + NW * j) * 8 + crow;
         const int c = cphys ^ ((r >> 1) & 7);
         a_src[j] = p.a + static_cast<int64_t>(s_tok[r]) * p.a_ld + c * 16;
     }
+    // weight tile row t (LDS row BM + t) is row t % WCOLS of wave column t / WCOLS
+    // (gate rows first, then up rows)
     const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
     const int64_t wrow_bytes = static_cast<int64_t>(p.K) * ELEM;
     uint32_t b_src[B_IN];                                   // byte offsets within the expert
 #pragma unroll
     for (int j = 0; j < B_IN; ++j) {
-        const int r = (wave + 4 * j) * 8 + crow;             // weight tile row
-        const int c = cphys ^ (((BM + r) >> 1) & 7);
-        const int wr = GATEUP ? (r < 128 ? n0 + r : p.I + n0 + r - 128) : n0 + r;
+        const int t = (wave + NW * j) * 8 + crow;
+        const int c = cphys ^ (((BM + t) >> 1) & 7);
+        const int w = t / WCOLS, jj = t % WCOLS;
+        const int wr = GATEUP ? (jj < HALF ? n0 + w * HALF + jj : p.I + n0 + w * HALF + jj - HALF) : n0 + t;
         b_src[j] = static_cast<uint32_t>(wr * wrow_bytes + c * 16);
     }
     // blockwise: wave w copies the scales of rows 64w .. 64w+63 (rows past BM
@@ -178,209 +235,282 @@ __global__ void __launch_bounds__(256, 1) grouped_gemm_kernel(const GemmArgs p) 
         const int r = wave * 64 + lane;
         sc_src = p.a_scale + static_cast<int64_t>(s_tok[r < BM ? r : 0]) * p.a_scale_ld;
     }
-    const int nk = static_cast<int>(wrow_bytes / kBK);
+    const int nbig = static_cast<int>(wrow_bytes / kRow);   // steps; K bytes are a multiple of 128
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     const uint32_t sc0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_ascale[0][0]));
 
-    // issue the copies of K step S into LDS stage BUF (uniform M0 per copy)
-    auto issue = [&](int S, int buf) {
-        const int64_t ko = static_cast<int64_t>(S) * kBK;
+    // copy D (0 .. N_BIG-1) of step S into LDS stage BUF (uniform M0 per copy)
+    auto issue_one = [&](auto D, int S, int buf) {
+        constexpr int d = decltype(D)::value;
+        const int64_t ko = static_cast<int64_t>(S) * kRow;
         const uint32_t st = lds0 + buf * STAGE;
-#pragma unroll
-        for (int j = 0; j < A_IN; ++j)
-            dma16(a_src[j] + ko, __builtin_amdgcn_readfirstlane(st + (wave + 4 * j) * 8 * kBK));
-#pragma unroll
-        for (int j = 0; j < B_IN; ++j)
-            dma16(wexp + b_src[j] + ko, __builtin_amdgcn_readfirstlane(st + (BM + (wave + 4 * j) * 8) * kBK));
-        if constexpr (BLOCKQ) dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 256 + wave * 64) * 4));
+        if constexpr (d < A_IN) {
+            dma16(a_src[d] + ko, __builtin_amdgcn_readfirstlane(st + (wave + NW * d) * 8 * kRow));
+        } else if constexpr (d < A_IN + B_IN) {
+            constexpr int j = d - A_IN;
+            dma16(wexp + b_src[j] + ko, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
+        } else {
+            dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 256 + wave * 64) * 4));
+        }
     };
+    auto issue = [&](int S) { static_for<N_BIG>([&](auto D) { issue_one(D, S, S % NS); }); };
 
-    // LDS rows of this lane's operands
-    int a_row[TM], b_row[TN];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) a_row[tm] = wm * WROWS + tm * 32 + (lane & 31);
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-        int r;
-        if (GATEUP) r = tn < TN / 2 ? wn * G + tn * 32 : 128 + wn * G + (tn - TN / 2) * 32;
-        else r = wn * WCOLS + tn * 32;
-        b_row[tn] = BM + r + (lane & 31);
+    // this wave's weight rows (first global row of each 32-row tile)
+    auto wrow_of = [&](int w, int tn) {
+        return GATEUP ? (tn < TN / 2 ? n0 + w * HALF + tn * 32 : p.I + n0 + w * HALF + (tn - TN / 2) * 32)
+                      : n0 + w * WCOLS + tn * 32;
+    };
+    const int brow = BM + wn * WCOLS + r32;    // LDS row of this lane's weight row in tile 0
+
+    // blockwise: the weight scales of this tile, [wave column * TN + tn][K block]
+    if constexpr (BLOCKQ) {
+        for (int idx = tid; idx < WN * TN * nbig; idx += NT) {
+            const int t = idx / nbig, kb = idx - t * nbig;
+            s_wscale[t][kb] = p.w_scale[e * p.ws_expert + (wrow_of(t / TN, t % TN) >> 7) * p.ws_ld + kb];
+        }
     }
-    const int h = lane >> 5;
 
     v16f acc[TM][TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16f{};
+    v16f part[BLOCKQ ? TM : 1][BLOCKQ ? TN : 1];
 
-    // one 128-byte K step on LDS stage `buf`: all operand fragments first, then the MFMAs
-    auto step = [&](int buf, int s) {
+    // Operand fragments, double-buffered in registers: set X holds the two
+    // 16-byte chunks of this lane's rows for one half-step; the blockwise
+    // mode also keeps a step's row scales (rows 8g + 4q .. + 3 of each tile).
+    u32x4 fa[2][TM][2], fb[2][TN][2];
+    float4 fs[BLOCKQ ? TM : 1][4];
+
+    // LDS read L (0 .. NL-1) of half-step H of the step in stage BUF into set
+    // X, in the order the MFMAs consume them: weight tile 0, the row tiles,
+    // then the other weight tiles (the MFMAs run weight tile by weight tile)
+    constexpr int NL = 2 * (TM + TN);
+    auto load_one = [&](auto X, auto Lc, int buf, int h) {
+        constexpr int l = decltype(Lc)::value, x = decltype(X)::value;
         const uint8_t* L = lds + buf * STAGE;
-        if constexpr (MODE == MOE_QUANT_NONE_BF16) {
-            v8bf av[4][TM], bv[4][TN];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) av[kk][tm] = __builtin_bit_cast(v8bf, lds16(L, lds_off(a_row[tm], 2 * kk + h)));
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn) bv[kk][tn] = __builtin_bit_cast(v8bf, lds16(L, lds_off(b_row[tn], 2 * kk + h)));
-            }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                    for (int tm = 0; tm < TM; ++tm)
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk][tm], bv[kk][tn], acc[tm][tn], 0, 0, 0);
+        if constexpr (l >= 2 && l < 2 + 2 * TM) {
+            constexpr int tm = (l - 2) / 2, c = (l - 2) % 2;
+            fa[x][tm][c] = lds16(L, lds_off(arow + tm * 32 + r32, 4 * h + 2 * q + c));
         } else {
-            v8i av[2][TM], bv[2][TN];
+            constexpr int lb = l < 2 ? l : l - 2 * TM;
+            constexpr int tn = lb / 2, c = lb % 2;
+            fb[x][tn][c] = lds16(L, lds_off(brow + tn * 32, 4 * h + 2 * q + c));
+        }
+    };
+    auto load_scales = [&](int buf) {
+        if constexpr (BLOCKQ) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    fs[tm][g] = *reinterpret_cast<const float4*>(&s_ascale[buf][arow + tm * 32 + 8 * g + 4 * q]);
+        }
+    };
+
+    // MFMA J (0 .. NM-1) of a half-step from fragment set X
+    constexpr int NM = (MODE == MOE_QUANT_NONE_BF16 ? 2 : 1) * TM * TN;
+    auto mma_one = [&](auto X, auto J) {
+        constexpr int j = decltype(J)::value, x = decltype(X)::value;
+        if constexpr (MODE == MOE_QUANT_NONE_BF16) {
+            constexpr int c = j / (TM * TN), tn = (j % (TM * TN)) / TM, tm = j % TM;
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fa[x][tm][c]),
+                                                                  __builtin_bit_cast(v8bf, fb[x][tn][c]), acc[tm][tn], 0,
+                                                                  0, 0);
+        } else {
+            constexpr int tn = j / TM, tm = j % TM;
+            const v8i av = cat8(fa[x][tm][0], fa[x][tm][1]), bv = cat8(fb[x][tn][0], fb[x][tn][1]);
+            // e4m3 x e4m3 (format selectors 0, 0), no block scaling
+            if constexpr (!BLOCKQ)
+                acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[tm][tn], 0, 0, 0, 0, 0, 0);
+            else
+                part[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, x == 0 ? v16f{} : part[tm][tn],
+                                                                               0, 0, 0, 0, 0, 0);
+        }
+    };
+    // blockwise: a step closes one 128-element scale block:
+    // acc += part * a_scale(row, kb) * w_scale(n-block, kb)
+    auto block_scale = [&](int kb) {
+        if constexpr (BLOCKQ) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const float wsc = s_wscale[wn * TN + tn][kb];
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
-                    av[kk][tm] = cat8(lds16(L, lds_off(a_row[tm], 4 * kk + 2 * h)), lds16(L, lds_off(a_row[tm], 4 * kk + 2 * h + 1)));
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
-                    bv[kk][tn] = cat8(lds16(L, lds_off(b_row[tn], 4 * kk + 2 * h)), lds16(L, lds_off(b_row[tn], 4 * kk + 2 * h + 1)));
-            }
-            if constexpr (!BLOCKQ) {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                        for (int tm = 0; tm < TM; ++tm)
-                            // e4m3 x e4m3 (format selectors 0, 0), no block scaling
-                            acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[kk][tm], bv[kk][tn], acc[tm][tn],
-                                                                                          0, 0, 0, 0, 0, 0);
-            } else {
-                // the step is one 128-element scale block:
-                // acc += part * a_scale(row, kb) * w_scale(n-block, kb)
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    const int wr0 = b_row[tn] - BM - (lane & 31);
-                    const int wr = GATEUP ? (wr0 < 128 ? n0 + wr0 : p.I + n0 + wr0 - 128) : n0 + wr0;
-                    const float wsc = p.w_scale[e * p.ws_expert + (wr >> 7) * p.ws_ld + s];
-#pragma unroll
-                    for (int tm = 0; tm < TM; ++tm) {
-                        v16f part = v16f{};
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
-                            part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[kk][tm], bv[kk][tn], part, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                            acc[tm][tn][i] += part[i] * (s_ascale[buf][row] * wsc);
-                        }
+                    for (int i = 0; i < 16; ++i) {
+                        const float4 f = fs[tm][i >> 2];
+                        const float as = (i & 3) == 0 ? f.x : (i & 3) == 1 ? f.y : (i & 3) == 2 ? f.z : f.w;
+                        acc[tm][tn][i] += part[tm][tn][i] * (as * wsc);
                     }
-                }
             }
         }
     };
 
-    // prologue: steps 0 and 1 in flight; wait for step 0
-    issue(0, 0);
-    if (nk > 1) {
-        issue(1, 1);
-        vmcnt_wait<N_IN>();
-    } else {
-        vmcnt_wait<0>();
-    }
+    // One half-step: its MFMAs from set X, issued one at a time, each
+    // followed by its share of the NL reads of the next half-step (into the
+    // other set, from stage RBUF, half RH; when RD) and of the ND copies
+    // [D0, D0 + ND) of step CS (when CP), so that a memory instruction that
+    // stalls at issue overlaps a running MFMA.
+    auto half_step = [&](auto X, auto D0c, auto NDc, bool rd, int rbuf, int rh, bool cp, int cs) {
+        constexpr int x = decltype(X)::value, D0 = decltype(D0c)::value, ND = decltype(NDc)::value;
+        using XN = std::integral_constant<int, 1 - x>;
+        static_for<NM>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            mma_one(X, J);
+            __builtin_amdgcn_sched_barrier(0);
+            if (rd) {
+                static_for<(j + 1) * NL / NM - j * NL / NM>([&](auto L) {
+                    load_one(XN{}, std::integral_constant<int, j * NL / NM + decltype(L)::value>{}, rbuf, rh);
+                });
+            }
+            if (cp) {
+                static_for<(j + 1) * ND / NM - j * ND / NM>([&](auto D) {
+                    issue_one(std::integral_constant<int, D0 + j * ND / NM + decltype(D)::value>{}, cs, cs % NS);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    // Prologue: steps 0 .. NS-2 and the first NB1 copies of step NS-1 go
+    // out; wait for step 0, then read the fragments of its first half.
+    for (int S = 0; S < NS - 1; ++S)
+        if (S < nbig) issue(S);
+    const bool pro_more = NS - 1 < nbig;
+    if (pro_more) static_for<NB1>([&](auto D) { issue_one(D, NS - 1, (NS - 1) % NS); });
+    if (pro_more) vmcnt_wait<(NS - 2) * N_BIG + NB1>();
+    else vmcnt_wait<0>();
     __syncthreads();
-    int s = 0;
-    // steady state: the copies of step s + 2 go out, step s computes, then
-    // this wave's copies of step s + 1 are waited for (those of s + 2 may
-    // stay in flight) and the barrier publishes them and frees stage s
-    for (; s + 2 < nk; ++s) {
-        const int b = s % NSTAGE;
-        issue(s + 2, (s + 2) % NSTAGE);
-        step(b, s);
-        vmcnt_wait<N_IN>();
-        __syncthreads();
+    static_for<NL>([&](auto L) { load_one(std::integral_constant<int, 0>{}, L, 0, 0); });
+
+    // Step S (stage S % NS, landed and published):
+    //   first half: MFMAs from set 0; read the second half of S into set 1;
+    //     issue the last NB2 copies of step S + NS - 1 (into the stage of
+    //     step S - 1, released by the previous barrier); wait until step
+    //     S + 1 has landed (copies issued after it may stay in flight) and
+    //     barrier: publishes S + 1 and releases stage S.
+    //   second half: MFMAs from set 1; read the first half of S + 1 into
+    //     set 0; issue the first NB1 copies of step S + NS (into stage S).
+    using X0 = std::integral_constant<int, 0>;
+    using X1 = std::integral_constant<int, 1>;
+    for (int S = 0; S < nbig; ++S) {
+        const int buf = S % NS;
+        const bool next = S + 1 < nbig;
+        const bool cp2 = S + NS - 1 < nbig, cp1 = S + NS < nbig;
+        half_step(X0{}, std::integral_constant<int, NB1>{}, std::integral_constant<int, NB2>{}, true, buf, 1, cp2,
+                  S + NS - 1);
+        if constexpr (BLOCKQ) load_scales(buf);
+        if (next) {
+            if (cp2) vmcnt_wait<(NS - 2) * N_BIG>();
+            else vmcnt_wait<0>();
+            __syncthreads();
+        }
+        // the reads of the next step's first half are issued even after the
+        // last step (they then read an idle stage into registers no MFMA
+        // uses): a branch around them would make the compiler wait for every
+        // outstanding LDS read before the MFMAs that follow
+        half_step(X1{}, std::integral_constant<int, 0>{}, std::integral_constant<int, NB1>{}, true, (S + 1) % NS, 0,
+                  cp1, S + NS);
+        block_scale(S);
     }
-    // last two steps (step nk-1 may already be the only one left)
-    for (; s < nk; ++s) {
-        step(s % NSTAGE, s);
-        vmcnt_wait<0>();
-        __syncthreads();
-    }
+    vmcnt_wait<0>();
 
     // ------------------------------------------------------------ epilogue
+    // lane holds column r32 and rows 8g + 4q + j (i = 4g + j) of each 32x32
+    // tile.  Stores go through a buffer resource based at the tile's first
+    // row: a 32-bit lane offset (row 4q of the 32-row tile, column) plus a
+    // wave-uniform row offset (8g + j rows) in a scalar register.
     const float* wsx = (MODE == MOE_QUANT_PTPC_FP8) ? p.w_scale + e * p.ws_expert : nullptr;
+    constexpr int OBYTES = (!GATEUP && MODE == MOE_QUANT_NONE_BF16) ? 4 : 2;
+    const int ldb = static_cast<int>(p.out_ld) * OBYTES;          // bytes per output row
+    const __amdgpu_buffer_rsrc_t rsrc =
+        tile_rsrc(static_cast<uint8_t*>(p.out) + static_cast<int64_t>(m0) * p.out_ld * OBYTES);
     if constexpr (GATEUP) {
-        uint16_t* out = static_cast<uint16_t*>(p.out);
 #pragma unroll
         for (int tg = 0; tg < TN / 2; ++tg) {
-            const int col = wn * G + tg * 32 + (lane & 31);     // act column within the tile
+            const int col = n0 + wn * HALF + tg * 32 + r32;     // act column
             float swg = 1.0f, swu = 1.0f;
             if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
-                swg = wsx[n0 + col];
-                swu = wsx[p.I + n0 + col];
+                swg = wsx[col];
+                swu = wsx[p.I + col];
             }
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
+                const int voff = (arow + tm * 32 + 4 * q) * ldb + col * 2;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                    float g = acc[tm][tg][i], u = acc[tm][tg + TN / 2][i];
+                    const int row = arow + tm * 32 + 8 * (i >> 2) + 4 * q + (i & 3);
                     const float rs = s_rowscale[row];
-                    g = g * rs * swg;
-                    u = u * rs * swu;
-                    out[static_cast<int64_t>(m0 + row) * p.out_ld + n0 + col] = f32_to_bf16(silu_mul(g, u));
+                    const float g = acc[tm][tg][i] * rs * swg, u = acc[tm][tg + TN / 2][i] * rs * swu;
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(silu_mul(g, u)), rsrc, voff,
+                                                          (8 * (i >> 2) + (i & 3)) * ldb, 0);
                 }
             }
         }
     } else {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-            const int col = wn * WCOLS + tn * 32 + (lane & 31);
+            const int col = wrow_of(wn, tn) + r32;
             float sw = 1.0f;
-            if constexpr (MODE == MOE_QUANT_PTPC_FP8) sw = wsx[n0 + col];
+            if constexpr (MODE == MOE_QUANT_PTPC_FP8) sw = wsx[col];
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
+                const int voff = (arow + tm * 32 + 4 * q) * ldb + col * OBYTES;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int row = wm * WROWS + tm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    const int row = arow + tm * 32 + 8 * (i >> 2) + 4 * q + (i & 3);
                     const float v = acc[tm][tn][i] * s_rowscale[row] * sw;
-                    const int64_t o = static_cast<int64_t>(m0 + row) * p.out_ld + n0 + col;
-                    if constexpr (MODE == MOE_QUANT_NONE_BF16) static_cast<float*>(p.out)[o] = v;
-                    else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(v);
+                    const int so = (8 * (i >> 2) + (i & 3)) * ldb;
+                    if constexpr (OBYTES == 4)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, voff, so, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rsrc, voff, so, 0);
                 }
             }
         }
     }
 }
 
-template <int MODE, bool GATEUP>
+template <int MODE, bool GATEUP, int TN>
 static int32_t launch_bm(int block_m, const GemmArgs& a, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(ceil_div(a.n_tiles, 8) * 8)), block(256);
+    const dim3 grid(static_cast<unsigned>(ceil_div(a.n_tiles, 8) * 8));
     if (block_m == 32) {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 32>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 32, TN>), grid, dim3(nw_of(32) * 64), 0, s, a);
         return moe_launch_status();
     }
     // the blockwise mode keeps its partial sums and scales in registers: row
     // blocks above 32 would spill
     if constexpr (MODE != MOE_QUANT_BLOCK128_FP8) {
         if (block_m == 64) {
-            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 64>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 64, TN>), grid, dim3(nw_of(64) * 64), 0, s, a);
             return moe_launch_status();
         }
         if (block_m == 128) {
-            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 128>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 128, TN>), grid, dim3(nw_of(128) * 64), 0, s, a);
             return moe_launch_status();
+        }
+        if constexpr (TN == 2) {   // tn_of gives the 256-row tile 2 weight tiles per wave
+            if (block_m == 256) {
+                hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 256, TN>), grid, dim3(nw_of(256) * 64), 0, s,
+                                   a);
+                return moe_launch_status();
+            }
         }
     }
     return MOE_ERR_UNSUPPORTED;
 }
 
 template <bool GATEUP>
-static int32_t launch_mode(int quant, int block_m, const GemmArgs& a, hipStream_t s) {
+static int32_t launch_mode(int quant, int tn, int block_m, const GemmArgs& a, hipStream_t s) {
     if (a.n_tiles == 0) return MOE_OK;
     switch (quant) {
-        case MOE_QUANT_NONE_BF16: return launch_bm<MOE_QUANT_NONE_BF16, GATEUP>(block_m, a, s);
-        case MOE_QUANT_PTPC_FP8: return launch_bm<MOE_QUANT_PTPC_FP8, GATEUP>(block_m, a, s);
-        case MOE_QUANT_BLOCK128_FP8: return launch_bm<MOE_QUANT_BLOCK128_FP8, GATEUP>(block_m, a, s);
+        case MOE_QUANT_NONE_BF16: return launch_bm<MOE_QUANT_NONE_BF16, GATEUP, 2>(block_m, a, s);
+        case MOE_QUANT_PTPC_FP8:
+            return tn == 4 ? launch_bm<MOE_QUANT_PTPC_FP8, GATEUP, 4>(block_m, a, s)
+                           : launch_bm<MOE_QUANT_PTPC_FP8, GATEUP, 2>(block_m, a, s);
+        case MOE_QUANT_BLOCK128_FP8: return launch_bm<MOE_QUANT_BLOCK128_FP8, GATEUP, 2>(block_m, a, s);
     }
     return MOE_ERR_UNSUPPORTED;
 }
@@ -416,9 +546,11 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
     g.I = L->I;
     g.out = act;
     g.out_ld = L->I;
-    g.n_ntiles = L->I / 128;
+    const int tn = tn_of(L->quant, 2 * L->I, block_m);
+    g.n_ntiles = L->I / ((nw_of(block_m) / wm_of(block_m)) * tn * 16);
     g.n_tiles = static_cast<int>(max_rows / block_m) * g.n_ntiles;
-    return launch_mode<true>(L->quant, block_m, g, s);
+    g.n_exp = L->E + L->n_shared;
+    return launch_mode<true>(L->quant, tn, block_m, g, s);
 }
 
 int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T, int block_m,
@@ -444,9 +576,11 @@ int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* 
     g.I = L->I;
     g.out = out_perm;
     g.out_ld = L->D;
-    g.n_ntiles = L->D / kBRows;
+    const int tn = tn_of(L->quant, L->D, block_m);
+    g.n_ntiles = L->D / ((nw_of(block_m) / wm_of(block_m)) * tn * 32);
     g.n_tiles = static_cast<int>(max_rows / block_m) * g.n_ntiles;
-    return launch_mode<false>(L->quant, block_m, g, s);
+    g.n_exp = L->E + L->n_shared;
+    return launch_mode<false>(L->quant, tn, block_m, g, s);
 }
 
 }  // namespace moe

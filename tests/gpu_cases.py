@@ -27,6 +27,9 @@ REDUCED = {
     "deepseek_r1_block_fp8_small": synth.get("deepseek_r1_block_fp8").replace(T=40, D=1024, I=256, E=32),
     "qwen3_235b_decode_ptpc_t64": synth.get("qwen3_235b_decode_ptpc").replace(T=64, D=1024, I=512, E=16),
     "bf16_small_t20": synth.get("tiny_bf16").replace(T=20, D=512, I=256, E=16, k=4),
+    # weight rows that do not split into 4 x 128 per wave column (2I = 768,
+    # D = 1280): the PTPC kernels fall back to 64-row wave tiles
+    "qwen3_30b_a3b_ptpc_i384": synth.get("qwen3_30b_a3b_ptpc").replace(T=200, D=1280, I=384, E=16),
 }
 
 

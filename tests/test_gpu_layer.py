@@ -43,6 +43,8 @@ def _check_exact(inter, ref, quant):
 @pytest.mark.parametrize("name,block_m", [("tiny_bf16", 0), ("tiny_bf16", 64), ("bf16_multi_tile_r", 0),
                                           ("qwen3_30b_a3b_ptpc", 0), ("qwen3_30b_a3b_ptpc", 128),
                                           ("qwen3_235b_prefill_ptpc_r", 0), ("qwen3_235b_prefill_ptpc_r", 32),
+                                          ("qwen3_235b_prefill_ptpc_r", 256), ("bf16_multi_tile_r", 256),
+                                          ("qwen3_30b_a3b_ptpc_i384", 0),
                                           ("qwen3_235b_decode_ptpc", 0), ("deepseek_r1_block_fp8_r", 0),
                                           ("deepseek_r1_block_fp8_r", 32), ("deepseek_r1_block_fp8_small", 0),
                                           ("qwen3_235b_decode_ptpc_t64", 0), ("qwen3_235b_decode_ptpc", 32),

@@ -210,6 +210,8 @@ def test_quant_weights(quant):
 
 @pytest.mark.parametrize("name,block_m", [("tiny_bf16", 32), ("bf16_multi_tile_r", 64), ("qwen3_30b_a3b_ptpc", 32),
                                           ("qwen3_235b_prefill_ptpc_r", 128), ("qwen3_235b_prefill_ptpc_r", 64),
+                                          ("qwen3_235b_prefill_ptpc_r", 256), ("bf16_multi_tile_r", 256),
+                                          ("qwen3_30b_a3b_ptpc_i384", 64), ("qwen3_30b_a3b_ptpc_i384", 256),
                                           ("deepseek_r1_block_fp8_r", 32),
                                           ("tiny_bf16", 16), ("bf16_small_t20", 16), ("qwen3_235b_decode_ptpc", 16),
                                           ("qwen3_235b_decode_ptpc_t64", 16), ("deepseek_r1_block_fp8_small", 16)])
@@ -246,6 +248,8 @@ def test_gateup_silu_entry(name, block_m):
 
 
 @pytest.mark.parametrize("name,block_m", [("tiny_bf16", 32), ("qwen3_235b_prefill_ptpc_r", 128),
+                                          ("qwen3_235b_prefill_ptpc_r", 256), ("bf16_multi_tile_r", 256),
+                                          ("qwen3_30b_a3b_ptpc_i384", 128), ("qwen3_30b_a3b_ptpc_i384", 256),
                                           ("qwen3_30b_a3b_ptpc", 64), ("deepseek_r1_block_fp8_r", 32),
                                           ("tiny_bf16", 16), ("qwen3_235b_decode_ptpc", 16),
                                           ("qwen3_235b_decode_ptpc_t64", 16), ("deepseek_r1_block_fp8_small", 16)])
