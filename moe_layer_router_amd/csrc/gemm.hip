@@ -281,7 +281,7 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
     // 16-byte chunks of this lane's rows for one half-step; the blockwise
     // mode also keeps a step's row scales (rows 8g + 4q .. + 3 of each tile).
     u32x4 fa[2][TM][2], fb[2][TN][2];
-    float4 fs[BLOCKQ ? TM : 1][4];
+    float fs[BLOCKQ ? TM : 1];
 
     // LDS read L (0 .. NL-1) of half-step H of the step in stage BUF into set
     // X, in the order the MFMAs consume them: weight tile 0, the row tiles,
@@ -302,10 +302,7 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
     auto load_scales = [&](int buf) {
         if constexpr (BLOCKQ) {
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    fs[tm][g] = *reinterpret_cast<const float4*>(&s_ascale[buf][arow + tm * 32 + 8 * g + 4 * q]);
+            for (int tm = 0; tm < TM; ++tm) fs[tm] = s_ascale[buf][arow + tm * 32 + r32];
         }
     };
 
@@ -315,17 +312,17 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
         constexpr int j = decltype(J)::value, x = decltype(X)::value;
         if constexpr (MODE == MOE_QUANT_NONE_BF16) {
             constexpr int c = j / (TM * TN), tn = (j % (TM * TN)) / TM, tm = j % TM;
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fa[x][tm][c]),
-                                                                  __builtin_bit_cast(v8bf, fb[x][tn][c]), acc[tm][tn], 0,
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fb[x][tn][c]),
+                                                                  __builtin_bit_cast(v8bf, fa[x][tm][c]), acc[tm][tn], 0,
                                                                   0, 0);
         } else {
             constexpr int tn = j / TM, tm = j % TM;
             const v8i av = cat8(fa[x][tm][0], fa[x][tm][1]), bv = cat8(fb[x][tn][0], fb[x][tn][1]);
             // e4m3 x e4m3 (format selectors 0, 0), no block scaling
             if constexpr (!BLOCKQ)
-                acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[tm][tn], 0, 0, 0, 0, 0, 0);
+                acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[tm][tn], 0, 0, 0, 0, 0, 0);
             else
-                part[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, x == 0 ? v16f{} : part[tm][tn],
+                part[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, x == 0 ? v16f{} : part[tm][tn],
                                                                                0, 0, 0, 0, 0, 0);
         }
     };
@@ -339,11 +336,7 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float4 f = fs[tm][i >> 2];
-                        const float as = (i & 3) == 0 ? f.x : (i & 3) == 1 ? f.y : (i & 3) == 2 ? f.z : f.w;
-                        acc[tm][tn][i] += part[tm][tn][i] * (as * wsc);
-                    }
+                    for (int i = 0; i < 16; ++i) acc[tm][tn][i] += part[tm][tn][i] * (fs[tm] * wsc);
             }
         }
     };
@@ -418,57 +411,83 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
     vmcnt_wait<0>();
 
     // ------------------------------------------------------------ epilogue
-    // lane holds column r32 and rows 8g + 4q + j (i = 4g + j) of each 32x32
-    // tile.  Stores go through a buffer resource based at the tile's first
-    // row: a 32-bit lane offset (row 4q of the 32-row tile, column) plus a
-    // wave-uniform row offset (8g + j rows) in a scalar register.
-    const float* wsx = (MODE == MOE_QUANT_PTPC_FP8) ? p.w_scale + e * p.ws_expert : nullptr;
+    // The MFMAs take the weight rows as their first operand, so lane
+    // (r32, q) holds row r32 of each 32-row tile and, in register
+    // i = 4g + j, output column 8g + 4q + j of each 32-column tile: four
+    // consecutive columns per g.  Per row tile, each wave packs them into
+    // 8 (bf16) or 16 (fp32) bytes, writes them row-major into its own LDS
+    // region (rows padded by 16 bytes), reads them back as 16-byte row
+    // pieces and stores whole 128-byte lines through a buffer resource
+    // based at the tile's first row.  The LDS regions reuse the stages: a
+    // barrier first lets every wave finish its last operand reads.
     constexpr int OBYTES = (!GATEUP && MODE == MOE_QUANT_NONE_BF16) ? 4 : 2;
+    constexpr int CW = GATEUP ? HALF : WCOLS;            // output columns per wave
+    constexpr int RB = CW * OBYTES;                       // bytes of one output row of the wave
+    constexpr int RBP = RB + 16;                          // padded LDS row stride
+    constexpr int LPR = RB / 16;                          // lanes per row on the way out
+    constexpr int RPI = 64 / LPR;                         // rows per store instruction
+    static_assert(64 % LPR == 0 && 32 % RPI == 0 && NW * 32 * RBP <= NS * STAGE, "epilogue layout");
+    __syncthreads();
+    uint8_t* reg = lds + wave * 32 * RBP;
     const int ldb = static_cast<int>(p.out_ld) * OBYTES;          // bytes per output row
     const __amdgpu_buffer_rsrc_t rsrc =
         tile_rsrc(static_cast<uint8_t*>(p.out) + static_cast<int64_t>(m0) * p.out_ld * OBYTES);
-    if constexpr (GATEUP) {
+    const float* wsx = (MODE == MOE_QUANT_PTPC_FP8) ? p.w_scale + e * p.ws_expert : nullptr;
+    // first output column of this wave
+    const int col0 = GATEUP ? n0 + wn * HALF : n0 + wn * WCOLS;
+    // channel scales of this lane's columns: [tile][g] -> 4 consecutive columns
+    float4 swa[GATEUP ? TN / 2 : TN][4], swb[GATEUP ? TN / 2 : 1][4];
 #pragma unroll
-        for (int tg = 0; tg < TN / 2; ++tg) {
-            const int col = n0 + wn * HALF + tg * 32 + r32;     // act column
-            float swg = 1.0f, swu = 1.0f;
+    for (int t = 0; t < (GATEUP ? TN / 2 : TN); ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c = col0 + t * 32 + 8 * g + 4 * q;
             if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
-                swg = wsx[col];
-                swu = wsx[p.I + col];
-            }
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const int voff = (arow + tm * 32 + 4 * q) * ldb + col * 2;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = arow + tm * 32 + 8 * (i >> 2) + 4 * q + (i & 3);
-                    const float rs = s_rowscale[row];
-                    const float g = acc[tm][tg][i] * rs * swg, u = acc[tm][tg + TN / 2][i] * rs * swu;
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(silu_mul(g, u)), rsrc, voff,
-                                                          (8 * (i >> 2) + (i & 3)) * ldb, 0);
-                }
+                swa[t][g] = *reinterpret_cast<const float4*>(wsx + c);
+                if constexpr (GATEUP) swb[t][g] = *reinterpret_cast<const float4*>(wsx + p.I + c);
+            } else {
+                swa[t][g] = float4{1.0f, 1.0f, 1.0f, 1.0f};
+                if constexpr (GATEUP) swb[t][g] = float4{1.0f, 1.0f, 1.0f, 1.0f};
             }
         }
-    } else {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const int col = wrow_of(wn, tn) + r32;
-            float sw = 1.0f;
-            if constexpr (MODE == MOE_QUANT_PTPC_FP8) sw = wsx[col];
+    for (int tm = 0; tm < TM; ++tm) {
+        const float rs = s_rowscale[arow + tm * 32 + r32];
+        // pack this row tile into the wave's region
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const int voff = (arow + tm * 32 + 4 * q) * ldb + col * OBYTES;
+        for (int t = 0; t < (GATEUP ? TN / 2 : TN); ++t)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = arow + tm * 32 + 8 * (i >> 2) + 4 * q + (i & 3);
-                    const float v = acc[tm][tn][i] * s_rowscale[row] * sw;
-                    const int so = (8 * (i >> 2) + (i & 3)) * ldb;
-                    if constexpr (OBYTES == 4)
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, voff, so, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rsrc, voff, so, 0);
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+                const float4 sa = swa[t][g];
+                const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (GATEUP) {
+                        const float4 sb = swb[t][g];
+                        const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
+                        v[j] = silu_mul(acc[tm][t][4 * g + j] * rs * sav[j], acc[tm][t + TN / 2][4 * g + j] * rs * sbv[j]);
+                    } else {
+                        v[j] = acc[tm][t][4 * g + j] * rs * sav[j];
+                    }
+                }
+                uint8_t* dst = reg + r32 * RBP + (t * 32 + 8 * g + 4 * q) * OBYTES;
+                if constexpr (OBYTES == 2) {
+                    const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+                    const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+                    *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+                } else {
+                    *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
                 }
             }
+        // read back 16-byte row pieces and store whole lines (the wave's
+        // LDS operations complete in order, so the next row tile's writes
+        // cannot overtake these reads)
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int row = it * RPI + lane / LPR, ch = lane % LPR;
+            const u32x4 d = *reinterpret_cast<const u32x4*>(reg + row * RBP + ch * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(d, rsrc, (arow + tm * 32 + row) * ldb + col0 * OBYTES + ch * 16, 0, 0);
         }
     }
 }
