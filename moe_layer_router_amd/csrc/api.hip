@@ -254,6 +254,7 @@ int32_t moe_default_block_m(const moe_layer_desc* L, int32_t T) {
     const int64_t per_expert = rows / (L->E + L->n_shared);
     if (T <= kStreamMaxT) return 16;
     if (L->quant == MOE_QUANT_BLOCK128_FP8) return 32;
+    if (per_expert >= 320) return 256;
     if (per_expert >= 96) return 128;
     if (per_expert >= 48) return 64;
     return 32;

@@ -40,7 +40,9 @@ __global__ void __launch_bounds__(kChunk) permute_count_kernel(const int* __rest
         chunk_cnt[static_cast<int64_t>(e) * nchunks + blockIdx.x] = cnt[e];
 }
 
-// One block of 1024 threads.
+// One block of 1024 threads.  Latency-bound (a few KB of counts), so each
+// wave keeps many loads in flight: it scans 4 experts at a time and loads
+// 4 x 64 chunk counts of each before scanning.
 __global__ void __launch_bounds__(1024) permute_scan_kernel(int* __restrict__ chunk_cnt, int Ep, int nchunks,
                                                             int block_m, int max_rows, int sentinel,
                                                             int* __restrict__ counts, int* __restrict__ offsets,
@@ -51,17 +53,35 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(int* __restrict__ ch
     __shared__ int s_wave[16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     // per-expert exclusive prefix over chunks (in place) and total
-    for (int e = wave; e < Ep; e += nw) {
-        int* row = chunk_cnt + static_cast<int64_t>(e) * nchunks;
-        int carry = 0;
-        for (int c0 = 0; c0 < nchunks; c0 += 64) {
-            const int c = c0 + lane;
-            const int v = c < nchunks ? row[c] : 0;
-            const int inc = wave_incl_scan_i(v, lane);
-            if (c < nchunks) row[c] = carry + inc - v;
-            carry += __shfl(inc, 63, 64);
+    constexpr int EB = 4, CG = 4;
+    for (int e0 = wave; e0 < Ep; e0 += nw * EB) {
+        int carry[EB] = {0, 0, 0, 0};
+        for (int c0 = 0; c0 < nchunks; c0 += 64 * CG) {
+            int v[EB][CG];
+#pragma unroll
+            for (int i = 0; i < EB; ++i) {
+                const int e = e0 + i * nw;
+#pragma unroll
+                for (int g = 0; g < CG; ++g) {
+                    const int c = c0 + 64 * g + lane;
+                    v[i][g] = (e < Ep && c < nchunks) ? chunk_cnt[static_cast<int64_t>(e) * nchunks + c] : 0;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < EB; ++i) {
+                const int e = e0 + i * nw;
+#pragma unroll
+                for (int g = 0; g < CG; ++g) {
+                    const int c = c0 + 64 * g + lane;
+                    const int inc = wave_incl_scan_i(v[i][g], lane);
+                    if (e < Ep && c < nchunks) chunk_cnt[static_cast<int64_t>(e) * nchunks + c] = carry[i] + inc - v[i][g];
+                    carry[i] += __shfl(inc, 63, 64);
+                }
+            }
         }
-        if (lane == 0) s_tot[e] = carry;
+#pragma unroll
+        for (int i = 0; i < EB; ++i)
+            if (lane == 0 && e0 + i * nw < Ep) s_tot[e0 + i * nw] = carry[i];
     }
     __syncthreads();
     // padded sizes -> exclusive scan over experts (Ep <= 1024 = one per thread)
@@ -86,14 +106,16 @@ __global__ void __launch_bounds__(1024) permute_scan_kernel(int* __restrict__ ch
     if (e == 0) { s_off[0] = 0; offsets[0] = 0; }
     __syncthreads();
     const int total = s_off[Ep];
-    // block -> expert map: each expert fills its own blocks
-    if (e < Ep)
-        for (int b = s_off[e] / block_m; b < s_off[e + 1] / block_m; ++b) block_expert[b] = e;
+    // one wave per expert: its blocks in the block -> expert map and the
+    // sentinel in its pad rows
+    for (int x = wave; x < Ep; x += nw) {
+        const int lo = s_off[x], hi = s_off[x + 1];
+        for (int b = lo / block_m + lane; b < hi / block_m; b += 64) block_expert[b] = x;
+        for (int r = lo + s_tot[x] + lane; r < hi; r += 64) sorted_ids[r] = sentinel;
+    }
+    // past the total: no expert, sentinel rows
     const int nblocks = max_rows / block_m;
     for (int b = total / block_m + threadIdx.x; b < nblocks; b += blockDim.x) block_expert[b] = -1;
-    // sentinel in the pads of every expert and past the total
-    if (e < Ep)
-        for (int r = s_off[e] + c; r < s_off[e + 1]; ++r) sorted_ids[r] = sentinel;
     for (int r = total + threadIdx.x; r < max_rows; r += blockDim.x) sorted_ids[r] = sentinel;
 }
 
