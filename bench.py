@@ -130,7 +130,9 @@ def active_expert_bytes(w, ids_np):
 
 def time_decode(torch, mlr, synth, steps, warmup):
     """Decode layer (T=32, Zipf-skewed routing): full forward, weights rotated
-    over copies so each step streams its experts from HBM."""
+    over copies so each step streams its experts from HBM.  Timed per call
+    (median, p10, p90), eagerly and replayed from captured HIP graphs (one
+    graph per weight copy; the replayed output must equal the eager one)."""
     from tests.gpu_cases import build_case
     w = synth.get("qwen3_235b_decode_ptpc")
     c = build_case(w)
@@ -142,21 +144,43 @@ def time_decode(torch, mlr, synth, steps, warmup):
         layers.append(mlr.MoELayer(D=w.D, I=w.I, E=w.E, top_k=w.k, weights=lw, quant=w.quant))
     y = torch.empty((w.T, w.D), dtype=torch.bfloat16, device="cuda")
     ws = layers[0].workspace(w.T)
-    for i in range(warmup):
-        layers[i % ncopy].forward(c.x, c.logits, y=y, workspace=ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        layers[i % ncopy].forward(c.x, c.logits, y=y, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    def timed(call):
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            call(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        pick = lambda f: t[min(len(t) - 1, int(f * len(t)))]
+        return pick(0.5), pick(0.1), pick(0.9)
+
+    med, p10, p90 = timed(lambda i: layers[i % ncopy].forward(c.x, c.logits, y=y, workspace=ws))
+    y_eager = y.clone()
     ids = layers[0].intermediates(w.T, 0, ws)["topk_ids"].cpu().numpy()
     nbytes, used = active_expert_bytes(w, ids)
-    return dict(workload=w.name, us_per_step=round(ms * 1e3, 2), active_experts=int(used),
-                expert_weight_bytes=int(nbytes), GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
-                hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    out = dict(workload=w.name, calls=steps, us_per_step=round(med, 2), p10_us=round(p10, 2), p90_us=round(p90, 2),
+               active_experts=int(used), expert_weight_bytes=int(nbytes),
+               GBps=round(nbytes / (med * 1e-6) / 1e9, 1), hbm_frac=round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+    graphs = []
+    for i in range(ncopy):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layers[i].forward(c.x, c.logits, y=y, workspace=ws)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    gmed, gp10, gp90 = timed(lambda i: graphs[i % ncopy].replay())
+    same = bool(torch.equal(y, y_eager))
+    out.update(graph_us_per_step=round(gmed, 2), graph_p10_us=round(gp10, 2), graph_p90_us=round(gp90, 2),
+               graph_GBps=round(nbytes / (gmed * 1e-6) / 1e9, 1),
+               graph_hbm_frac=round(nbytes / (gmed * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), graph_output_equal=same)
+    if not same:
+        raise SystemExit("graph replay of the decode forward differs from the eager forward")
+    return out
 
 
 def cpu_baseline(case, y_gpu, tokens):
@@ -287,7 +311,7 @@ def main():
     }
     if not args.no_decode and w.name != "qwen3_235b_decode_ptpc":
         log("decode leg")
-        out["decode"] = time_decode(torch, mlr, synth, max(args.steps, 20), args.warmup)
+        out["decode"] = time_decode(torch, mlr, synth, max(args.steps, 100), args.warmup)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on", args.cpu_tokens, "tokens")
         cb, ok, err = cpu_baseline(case, st.y, args.cpu_tokens)

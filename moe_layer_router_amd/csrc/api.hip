@@ -16,6 +16,10 @@ int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const 
                           float* scale, hipStream_t s);
 int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, uint8_t* q, float* scale,
                             hipStream_t s);
+bool front_small_ok(int T, int k, int n_shared);
+int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int block_m,
+                           int max_rows, int* ids, float* w, int* counts, int* offsets, int* sorted, int* bexp,
+                           int* inv, uint8_t* xq, float* xs, hipStream_t s);
 int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T, int block_m,
                            int64_t max_rows, const int* sorted_ids, const int* block_expert, const int* offsets,
                            void* act, hipStream_t s);
@@ -315,25 +319,31 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     }
     int* ids = static_cast<int*>(at(o.topk_ids));
     float* w = static_cast<float*>(at(o.topk_w));
-    if ((st = route_topk_launch(logits, T, E, k, L->scoring, L->n_groups, L->topk_groups, L->sel_bias,
-                                L->renormalize, L->route_scale, ids, w, s)) != MOE_OK)
-        return st;
     int* offsets = static_cast<int*>(at(o.offsets));
     int* sorted = static_cast<int*>(at(o.sorted_ids));
     int* bexp = static_cast<int*>(at(o.block_expert));
     int* inv = static_cast<int*>(at(o.inv_perm));
-    if ((st = permute_align_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
-                                   static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, at(o.scratch), s)) !=
-        MOE_OK)
-        return st;
-    const void* a = x_bf16;
-    const float* a_scale = nullptr;
-    if (fp8) {
-        if ((st = quant_rows_launch(static_cast<const uint16_t*>(x_bf16), T, L->D, group, nullptr,
-                                    static_cast<uint8_t*>(at(o.xq)), static_cast<float*>(at(o.xs)), s)) != MOE_OK)
+    const void* a = fp8 ? at(o.xq) : x_bf16;
+    const float* a_scale = fp8 ? static_cast<float*>(at(o.xs)) : nullptr;
+    if (block_m == 16 && front_small_ok(T, k, L->n_shared)) {
+        // small batch: routing, permutation and x quantization in one launch
+        if ((st = front_small_launch(L, x_bf16, logits, T, block_m, static_cast<int>(o.max_rows), ids, w,
+                                     static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv,
+                                     fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr,
+                                     fp8 ? static_cast<float*>(at(o.xs)) : nullptr, s)) != MOE_OK)
             return st;
-        a = at(o.xq);
-        a_scale = static_cast<float*>(at(o.xs));
+    } else {
+        if ((st = route_topk_launch(logits, T, E, k, L->scoring, L->n_groups, L->topk_groups, L->sel_bias,
+                                    L->renormalize, L->route_scale, ids, w, s)) != MOE_OK)
+            return st;
+        if ((st = permute_align_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
+                                       static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, at(o.scratch),
+                                       s)) != MOE_OK)
+            return st;
+        if (fp8 && (st = quant_rows_launch(static_cast<const uint16_t*>(x_bf16), T, L->D, group, nullptr,
+                                           static_cast<uint8_t*>(at(o.xq)), static_cast<float*>(at(o.xs)), s)) !=
+                       MOE_OK)
+            return st;
     }
     void* act = at(o.act);
     if ((st = gemm_gateup_launch(L, a, a_scale, T, block_m, o.max_rows, sorted, bexp, offsets, act, s)) != MOE_OK)

@@ -1,0 +1,263 @@
+// Fused front end for small batches (decode).
+//
+// At a few dozen tokens the routing, the three permutation steps and the FP8
+// quantization of x each move a few KB; as separate launches they cost more
+// in launch latency and dependent round trips than in work (the Qwen 3.5
+// roadmap item asks for top-k to run next to the scores, and the MI300X
+// page tunes small-batch latency).  Here one workgroup of 16 waves does all
+// of it and writes exactly what the separate entry points write:
+//   1. routing: wave w routes tokens w, w+16, ... (route_token, shared with
+//      the routing kernel); the picks also go to LDS;
+//   2. per-expert counts (LDS atomics), padded and unpadded exclusive scans
+//      over experts;
+//   3. a token's k picks are distinct experts and T <= 64, so every expert's
+//      rows are a 64-bit mask of tokens (LDS atomicOr); a row's rank in its
+//      expert's segment is the number of mask bits below its token, which is
+//      the stable ascending order of flat indices the multi-kernel
+//      permutation produces (shared-expert rows: token order);
+//   4. pads, block -> expert map, the tail past the padded total;
+//   5. FP8 quantization of x (per row or per 1x128 group), one wave per row,
+//      the same arithmetic as the row-quantization kernel; each wave issues
+//      its row's loads before routing the same token, so the two overlap.
+#include "quant_dev.h"
+#include "route_dev.h"
+
+namespace moe {
+
+constexpr int kFrontWaves = 16;
+constexpr int kFrontMaxT = 64;
+constexpr int kFrontMaxRows = kFrontMaxT * (MOE_MAX_TOPK + 1);
+
+struct FrontArgs {
+    const float* logits;
+    const uint16_t* x;
+    int T, D, E, k, n_shared;
+    int n_groups, topk_groups;
+    const float* sel_bias;
+    int renormalize;
+    float route_scale;
+    int block_m, max_rows;
+    int* ids;
+    float* w;
+    int* counts;
+    int* offsets;
+    int* sorted;
+    int* bexp;
+    int* inv;
+    uint8_t* xq;               // FP8 modes: codes [T, D]; NULL for bf16
+    float* xs;                 // scales [T] or [T, D/128]
+};
+
+// One row of x into codes with the wave, in chunks of 4096 elements (8
+// vectors of 8 per lane, all loads of a chunk in flight together).  GROUP 0
+// (one scale per row): amax over the chunks, then codes (a single-chunk row
+// stays in registers, longer rows are read again); GROUP 128: one pass,
+// 16-lane groups.
+template <int GROUP>
+__device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, int K, uint8_t* __restrict__ qr,
+                                               float* __restrict__ sr, int lane) {
+    constexpr int CV = 8;
+    const int nvec = K >> 3;
+    const int nch = (nvec + 64 * CV - 1) / (64 * CV);
+    const bf16x8* xv = reinterpret_cast<const bf16x8*>(xr);
+    uint2* qv = reinterpret_cast<uint2*>(qr);
+    bf16x8 v[CV];
+    auto load = [&](int ch) {
+#pragma unroll
+        for (int i = 0; i < CV; ++i) {
+            const int c = ch * 64 * CV + lane + 64 * i;
+            v[i] = c < nvec ? xv[c] : bf16x8{};
+        }
+    };
+    if constexpr (GROUP == 0) {
+        float m = 0.0f;
+        for (int ch = 0; ch < nch; ++ch) {
+            load(ch);
+#pragma unroll
+            for (int i = 0; i < CV; ++i) m = fmaxf(m, amax8(v[i]));
+        }
+        m = wave_max(m);
+        float sc, inv;
+        scale_pair(m, sc, inv);
+        for (int ch = 0; ch < nch; ++ch) {
+            if (nch > 1) load(ch);
+#pragma unroll
+            for (int i = 0; i < CV; ++i) {
+                const int c = ch * 64 * CV + lane + 64 * i;
+                if (c < nvec) qv[c] = quant8(v[i], inv);
+            }
+        }
+        if (lane == 0) sr[0] = sc;
+    } else {
+        for (int ch = 0; ch < nch; ++ch) {
+            load(ch);
+#pragma unroll
+            for (int i = 0; i < CV; ++i) {
+                const int c = ch * 64 * CV + lane + 64 * i;
+                float m = amax8(v[i]);
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                float sc, inv;
+                scale_pair(m, sc, inv);
+                if (c < nvec) {
+                    qv[c] = quant8(v[i], inv);
+                    if ((lane & 15) == 0) sr[c >> 4] = sc;
+                }
+            }
+        }
+    }
+}
+
+// GROUP: -1 (bf16 layer, no quantization), 0 (per row), 128 (1x128).
+template <int EPL, int SCORING, int GROUP>
+__global__ void __launch_bounds__(kFrontWaves * 64) front_small_kernel(const FrontArgs p) {
+    __shared__ int s_e[kFrontMaxRows];           // expert of each routed row (-1: no row)
+    __shared__ uint32_t s_mlo[MOE_MAX_EXPERTS];  // tokens 0..31 routed to the expert
+    __shared__ uint32_t s_mhi[MOE_MAX_EXPERTS];  // tokens 32..63
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];   // padded offsets
+    __shared__ int s_wave[kFrontWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NT = kFrontWaves * 64;
+    const int E = p.E, Ep = E + p.n_shared, k = p.k, B = p.block_m, T = p.T;
+    const int TK = T * k, A = T * (k + p.n_shared);
+
+    for (int e = tid; e < Ep; e += NT) {
+        s_mlo[e] = 0;
+        s_mhi[e] = 0;
+    }
+    __syncthreads();
+    // 1 + 5. routing of token t and quantization of x row t, wave w takes
+    // t = w, w + 16, ...
+    for (int t = wave; t < T; t += kFrontWaves) {
+        int id;
+        float wt;
+        route_token<EPL, SCORING>(p.logits + static_cast<int64_t>(t) * E, E, k, p.n_groups, p.topk_groups,
+                                  p.sel_bias, p.renormalize, p.route_scale, lane, &id, &wt);
+        if (lane < k) {
+            p.ids[t * k + lane] = id;
+            p.w[t * k + lane] = wt;
+            const int e = (id >= 0 && id < E) ? id : -1;         // no valid pick: no row
+            s_e[t * k + lane] = e;
+            if (e >= 0) {
+                if (t < 32) atomicOr(&s_mlo[e], 1u << t);
+                else atomicOr(&s_mhi[e], 1u << (t - 32));
+            }
+        }
+        if constexpr (GROUP >= 0) {
+            const int ng = GROUP == 0 ? 1 : p.D / 128;
+            quant_row_wave<GROUP>(p.x + static_cast<int64_t>(t) * p.D, p.D, p.xq + static_cast<int64_t>(t) * p.D,
+                                  p.xs + static_cast<int64_t>(t) * ng, lane);
+        }
+    }
+    __syncthreads();
+
+    // 2. counts and padded offsets (one expert per thread, Ep <= 1024)
+    const int c = tid < E ? __popc(s_mlo[tid]) + __popc(s_mhi[tid]) : (tid < Ep ? T : 0);
+    const int padded = (c + B - 1) / B * B;
+    int inc = wave_incl_scan_i(padded, lane);
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        const int v = lane < kFrontWaves ? s_wave[lane] : 0;
+        const int sc = wave_incl_scan_i(v, lane);
+        if (lane < kFrontWaves) s_wave[lane] = sc - v;           // exclusive wave bases
+    }
+    __syncthreads();
+    inc += s_wave[wave];
+    if (tid < Ep) {
+        s_off[tid + 1] = inc;
+        p.counts[tid] = c;
+        p.offsets[tid + 1] = inc;
+    }
+    if (tid == 0) {
+        s_off[0] = 0;
+        p.offsets[0] = 0;
+    }
+    __syncthreads();
+
+    // 3. rows: rank of token t in expert e = tokens below t routed to e
+    for (int f = tid; f < A; f += NT) {
+        int row;
+        if (f < TK) {
+            const int e = s_e[f], t = f / k;
+            if (e < 0) {
+                p.inv[f] = -1;
+                continue;
+            }
+            const int below = t < 32 ? __popc(s_mlo[e] & ((1u << t) - 1u))
+                                      : __popc(s_mlo[e]) + __popc(s_mhi[e] & ((1u << (t - 32)) - 1u));
+            row = s_off[e] + below;
+        } else {
+            row = s_off[E] + (f - TK);                                  // shared expert: token order
+        }
+        p.sorted[row] = f;
+        p.inv[f] = row;
+    }
+    // 4. pads and block map (one wave per expert), tail past the total
+    for (int e = wave; e < Ep; e += kFrontWaves) {
+        const int n = e < E ? __popc(s_mlo[e]) + __popc(s_mhi[e]) : T;
+        const int lo = s_off[e], hi = s_off[e + 1];
+        for (int r = lo + n + lane; r < hi; r += 64) p.sorted[r] = A;
+        for (int b = lo / B + lane; b < hi / B; b += 64) p.bexp[b] = e;
+    }
+    const int total = s_off[Ep];
+    for (int b = total / B + tid; b < p.max_rows / B; b += NT) p.bexp[b] = -1;
+    for (int r = total + tid; r < p.max_rows; r += NT) p.sorted[r] = A;
+}
+
+template <int EPL, int SCORING>
+static void front_group(int group, const FrontArgs& a, hipStream_t s) {
+    const dim3 g(1), b(kFrontWaves * 64);
+    if (group < 0) hipLaunchKernelGGL((front_small_kernel<EPL, SCORING, -1>), g, b, 0, s, a);
+    else if (group == 0) hipLaunchKernelGGL((front_small_kernel<EPL, SCORING, 0>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((front_small_kernel<EPL, SCORING, 128>), g, b, 0, s, a);
+}
+
+template <int EPL>
+static void front_scoring(int scoring, int group, const FrontArgs& a, hipStream_t s) {
+    if (scoring == MOE_SCORING_SOFTMAX) front_group<EPL, 0>(group, a, s);
+    else front_group<EPL, 1>(group, a, s);
+}
+
+bool front_small_ok(int T, int k, int n_shared) {
+    return T >= 1 && T <= kFrontMaxT && T * (k + n_shared) <= kFrontMaxRows;
+}
+
+int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int block_m,
+                           int max_rows, int* ids, float* w, int* counts, int* offsets, int* sorted, int* bexp,
+                           int* inv, uint8_t* xq, float* xs, hipStream_t s) {
+    FrontArgs a{};
+    a.logits = logits;
+    a.x = static_cast<const uint16_t*>(x);
+    a.T = T;
+    a.D = L->D;
+    a.E = L->E;
+    a.k = L->top_k;
+    a.n_shared = L->n_shared;
+    a.n_groups = L->n_groups;
+    a.topk_groups = L->topk_groups;
+    a.sel_bias = L->sel_bias;
+    a.renormalize = L->renormalize;
+    a.route_scale = L->route_scale;
+    a.block_m = block_m;
+    a.max_rows = max_rows;
+    a.ids = ids;
+    a.w = w;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.sorted = sorted;
+    a.bexp = bexp;
+    a.inv = inv;
+    a.xq = xq;
+    a.xs = xs;
+    const int group = L->quant == MOE_QUANT_NONE_BF16 ? -1 : (L->quant == MOE_QUANT_BLOCK128_FP8 ? 128 : 0);
+    const int epl = static_cast<int>(ceil_div(L->E, 64));
+    if (epl <= 1) front_scoring<1>(L->scoring, group, a, s);
+    else if (epl <= 2) front_scoring<2>(L->scoring, group, a, s);
+    else if (epl <= 4) front_scoring<4>(L->scoring, group, a, s);
+    else if (epl <= 8) front_scoring<8>(L->scoring, group, a, s);
+    else front_scoring<16>(L->scoring, group, a, s);
+    return moe_launch_status();
+}
+
+}  // namespace moe

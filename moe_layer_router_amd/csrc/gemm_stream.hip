@@ -5,15 +5,20 @@
 // finds MoE inference memory-bound; its 2.1.4 tunes CU-level load balance at
 // low concurrency; the MI355X MoRI page notes that small-batch TP decode
 // gives tall-skinny expert GEMMs).  Design:
-//   - one workgroup = one expert x a slice of weight rows; the expert's rows
-//     (at most 16*MT, every expert holds at most T rows) are all handled by
-//     the wave that streams a weight slice, so each weight byte is read once;
+//   - the work is (active expert x slice of weight rows) items, one wave per
+//     item; the expert's rows (at most 16*MT, every expert holds at most T
+//     rows) are all handled by the wave that streams the slice, so each
+//     weight byte is read once;
+//   - the grid is persistent (the workgroups that fit at once); each
+//     workgroup lists the active experts (offsets[e+1] > offsets[e]) in LDS
+//     and its waves walk the items so that every CU gets the same number of
+//     items within one: only active experts cost time and no second, partly
+//     filled round of workgroups idles most of the chip;
 //   - no LDS: each lane streams 32 B of a weight row per 128-byte K step
 //     straight into MFMA operand registers (v_mfma_f32_16x16x128_f8f6f4, or
 //     two v_mfma_f32_16x16x32_bf16), the next step's loads in flight while
 //     the current step multiplies;
-//   - activation rows are tiny and stay in L2;
-//   - workgroups of experts without rows exit at once.
+//   - activation rows are tiny and stay in L2.
 #include "common.h"
 
 namespace moe {
@@ -41,6 +46,8 @@ struct StreamArgs {
     int I;                     // gate_up act columns
     void* out;
     int64_t out_ld;
+    int n_exp;                 // E'
+    int nslice;                // weight slices (one wave each) per expert
 };
 
 template <int MODE>
@@ -86,16 +93,14 @@ __device__ __forceinline__ int src_row(const StreamArgs& p, bool gateup, int row
 // MT: 16-row activation tiles (rows per expert <= 16*MT).  PF: K steps in
 // flight.  The steady-state loop has no data-dependent branch, so the
 // compiler can wait for exactly the step it is about to use.
+// One item: expert E, weight slice SL (COLS_W output columns), on this wave.
 template <int MODE, bool GATEUP, int TN, int MT, int PF>
-__global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
+__device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, int lane) {
     constexpr bool BLOCKQ = MODE == MOE_QUANT_BLOCK128_FP8;
     constexpr int COLS_W = GATEUP ? TN / 2 * 16 : TN * 16;     // output columns per wave
-    const int e = blockIdx.y;
     const int row0 = p.offsets[e];
     const int cnt = p.offsets[e + 1] - row0;                    // padded rows of this expert
-    if (cnt == 0) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c0 = (blockIdx.x * 4 + wave) * COLS_W;            // first output column of this wave
+    const int c0 = sl * COLS_W;                                 // first output column of this wave
     const int r16 = lane & 15, kq = (lane >> 4) * 16;
 
     const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
@@ -138,10 +143,10 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
         for (int t = 0; t < TN; ++t) acc[m][t] = v4f{0, 0, 0, 0};
 
     const int nk = static_cast<int>(wrow / 128);
-    // Each wave starts its K sweep at its own step (wrapping around), so the
-    // waves spread over the byte offsets of the weight rows.  The K order of a
-    // wave is fixed by its position: results stay deterministic.
-    const int kbeg = ((blockIdx.x * 4 + wave) * 5 + e * 3) % nk;
+    // Each item starts its K sweep at its own step (wrapping around), so the
+    // waves spread over the byte offsets of the weight rows.  The K order is
+    // fixed by the item (expert, slice): results stay deterministic.
+    const int kbeg = (sl * 5 + e * 3) % nk;
 
     u32x8 bq[PF][TN], aqr[PF][MT];
     float asq[PF][MT][4];
@@ -184,16 +189,23 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
         }
     };
 
+    // prologue: PF fills, unconditional (a step index past the end reloads
+    // the last step, never used) so the compiler knows exactly how many
+    // loads are in flight when the steady loop starts
 #pragma unroll
-    for (int j = 0; j < PF; ++j)
-        if (j < nk) fill(j, j);
+    for (int j = 0; j < PF; ++j) fill(j, j < nk ? j : nk - 1);
     int s0 = 0;
-    // steady state: every refill targets a step < nk
+    // steady state: every refill targets a step < nk.  Scheduling barriers
+    // keep "MFMAs of step s, then the loads of step s + PF" in program order
+    // (hoisting the MFMAs above the loads would leave each step waiting on
+    // loads issued just before it).
     for (; s0 + 2 * PF <= nk; s0 += PF) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             compute(j, s0 + j);
+            __builtin_amdgcn_sched_barrier(0);
             fill(j, s0 + j + PF);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // tail: the last PF .. 2PF-1 steps
@@ -245,6 +257,42 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
     }
 }
 
+// Persistent: G workgroups of 4 waves.  Item i (active expert i / nslice,
+// slice i % nslice) goes to workgroup i % G, wave (i / G) % 4, round
+// i / (4G): consecutive items spread over workgroups first, so the per-CU
+// item counts differ by at most one.
+template <int MODE, bool GATEUP, int TN, int MT, int PF>
+__global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
+    __shared__ int s_act[MOE_MAX_EXPERTS];
+    __shared__ int s_wcnt[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // active experts in index order: thread t looks at experts t, t+256, ...
+    int base = 0;
+    for (int e0 = 0; e0 < p.n_exp; e0 += 256) {
+        const int e = e0 + threadIdx.x;
+        const bool act = e < p.n_exp && p.offsets[e + 1] > p.offsets[e];
+        const uint64_t m = __ballot(act);
+        if (lane == 0) s_wcnt[wave] = __popcll(m);
+        __syncthreads();
+        int before = base;
+        for (int w = 0; w < wave; ++w) before += s_wcnt[w];
+        if (act) s_act[before + __popcll(m & ((uint64_t{1} << lane) - 1))] = e;
+        base += s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+        __syncthreads();
+    }
+    const int n_items = base * p.nslice;
+    const int G = gridDim.x;
+    for (int i = blockIdx.x + G * wave; i < n_items; i += 4 * G) {
+        const int j = i / p.nslice, e = s_act[j];
+        // experts with at most 16 rows take the one-tile path (half the
+        // activation loads and registers); each path is branch-free inside
+        if (MT > 1 && p.offsets[e + 1] - p.offsets[e] <= 16)
+            stream_item<MODE, GATEUP, TN, 1, PF>(p, e, i - j * p.nslice, lane);
+        else
+            stream_item<MODE, GATEUP, TN, MT, PF>(p, e, i - j * p.nslice, lane);
+    }
+}
+
 #ifndef MOE_STREAM_TN
 #define MOE_STREAM_TN 2
 #endif
@@ -254,14 +302,40 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
 constexpr int kStreamTN = MOE_STREAM_TN;     // 16-row weight tiles per wave
 constexpr int kStreamPF = MOE_STREAM_PF;     // K steps in flight per wave
 
-template <int MODE, bool GATEUP>
-static int32_t stream_launch_mode(const StreamArgs& a, int Ep, int ncols, int T, hipStream_t s) {
-    constexpr int COLS_W = GATEUP ? kStreamTN / 2 * 16 : kStreamTN * 16;
-    const dim3 grid(static_cast<unsigned>(ncols / (4 * COLS_W)), static_cast<unsigned>(Ep)), block(256);
-    if (T <= 16) hipLaunchKernelGGL((stream_gemm_kernel<MODE, GATEUP, kStreamTN, 1, kStreamPF>), grid, block, 0, s, a);
-    else if (T <= 32) hipLaunchKernelGGL((stream_gemm_kernel<MODE, GATEUP, kStreamTN, 2, kStreamPF>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stream_gemm_kernel<MODE, GATEUP, kStreamTN, 4, kStreamPF>), grid, block, 0, s, a);
+// Workgroups of a kernel that fit on the device at once, per device.
+template <typename Kern>
+static int resident_blocks(Kern kernel) {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (n == 0) {
+        int cus = 0, occ = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess || occ <= 0) occ = 1;
+        n = cus * occ;
+        __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+    }
+    return n;
+}
+
+template <int MODE, bool GATEUP, int MT>
+static int32_t stream_launch_mt(const StreamArgs& a, hipStream_t s) {
+    auto kern = stream_gemm_kernel<MODE, GATEUP, kStreamTN, MT, kStreamPF>;
+    // no more workgroups than items could need (E' experts x slices / 4 waves)
+    const int wgs = min(resident_blocks(kern), static_cast<int>(ceil_div(static_cast<int64_t>(a.n_exp) * a.nslice, 4)));
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(max(wgs, 1))), dim3(256), 0, s, a);
     return moe_launch_status();
+}
+
+template <int MODE, bool GATEUP>
+static int32_t stream_launch_mode(StreamArgs a, int Ep, int ncols, int T, hipStream_t s) {
+    constexpr int COLS_W = GATEUP ? kStreamTN / 2 * 16 : kStreamTN * 16;
+    a.n_exp = Ep;
+    a.nslice = ncols / COLS_W;
+    if (T <= 16) return stream_launch_mt<MODE, GATEUP, 1>(a, s);
+    if (T <= 32) return stream_launch_mt<MODE, GATEUP, 2>(a, s);
+    return stream_launch_mt<MODE, GATEUP, 4>(a, s);
 }
 
 template <bool GATEUP>
@@ -274,8 +348,6 @@ static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, 
     return MOE_ERR_UNSUPPORTED;
 }
 
-// Columns per workgroup: gate_up 128 act columns, down 256 output columns.
-int stream_cols_per_block(bool gateup) { return gateup ? 4 * (kStreamTN / 2) * 16 : 4 * kStreamTN * 16; }
 
 int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
                              const int* sorted_ids, const int* offsets, void* act, hipStream_t s) {
