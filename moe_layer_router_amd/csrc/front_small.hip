@@ -1,24 +1,21 @@
-// Fused front end for small batches (decode).
+// Front end for small batches (decode), in two launches.
 //
 // At a few dozen tokens the routing, the three permutation steps and the FP8
-// quantization of x each move a few KB; as separate launches they cost more
-// in launch latency and dependent round trips than in work (the Qwen 3.5
-// roadmap item asks for top-k to run next to the scores, and the MI300X
-// page tunes small-batch latency).  Here one workgroup of 16 waves does all
-// of it and writes exactly what the separate entry points write:
-//   1. routing: wave w routes tokens w, w+16, ... (route_token, shared with
-//      the routing kernel); the picks also go to LDS;
-//   2. per-expert counts (LDS atomics), padded and unpadded exclusive scans
-//      over experts;
-//   3. a token's k picks are distinct experts and T <= 64, so every expert's
-//      rows are a 64-bit mask of tokens (LDS atomicOr); a row's rank in its
-//      expert's segment is the number of mask bits below its token, which is
-//      the stable ascending order of flat indices the multi-kernel
-//      permutation produces (shared-expert rows: token order);
-//   4. pads, block -> expert map, the tail past the padded total;
-//   5. FP8 quantization of x (per row or per 1x128 group), one wave per row,
-//      the same arithmetic as the row-quantization kernel; each wave issues
-//      its row's loads before routing the same token, so the two overlap.
+// quantization of x each move a few KB; as five separate launches they cost
+// more in launch latency and dependent round trips than in work (the Qwen
+// 3.5 roadmap item asks for top-k to run next to the scores, and the MI300X
+// page tunes small-batch latency).  Here:
+//   token_front_kernel: one workgroup of two waves per token; wave 0 routes
+//     the token (route_token, shared with the routing kernel), wave 1
+//     quantizes its x row (the row-quantization arithmetic), in parallel and
+//     spread over T CUs;
+//   permute_small_kernel: one workgroup.  A token's k picks are distinct
+//     experts and T <= 64, so every expert's rows are a 64-bit mask of
+//     tokens (LDS atomicOr); a row's rank in its expert's segment is the
+//     number of mask bits below its token -- the stable ascending order of
+//     flat indices the multi-kernel permutation produces (shared-expert
+//     rows: token order).  Counts, padded offsets, sorted ids, inverse map,
+//     pads, block -> expert map and the tail are written exactly as there.
 #include "quant_dev.h"
 #include "route_dev.h"
 
@@ -110,7 +107,25 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, 
 
 // GROUP: -1 (bf16 layer, no quantization), 0 (per row), 128 (1x128).
 template <int EPL, int SCORING, int GROUP>
-__global__ void __launch_bounds__(kFrontWaves * 64) front_small_kernel(const FrontArgs p) {
+__global__ void __launch_bounds__(128) token_front_kernel(const FrontArgs p) {
+    const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave == 0) {
+        int id;
+        float wt;
+        route_token<EPL, SCORING>(p.logits + static_cast<int64_t>(t) * p.E, p.E, p.k, p.n_groups, p.topk_groups,
+                                  p.sel_bias, p.renormalize, p.route_scale, lane, &id, &wt);
+        if (lane < p.k) {
+            p.ids[t * p.k + lane] = id;
+            p.w[t * p.k + lane] = wt;
+        }
+    } else if constexpr (GROUP >= 0) {
+        const int ng = GROUP == 0 ? 1 : p.D / 128;
+        quant_row_wave<GROUP>(p.x + static_cast<int64_t>(t) * p.D, p.D, p.xq + static_cast<int64_t>(t) * p.D,
+                              p.xs + static_cast<int64_t>(t) * ng, lane);
+    }
+}
+
+__global__ void __launch_bounds__(kFrontWaves * 64) permute_small_kernel(const FrontArgs p) {
     __shared__ int s_e[kFrontMaxRows];           // expert of each routed row (-1: no row)
     __shared__ uint32_t s_mlo[MOE_MAX_EXPERTS];  // tokens 0..31 routed to the expert
     __shared__ uint32_t s_mhi[MOE_MAX_EXPERTS];  // tokens 32..63
@@ -126,32 +141,18 @@ __global__ void __launch_bounds__(kFrontWaves * 64) front_small_kernel(const Fro
         s_mhi[e] = 0;
     }
     __syncthreads();
-    // 1 + 5. routing of token t and quantization of x row t, wave w takes
-    // t = w, w + 16, ...
-    for (int t = wave; t < T; t += kFrontWaves) {
-        int id;
-        float wt;
-        route_token<EPL, SCORING>(p.logits + static_cast<int64_t>(t) * E, E, k, p.n_groups, p.topk_groups,
-                                  p.sel_bias, p.renormalize, p.route_scale, lane, &id, &wt);
-        if (lane < k) {
-            p.ids[t * k + lane] = id;
-            p.w[t * k + lane] = wt;
-            const int e = (id >= 0 && id < E) ? id : -1;         // no valid pick: no row
-            s_e[t * k + lane] = e;
-            if (e >= 0) {
-                if (t < 32) atomicOr(&s_mlo[e], 1u << t);
-                else atomicOr(&s_mhi[e], 1u << (t - 32));
-            }
-        }
-        if constexpr (GROUP >= 0) {
-            const int ng = GROUP == 0 ? 1 : p.D / 128;
-            quant_row_wave<GROUP>(p.x + static_cast<int64_t>(t) * p.D, p.D, p.xq + static_cast<int64_t>(t) * p.D,
-                                  p.xs + static_cast<int64_t>(t) * ng, lane);
+    for (int f = tid; f < TK; f += NT) {
+        const int id = p.ids[f], t = f / k;
+        const int e = (id >= 0 && id < E) ? id : -1;             // no valid pick: no row
+        s_e[f] = e;
+        if (e >= 0) {
+            if (t < 32) atomicOr(&s_mlo[e], 1u << t);
+            else atomicOr(&s_mhi[e], 1u << (t - 32));
         }
     }
     __syncthreads();
 
-    // 2. counts and padded offsets (one expert per thread, Ep <= 1024)
+    // counts and padded offsets (one expert per thread, Ep <= 1024)
     const int c = tid < E ? __popc(s_mlo[tid]) + __popc(s_mhi[tid]) : (tid < Ep ? T : 0);
     const int padded = (c + B - 1) / B * B;
     int inc = wave_incl_scan_i(padded, lane);
@@ -175,7 +176,7 @@ __global__ void __launch_bounds__(kFrontWaves * 64) front_small_kernel(const Fro
     }
     __syncthreads();
 
-    // 3. rows: rank of token t in expert e = tokens below t routed to e
+    // rows: rank of token t in expert e = tokens below t routed to e
     for (int f = tid; f < A; f += NT) {
         int row;
         if (f < TK) {
@@ -193,7 +194,7 @@ __global__ void __launch_bounds__(kFrontWaves * 64) front_small_kernel(const Fro
         p.sorted[row] = f;
         p.inv[f] = row;
     }
-    // 4. pads and block map (one wave per expert), tail past the total
+    // pads and block map (one wave per expert), tail past the total
     for (int e = wave; e < Ep; e += kFrontWaves) {
         const int n = e < E ? __popc(s_mlo[e]) + __popc(s_mhi[e]) : T;
         const int lo = s_off[e], hi = s_off[e + 1];
@@ -207,10 +208,10 @@ __global__ void __launch_bounds__(kFrontWaves * 64) front_small_kernel(const Fro
 
 template <int EPL, int SCORING>
 static void front_group(int group, const FrontArgs& a, hipStream_t s) {
-    const dim3 g(1), b(kFrontWaves * 64);
-    if (group < 0) hipLaunchKernelGGL((front_small_kernel<EPL, SCORING, -1>), g, b, 0, s, a);
-    else if (group == 0) hipLaunchKernelGGL((front_small_kernel<EPL, SCORING, 0>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((front_small_kernel<EPL, SCORING, 128>), g, b, 0, s, a);
+    const dim3 g(static_cast<unsigned>(a.T)), b(128);
+    if (group < 0) hipLaunchKernelGGL((token_front_kernel<EPL, SCORING, -1>), g, b, 0, s, a);
+    else if (group == 0) hipLaunchKernelGGL((token_front_kernel<EPL, SCORING, 0>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((token_front_kernel<EPL, SCORING, 128>), g, b, 0, s, a);
 }
 
 template <int EPL>
@@ -257,6 +258,7 @@ int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* 
     else if (epl <= 4) front_scoring<4>(L->scoring, group, a, s);
     else if (epl <= 8) front_scoring<8>(L->scoring, group, a, s);
     else front_scoring<16>(L->scoring, group, a, s);
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kFrontWaves * 64), 0, s, a);
     return moe_launch_status();
 }
 

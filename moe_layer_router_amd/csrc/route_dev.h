@@ -11,14 +11,44 @@ __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
-// Arg-best of the wave: every lane ends with the winning (value, index).
-__device__ __forceinline__ void wave_argbest(float& v, int& i) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(v, o, 64);
-        const int oi = __shfl_xor(i, o, 64);
-        if (beats(ov, oi, v, i)) { v = ov; i = oi; }
+// One step of a DPP reduction: take (value, index) from the lane the DPP
+// control names when it beats ours (lanes without a source keep their own).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_best_step(float& v, int& i) {
+    const float ov = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                           false));
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xF, false);
+    if (beats(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
     }
+}
+
+// Arg-best of the wave, returned wave-uniform: DPP row shifts by 1, 2, 4, 8
+// leave each 16-lane row's best in its lane 15, row broadcasts 15 and 31
+// carry them to lane 63, which v_readlane reads.  (value, index) under
+// `beats` is a total order, so the result does not depend on the tree.
+__device__ __forceinline__ void wave_argbest(float& v, int& i) {
+    dpp_best_step<0x111, 0xF>(v, i);   // row_shr:1
+    dpp_best_step<0x112, 0xF>(v, i);   // row_shr:2
+    dpp_best_step<0x114, 0xF>(v, i);   // row_shr:4
+    dpp_best_step<0x118, 0xF>(v, i);   // row_shr:8
+    dpp_best_step<0x142, 0xA>(v, i);   // row_bcast:15 into rows 1 and 3
+    dpp_best_step<0x143, 0xC>(v, i);   // row_bcast:31 into rows 2 and 3
+    v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// value of lane j (j wave-uniform)
+__device__ __forceinline__ float lane_f(float v, int j) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+}
+__device__ __forceinline__ double lane_d(double v, int j) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), j);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), j);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // Largest two of the wave (values only), every lane ends with (m1, m2).
@@ -83,7 +113,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lr, int E,
         // group g is kept iff fewer than topk_groups groups rank before it
         int r = 0;
         for (int h = 0; h < n_groups; ++h) {
-            const float other = __shfl(mine, h, 64);
+            const float other = lane_f(mine, h);
             r += (h != lane) && beats(other, h, mine, lane);
         }
         const uint64_t keep = __ballot(lane < n_groups && r < topk_groups);
@@ -115,7 +145,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lr, int E,
             for (int q = 0; q < EPL; ++q)
                 if (q == i) { s_pick = sc[q]; key[q] = NEG; }
         }
-        s_pick = __shfl(s_pick, bi & 63, 64);
+        s_pick = lane_f(s_pick, bi & 63);
         if (j == 0) vfirst = s_pick;
         if (lane == j) { selv = s_pick; seli = bi; }
     }
@@ -126,7 +156,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lr, int E,
         const double lmax = static_cast<double>(vfirst);
         wj = lane < k ? exp(static_cast<double>(selv) - lmax) : 0.0;
         if (renormalize) {
-            for (int j = 0; j < k; ++j) den += __shfl(wj, j, 64);
+            for (int j = 0; j < k; ++j) den += lane_d(wj, j);
         } else {
             double part = 0.0;
 #pragma unroll
@@ -143,7 +173,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lr, int E,
     } else {
         wj = lane < k ? static_cast<double>(selv) : 0.0;
         if (renormalize) {
-            for (int j = 0; j < k; ++j) den += __shfl(wj, j, 64);
+            for (int j = 0; j < k; ++j) den += lane_d(wj, j);
             wj = wj / den;
         }
         wj *= static_cast<double>(route_scale);
