@@ -97,7 +97,7 @@ class Steps:
         if ev is not None:
             ev[0].record()
         L.check("gateup", lib.moe_grouped_gemm_gateup_silu(d, a, a_s, self.T, self.B, p["sorted_ids"],
-                                                           p["block_expert"], p["offsets"], p["act"], s))
+                                                           p["block_expert"], p["offsets"], p["counts"], p["act"], s))
         if ev is not None:
             ev[1].record()
         act, act_s = p["act"], None
@@ -108,7 +108,7 @@ class Steps:
         if ev is not None:
             ev[2].record()
         L.check("down", lib.moe_grouped_gemm_down(d, act, act_s, self.T, self.B, p["block_expert"], p["offsets"],
-                                                  p["out_perm"], s))
+                                                  p["counts"], p["out_perm"], s))
         if ev is not None:
             ev[3].record()
         L.check("combine", lib.moe_unpermute_combine(p["out_perm"], 1 if fp8 else 0, p["inv_perm"], p["topk_w"],

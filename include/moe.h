@@ -208,30 +208,34 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
  *   activation scale and the weight scales), act[r] = bf16(silu(g) * u).
  * a: quant 0: x bf16 [T, D]; quant 1/2: codes [T, D] with a_scale [T] or
  * [T, D/128].  act: [R, I] bf16 where R = moe_permute_max_rows(...).
+ * expert_counts (device, [E+n_shared], as moe_permute_align writes it; may
+ * be NULL) lets the LDS-tiled kernels skip the 32-row tiles at the end of an
+ * expert's segment that hold only pads; it must match expert_offsets.
  * Pad rows (sentinel) get act = 0; rows at or past expert_offsets[E'] are not
  * written.  block_m must equal the block_m of moe_permute_align and be one
- * of: 16 (weight-streaming kernels for small batches; requires T <= 64 and
- * at most T rows per expert, which holds when each token's k ids are
- * distinct), 32, 64, 128 or 256 (LDS-tiled kernels; the blockwise FP8
- * mode supports 16 and 32 only).  Shapes: I % 128 == 0 and D % 256 == 0.
+ * of: 16 (weight-streaming kernels for small batches: each weight byte is
+ * read once per 64 rows of its expert), 32, 64, 128 or 256 (LDS-tiled
+ * kernels).  Shapes: I % 128 == 0 and D % 256 == 0.
  */
 int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
                                      const float* a_scale, int32_t T, int32_t block_m,
                                      const int32_t* sorted_ids, const int32_t* block_expert,
-                                     const int32_t* expert_offsets, void* act_bf16,
-                                     void* stream);
+                                     const int32_t* expert_offsets, const int32_t* expert_counts,
+                                     void* act_bf16, void* stream);
 
 /*
  * Grouped GEMM down: out_perm[r] = act[r] . W2[e]^T for the valid rows
- * (dequantized by the row scale(s) and the weight scales).  Same block_m and
- * shape rules as moe_grouped_gemm_gateup_silu; pad rows of act must hold
- * zeros (moe_grouped_gemm_gateup_silu writes them so).  act: quant 0:
+ * (dequantized by the row scale(s) and the weight scales).  Same block_m,
+ * expert_counts and shape rules as moe_grouped_gemm_gateup_silu.  Pad rows
+ * of out_perm are written as 0; with expert_counts NULL that needs the pad
+ * rows of act to hold zeros (moe_grouped_gemm_gateup_silu writes them so).  act: quant 0:
  * bf16 [R, I]; quant 1/2: codes [R, I] with act_scale [R] or [R, I/128].
  * out_perm [R, D]: fp32 for quant 0, bf16 for quant 1/2.
  */
 int32_t moe_grouped_gemm_down(const moe_layer_desc* L, const void* act, const float* act_scale,
                               int32_t T, int32_t block_m, const int32_t* block_expert,
-                              const int32_t* expert_offsets, void* out_perm, void* stream);
+                              const int32_t* expert_offsets, const int32_t* expert_counts,
+                              void* out_perm, void* stream);
 
 /*
  * Unpermute and weighted combine (SparseCore unpermutation item of the

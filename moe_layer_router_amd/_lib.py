@@ -48,9 +48,9 @@ SIGNATURES = {
     "moe_quant_weight_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                        c_void_p]),
     "moe_grouped_gemm_gateup_silu": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_int32,
-                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_grouped_gemm_down": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_int32, c_void_p,
-                                        c_void_p, c_void_p, c_void_p]),
+                                        c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_unpermute_combine": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                         c_int32, c_void_p, c_void_p]),
     "moe_default_block_m": (c_int32, [POINTER(LayerDesc), c_int32]),

@@ -22,10 +22,10 @@ int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* 
                            int* inv, uint8_t* xq, float* xs, hipStream_t s);
 int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T, int block_m,
                            int64_t max_rows, const int* sorted_ids, const int* block_expert, const int* offsets,
-                           void* act, hipStream_t s);
+                           const int* counts, void* act, hipStream_t s);
 int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T, int block_m,
-                         int64_t max_rows, const int* block_expert, const int* offsets, void* out_perm,
-                         hipStream_t s);
+                         int64_t max_rows, const int* block_expert, const int* offsets, const int* counts,
+                         void* out_perm, hipStream_t s);
 int32_t combine_launch(const void* out_perm, int out_dtype, const int* inv_perm, const float* topk_w, int T,
                        int k, int n_shared, int D, uint16_t* y, hipStream_t s);
 }  // namespace moe
@@ -46,14 +46,12 @@ int64_t max_rows_of(int64_t T, int64_t k, int64_t E, int64_t n_sh, int64_t B) {
     return blocks * B;
 }
 
-// block_m 16 selects the weight-streaming kernels (every expert holds at most
-// T rows, so T <= 64 bounds the rows one wave carries); 32/64/128 the LDS-tiled ones.
-constexpr int kStreamMaxT = 64;
+// block_m 16 selects the weight-streaming kernels (a wave carries up to 64
+// rows of an expert at a time); 32/64/128/256 the LDS-tiled ones.
+constexpr int kStreamMaxT = 64;          // the automatic choice streams at or below this batch
 
-bool block_m_ok(int quant, int block_m, int T) {
-    if (block_m == 16) return T <= kStreamMaxT;
-    if (block_m == 32) return true;
-    return (block_m == 64 || block_m == 128 || block_m == 256) && quant != MOE_QUANT_BLOCK128_FP8;
+bool block_m_ok(int block_m) {
+    return block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128 || block_m == 256;
 }
 
 int32_t check_routing(int E, int k, int scoring, int n_groups, int topk_groups) {
@@ -212,31 +210,33 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
 
 int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a, const float* a_scale, int32_t T,
                                      int32_t block_m, const int32_t* sorted_ids, const int32_t* block_expert,
-                                     const int32_t* expert_offsets, void* act_bf16, void* stream) {
+                                     const int32_t* expert_offsets, const int32_t* expert_counts, void* act_bf16,
+                                     void* stream) {
     int32_t st = check_layer(L);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(T >= 0);
-    MOE_CHECK_SUP(block_m_ok(L->quant, block_m, T));
+    MOE_CHECK_SUP(block_m_ok(block_m));
     if (T == 0) return MOE_OK;
     MOE_CHECK_ARG(a && sorted_ids && block_expert && expert_offsets && act_bf16);
     MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || a_scale);
     const int64_t R = max_rows_of(T, L->top_k, L->E, L->n_shared, block_m);
-    return gemm_gateup_launch(L, a, a_scale, T, block_m, R, sorted_ids, block_expert, expert_offsets, act_bf16,
+    return gemm_gateup_launch(L, a, a_scale, T, block_m, R, sorted_ids, block_expert, expert_offsets, expert_counts,
+                              act_bf16,
                               as_stream(stream));
 }
 
 int32_t moe_grouped_gemm_down(const moe_layer_desc* L, const void* act, const float* act_scale, int32_t T,
                               int32_t block_m, const int32_t* block_expert, const int32_t* expert_offsets,
-                              void* out_perm, void* stream) {
+                              const int32_t* expert_counts, void* out_perm, void* stream) {
     int32_t st = check_layer(L);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(T >= 0);
-    MOE_CHECK_SUP(block_m_ok(L->quant, block_m, T));
+    MOE_CHECK_SUP(block_m_ok(block_m));
     if (T == 0) return MOE_OK;
     MOE_CHECK_ARG(act && block_expert && expert_offsets && out_perm);
     MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || act_scale);
     const int64_t R = max_rows_of(T, L->top_k, L->E, L->n_shared, block_m);
-    return gemm_down_launch(L, act, act_scale, T, block_m, R, block_expert, expert_offsets, out_perm,
+    return gemm_down_launch(L, act, act_scale, T, block_m, R, block_expert, expert_offsets, expert_counts, out_perm,
                             as_stream(stream));
 }
 
@@ -257,17 +257,17 @@ int32_t moe_default_block_m(const moe_layer_desc* L, int32_t T) {
     const int64_t rows = static_cast<int64_t>(T) * (L->top_k + L->n_shared);
     const int64_t per_expert = rows / (L->E + L->n_shared);
     if (T <= kStreamMaxT) return 16;
-    if (L->quant == MOE_QUANT_BLOCK128_FP8) return 32;
-    if (per_expert >= 320) return 256;
-    if (per_expert >= 96) return 128;
-    if (per_expert >= 48) return 64;
+    // 32-row tiles of pads are skipped, so a tall tile costs little beyond
+    // the expert's rows and reads each weight tile once per 256 rows
+    if (per_expert >= 96) return 256;
+    if (per_expert >= 48) return 128;
     return 32;
 }
 
 size_t moe_forward_workspace_size(const moe_layer_desc* L, int32_t T, int32_t block_m) {
     if (check_layer(L) != MOE_OK || T < 0) return 0;
     if (block_m == 0) block_m = moe_default_block_m(L, T);
-    if (!block_m_ok(L->quant, block_m, T)) return 0;
+    if (!block_m_ok(block_m)) return 0;
     moe_ws_layout o;
     layout_of(L, T, block_m, &o);
     return static_cast<size_t>(o.total);
@@ -278,7 +278,7 @@ int32_t moe_workspace_layout(const moe_layer_desc* L, int32_t T, int32_t block_m
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(T >= 0 && out);
     if (block_m == 0) block_m = moe_default_block_m(L, T);
-    MOE_CHECK_SUP(block_m_ok(L->quant, block_m, T));
+    MOE_CHECK_SUP(block_m_ok(block_m));
     layout_of(L, T, block_m, out);
     return MOE_OK;
 }
@@ -289,7 +289,7 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(T >= 0);
     if (block_m == 0) block_m = moe_default_block_m(L, T);
-    MOE_CHECK_SUP(block_m_ok(L->quant, block_m, T));
+    MOE_CHECK_SUP(block_m_ok(block_m));
     const int64_t A = static_cast<int64_t>(T) * (L->top_k + L->n_shared);
     MOE_CHECK_SUP(A < (1LL << 30));
     if (T == 0) return MOE_OK;
@@ -346,7 +346,9 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
             return st;
     }
     void* act = at(o.act);
-    if ((st = gemm_gateup_launch(L, a, a_scale, T, block_m, o.max_rows, sorted, bexp, offsets, act, s)) != MOE_OK)
+    const int* counts = static_cast<int*>(at(o.counts));
+    if ((st = gemm_gateup_launch(L, a, a_scale, T, block_m, o.max_rows, sorted, bexp, offsets, counts, act, s)) !=
+        MOE_OK)
         return st;
     const void* act_in = act;
     const float* act_scale = nullptr;
@@ -358,7 +360,8 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
         act_scale = static_cast<float*>(at(o.as));
     }
     void* outp = at(o.out_perm);
-    if ((st = gemm_down_launch(L, act_in, act_scale, T, block_m, o.max_rows, bexp, offsets, outp, s)) != MOE_OK)
+    if ((st = gemm_down_launch(L, act_in, act_scale, T, block_m, o.max_rows, bexp, offsets, counts, outp, s)) !=
+        MOE_OK)
         return st;
     return combine_launch(outp, fp8 ? 1 : 0, inv, w, T, k, L->n_shared, L->D, static_cast<uint16_t*>(y_bf16), s);
 }

@@ -82,6 +82,7 @@ struct GemmArgs {
     int topk, TK, sentinel;
     const int* block_expert;
     const int* offsets;        // [E'+1] padded expert offsets
+    const int* counts;         // [E'] routed rows per expert (NULL: every row of a segment is live)
     const uint8_t* w;          // [E', Nw, K] weights
     int64_t w_expert_bytes;
     const float* w_scale;      // PTPC: [E', Nw]; block: [E', Nw/128, K/128]
@@ -161,12 +162,13 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
     constexpr int N_BIG = A_IN + B_IN + (BLOCKQ ? 1 : 0);   // copies per wave per step
     constexpr int NB1 = N_BIG / 2, NB2 = N_BIG - NB1;       // issued in the two half-steps
     static_assert(TM >= 1 && A_IN >= 1 && B_IN >= 1 && BM % (8 * NW) == 0 && NROWS % (8 * NW) == 0 && BM <= 256 &&
-                      2 * STAGE <= kLdsBudget && (!BLOCKQ || NW == 4),
+                      2 * STAGE <= kLdsBudget && (!BLOCKQ || BM <= 64 * NW),
                   "tile shape");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE];
     __shared__ float s_rowscale[BM];          // PTPC: row scale; other modes: row mask (pad rows 0)
-    __shared__ __attribute__((aligned(16))) float s_ascale[BLOCKQ ? NS : 1][256];   // blockwise: row scales of a stage
+    // blockwise: row scales of a stage (wave w copies rows 64w .. 64w + 63)
+    __shared__ __attribute__((aligned(16))) float s_ascale[BLOCKQ ? NS : 1][BLOCKQ ? 64 * NW : 1];
     __shared__ int s_tok[BM];
     __shared__ float s_wscale[BLOCKQ ? WN * TN : 1][BLOCKQ ? 128 : 1];   // blockwise: weight scales of the tile
 
@@ -188,10 +190,14 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
     const int wm = wave / WN, wn = wave % WN;
     const int q = lane >> 5, r32 = lane & 31;
     const int arow = wm * TM * 32;            // first tile row of this wave
+    // rows of the block that hold routed rows (the expert's pads follow them)
+    const int live = p.counts ? min(BM, max(0, p.offsets[e] + p.counts[e] - m0)) : BM;
 
     if (tid < BM) {
-        int tok = m0 + tid;
-        float rs = 1.0f;
+        // rows past `live` are pads: down reads the block's first row for
+        // them (no HBM traffic for pad rows) and masks them out
+        int tok = tid < live ? m0 + tid : m0;
+        float rs = tid < live ? 1.0f : 0.0f;
         if (p.sorted_ids) {
             const int f = p.sorted_ids[m0 + tid];
             const bool pad = f == p.sentinel;
@@ -250,7 +256,7 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
             constexpr int j = d - A_IN;
             dma16(wexp + b_src[j] + ko, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
         } else {
-            dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 256 + wave * 64) * 4));
+            dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 64 * NW + wave * 64) * 4));
         }
     };
     auto issue = [&](int S) { static_for<N_BIG>([&](auto D) { issue_one(D, S, S % NS); }); };
@@ -275,221 +281,273 @@ __global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const G
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = v16f{};
-    v16f part[BLOCKQ ? TM : 1][BLOCKQ ? TN : 1];
-
     // Operand fragments, double-buffered in registers: set X holds the two
-    // 16-byte chunks of this lane's rows for one half-step; the blockwise
-    // mode also keeps a step's row scales (rows 8g + 4q .. + 3 of each tile).
+    // 16-byte chunks of this lane's rows for one half-step.
     u32x4 fa[2][TM][2], fb[2][TN][2];
-    float fs[BLOCKQ ? TM : 1];
 
-    // LDS read L (0 .. NL-1) of half-step H of the step in stage BUF into set
-    // X, in the order the MFMAs consume them: weight tile 0, the row tiles,
-    // then the other weight tiles (the MFMAs run weight tile by weight tile)
-    constexpr int NL = 2 * (TM + TN);
-    auto load_one = [&](auto X, auto Lc, int buf, int h) {
-        constexpr int l = decltype(Lc)::value, x = decltype(X)::value;
-        const uint8_t* L = lds + buf * STAGE;
-        if constexpr (l >= 2 && l < 2 + 2 * TM) {
-            constexpr int tm = (l - 2) / 2, c = (l - 2) % 2;
-            fa[x][tm][c] = lds16(L, lds_off(arow + tm * 32 + r32, 4 * h + 2 * q + c));
-        } else {
-            constexpr int lb = l < 2 ? l : l - 2 * TM;
-            constexpr int tn = lb / 2, c = lb % 2;
-            fb[x][tn][c] = lds16(L, lds_off(brow + tn * 32, 4 * h + 2 * q + c));
-        }
-    };
-    auto load_scales = [&](int buf) {
-        if constexpr (BLOCKQ) {
+    // Row tiles of this wave that hold at least one routed row: 32-row tiles
+    // made only of pads get no operand reads and no MFMAs (their
+    // accumulators stay 0).  The wave still issues its share of the copies.
+    const int ta = __builtin_amdgcn_readfirstlane(min(TM, max(0, (live - arow + 31) >> 5)));
+
+    // The main loop for TA live row tiles (TA is uniform over the tile's K
+    // sweep, so each variant is branch-free).
+    auto run = [&](auto TAc) __attribute__((always_inline)) {
+        constexpr int TA = decltype(TAc)::value;
+        // LDS reads per half-step (none without live rows) and MFMAs
+        constexpr int NL = TA > 0 ? 2 * (TA + TN) : 0;
+        constexpr int NM = (MODE == MOE_QUANT_NONE_BF16 ? 2 : 1) * TA * TN;
+
+        // LDS read L (0 .. NL-1) of half-step H of the step in stage BUF into
+        // set X, in the order the MFMAs consume them: weight tile 0, the row
+        // tiles, then the other weight tiles (the MFMAs run weight tile by
+        // weight tile)
+        auto load_one = [&](auto X, auto Lc, int buf, int h) {
+            constexpr int l = decltype(Lc)::value, x = decltype(X)::value;
+            const uint8_t* L = lds + buf * STAGE;
+            if constexpr (l >= 2 && l < 2 + 2 * TA) {
+                constexpr int tm = (l - 2) / 2, c = (l - 2) % 2;
+                fa[x][tm][c] = lds16(L, lds_off(arow + tm * 32 + r32, 4 * h + 2 * q + c));
+            } else {
+                constexpr int lb = l < 2 ? l : l - 2 * TA;
+                constexpr int tn = lb / 2, c = lb % 2;
+                fb[x][tn][c] = lds16(L, lds_off(brow + tn * 32, 4 * h + 2 * q + c));
+            }
+        };
+
+        // Blockwise scales.  A 128-byte step is one 128-element scale block;
+        // the MFMAs accumulate straight into acc, kept in units of the current
+        // block's scale a_scale(row, kb) * w_scale(n-block, kb): at the start
+        // of block kb each tile's acc is multiplied by
+        // (scale of block kb-1) / (scale of block kb), and after the last
+        // block by that block's scale.  The lane's activation row is fixed
+        // (row r32 of each row tile) and the weight scale is uniform over a
+        // 32-row weight tile, so each factor is one float per (tm, tn).
+        float pa[BLOCKQ ? TM : 1], pw[BLOCKQ ? TN : 1], ra[BLOCKQ ? TM : 1], rw[BLOCKQ ? TN : 1];
+        auto step_scales = [&](int buf, int kb) {
+            if constexpr (BLOCKQ) {
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) fs[tm] = s_ascale[buf][arow + tm * 32 + r32];
-        }
-    };
+                for (int tm = 0; tm < TA; ++tm) {
+                    const float a = s_ascale[buf][arow + tm * 32 + r32];
+                    ra[tm] = pa[tm] / a;
+                    pa[tm] = a;
+                }
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    const float w = s_wscale[wn * TN + tn][kb];
+                    rw[tn] = pw[tn] / w;
+                    pw[tn] = w;
+                }
+            }
+        };
 
-    // MFMA J (0 .. NM-1) of a half-step from fragment set X
-    constexpr int NM = (MODE == MOE_QUANT_NONE_BF16 ? 2 : 1) * TM * TN;
-    auto mma_one = [&](auto X, auto J) {
-        constexpr int j = decltype(J)::value, x = decltype(X)::value;
-        if constexpr (MODE == MOE_QUANT_NONE_BF16) {
-            constexpr int c = j / (TM * TN), tn = (j % (TM * TN)) / TM, tm = j % TM;
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fb[x][tn][c]),
-                                                                  __builtin_bit_cast(v8bf, fa[x][tm][c]), acc[tm][tn], 0,
-                                                                  0, 0);
-        } else {
-            constexpr int tn = j / TM, tm = j % TM;
-            const v8i av = cat8(fa[x][tm][0], fa[x][tm][1]), bv = cat8(fb[x][tn][0], fb[x][tn][1]);
-            // e4m3 x e4m3 (format selectors 0, 0), no block scaling
-            if constexpr (!BLOCKQ)
+        // MFMA J (0 .. NM-1) of a half-step from fragment set X; in the first
+        // half of a blockwise step the tile's acc is rescaled just before its
+        // first MFMA (its last MFMA of the previous step issued NM MFMAs ago)
+        auto mma_one = [&](auto X, auto J, auto H0) {
+            constexpr int j = decltype(J)::value, x = decltype(X)::value;
+            if constexpr (MODE == MOE_QUANT_NONE_BF16) {
+                constexpr int c = j / (TA * TN), tn = (j % (TA * TN)) / TA, tm = j % TA;
+                acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fb[x][tn][c]),
+                                                                      __builtin_bit_cast(v8bf, fa[x][tm][c]),
+                                                                      acc[tm][tn], 0, 0, 0);
+            } else {
+                constexpr int tn = j / TA, tm = j % TA;
+                if constexpr (BLOCKQ && decltype(H0)::value) {
+                    const float r = ra[tm] * rw[tn];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[tm][tn][i] *= r;
+                }
+                const v8i av = cat8(fa[x][tm][0], fa[x][tm][1]), bv = cat8(fb[x][tn][0], fb[x][tn][1]);
+                // e4m3 x e4m3 (format selectors 0, 0), no hardware block scaling
                 acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[tm][tn], 0, 0, 0, 0, 0, 0);
-            else
-                part[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, x == 0 ? v16f{} : part[tm][tn],
-                                                                               0, 0, 0, 0, 0, 0);
-        }
-    };
-    // blockwise: a step closes one 128-element scale block:
-    // acc += part * a_scale(row, kb) * w_scale(n-block, kb)
-    auto block_scale = [&](int kb) {
+            }
+        };
+
+        // One half-step: its MFMAs from set X, issued one at a time, each
+        // followed by its share of the NL reads of the next half-step (into
+        // the other set, from stage RBUF, half RH; when RD) and of the ND
+        // copies [D0, D0 + ND) of step CS (when CP), so that a memory
+        // instruction that stalls at issue overlaps a running MFMA.
+        auto half_step = [&](auto X, auto H0, auto D0c, auto NDc, bool rd, int rbuf, int rh, bool cp, int cs) {
+            constexpr int D0 = decltype(D0c)::value, ND = decltype(NDc)::value;
+            using XN = std::integral_constant<int, 1 - decltype(X)::value>;
+            if constexpr (NM == 0) {
+                if (cp) static_for<ND>([&](auto D) {
+                    issue_one(std::integral_constant<int, D0 + decltype(D)::value>{}, cs, cs % NS);
+                });
+            } else {
+                static_for<NM>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    mma_one(X, J, H0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (rd) {
+                        static_for<(j + 1) * NL / NM - j * NL / NM>([&](auto L) {
+                            load_one(XN{}, std::integral_constant<int, j * NL / NM + decltype(L)::value>{}, rbuf, rh);
+                        });
+                    }
+                    if (cp) {
+                        static_for<(j + 1) * ND / NM - j * ND / NM>([&](auto D) {
+                            issue_one(std::integral_constant<int, D0 + j * ND / NM + decltype(D)::value>{}, cs,
+                                      cs % NS);
+                        });
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
+        };
+
+        // Prologue: steps 0 .. NS-2 and the first NB1 copies of step NS-1 go
+        // out; wait for step 0, then read the fragments of its first half.
+        for (int S = 0; S < NS - 1; ++S)
+            if (S < nbig) issue(S);
+        const bool pro_more = NS - 1 < nbig;
+        if (pro_more) static_for<NB1>([&](auto D) { issue_one(D, NS - 1, (NS - 1) % NS); });
+        if (pro_more) vmcnt_wait<(NS - 2) * N_BIG + NB1>();
+        else vmcnt_wait<0>();
+        __syncthreads();
+        static_for<NL>([&](auto L) { load_one(std::integral_constant<int, 0>{}, L, 0, 0); });
         if constexpr (BLOCKQ) {
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const float wsc = s_wscale[wn * TN + tn][kb];
+            for (int tm = 0; tm < TA; ++tm) pa[tm] = s_ascale[0][arow + tm * 32 + r32];
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[tm][tn][i] += part[tm][tn][i] * (fs[tm] * wsc);
+            for (int tn = 0; tn < TN; ++tn) pw[tn] = s_wscale[wn * TN + tn][0];
+        }
+
+        // Step S (stage S % NS, landed and published):
+        //   first half: MFMAs from set 0; read the second half of S into set
+        //     1; issue the last NB2 copies of step S + NS - 1 (into the stage
+        //     of step S - 1, released by the previous barrier); wait until
+        //     step S + 1 has landed (copies issued after it may stay in
+        //     flight) and barrier: publishes S + 1 and releases stage S.
+        //   second half: MFMAs from set 1; read the first half of S + 1 into
+        //     set 0; issue the first NB1 copies of step S + NS (into stage S).
+        using X0 = std::integral_constant<int, 0>;
+        using X1 = std::integral_constant<int, 1>;
+        using First = std::integral_constant<bool, true>;
+        using Second = std::integral_constant<bool, false>;
+        for (int S = 0; S < nbig; ++S) {
+            const int buf = S % NS;
+            const bool next = S + 1 < nbig;
+            const bool cp2 = S + NS - 1 < nbig, cp1 = S + NS < nbig;
+            step_scales(buf, S);
+            half_step(X0{}, First{}, std::integral_constant<int, NB1>{}, std::integral_constant<int, NB2>{}, true,
+                      buf, 1, cp2, S + NS - 1);
+            if (next) {
+                if (cp2) vmcnt_wait<(NS - 2) * N_BIG>();
+                else vmcnt_wait<0>();
+                __syncthreads();
             }
+            // the reads of the next step's first half are issued even after
+            // the last step (they then read an idle stage into registers no
+            // MFMA uses): a branch around them would make the compiler wait
+            // for every outstanding LDS read before the MFMAs that follow
+            half_step(X1{}, Second{}, std::integral_constant<int, 0>{}, std::integral_constant<int, NB1>{}, true,
+                      (S + 1) % NS, 0, cp1, S + NS);
+        }
+        vmcnt_wait<0>();
+        if constexpr (BLOCKQ) {
+#pragma unroll
+            for (int tm = 0; tm < TA; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    const float r = pa[tm] * pw[tn];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[tm][tn][i] *= r;
+                }
         }
     };
-
-    // One half-step: its MFMAs from set X, issued one at a time, each
-    // followed by its share of the NL reads of the next half-step (into the
-    // other set, from stage RBUF, half RH; when RD) and of the ND copies
-    // [D0, D0 + ND) of step CS (when CP), so that a memory instruction that
-    // stalls at issue overlaps a running MFMA.
-    auto half_step = [&](auto X, auto D0c, auto NDc, bool rd, int rbuf, int rh, bool cp, int cs) {
-        constexpr int x = decltype(X)::value, D0 = decltype(D0c)::value, ND = decltype(NDc)::value;
-        using XN = std::integral_constant<int, 1 - x>;
-        static_for<NM>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            mma_one(X, J);
-            __builtin_amdgcn_sched_barrier(0);
-            if (rd) {
-                static_for<(j + 1) * NL / NM - j * NL / NM>([&](auto L) {
-                    load_one(XN{}, std::integral_constant<int, j * NL / NM + decltype(L)::value>{}, rbuf, rh);
-                });
-            }
-            if (cp) {
-                static_for<(j + 1) * ND / NM - j * ND / NM>([&](auto D) {
-                    issue_one(std::integral_constant<int, D0 + j * ND / NM + decltype(D)::value>{}, cs, cs % NS);
-                });
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-
-    // Prologue: steps 0 .. NS-2 and the first NB1 copies of step NS-1 go
-    // out; wait for step 0, then read the fragments of its first half.
-    for (int S = 0; S < NS - 1; ++S)
-        if (S < nbig) issue(S);
-    const bool pro_more = NS - 1 < nbig;
-    if (pro_more) static_for<NB1>([&](auto D) { issue_one(D, NS - 1, (NS - 1) % NS); });
-    if (pro_more) vmcnt_wait<(NS - 2) * N_BIG + NB1>();
-    else vmcnt_wait<0>();
-    __syncthreads();
-    static_for<NL>([&](auto L) { load_one(std::integral_constant<int, 0>{}, L, 0, 0); });
-
-    // Step S (stage S % NS, landed and published):
-    //   first half: MFMAs from set 0; read the second half of S into set 1;
-    //     issue the last NB2 copies of step S + NS - 1 (into the stage of
-    //     step S - 1, released by the previous barrier); wait until step
-    //     S + 1 has landed (copies issued after it may stay in flight) and
-    //     barrier: publishes S + 1 and releases stage S.
-    //   second half: MFMAs from set 1; read the first half of S + 1 into
-    //     set 0; issue the first NB1 copies of step S + NS (into stage S).
-    using X0 = std::integral_constant<int, 0>;
-    using X1 = std::integral_constant<int, 1>;
-    for (int S = 0; S < nbig; ++S) {
-        const int buf = S % NS;
-        const bool next = S + 1 < nbig;
-        const bool cp2 = S + NS - 1 < nbig, cp1 = S + NS < nbig;
-        half_step(X0{}, std::integral_constant<int, NB1>{}, std::integral_constant<int, NB2>{}, true, buf, 1, cp2,
-                  S + NS - 1);
-        if constexpr (BLOCKQ) load_scales(buf);
-        if (next) {
-            if (cp2) vmcnt_wait<(NS - 2) * N_BIG>();
-            else vmcnt_wait<0>();
-            __syncthreads();
-        }
-        // the reads of the next step's first half are issued even after the
-        // last step (they then read an idle stage into registers no MFMA
-        // uses): a branch around them would make the compiler wait for every
-        // outstanding LDS read before the MFMAs that follow
-        half_step(X1{}, std::integral_constant<int, 0>{}, std::integral_constant<int, NB1>{}, true, (S + 1) % NS, 0,
-                  cp1, S + NS);
-        block_scale(S);
-    }
-    vmcnt_wait<0>();
 
     // ------------------------------------------------------------ epilogue
-    // The MFMAs take the weight rows as their first operand, so lane
-    // (r32, q) holds row r32 of each 32-row tile and, in register
-    // i = 4g + j, output column 8g + 4q + j of each 32-column tile: four
-    // consecutive columns per g.  Per row tile, each wave packs them into
-    // 8 (bf16) or 16 (fp32) bytes, writes them row-major into its own LDS
-    // region (rows padded by 16 bytes), reads them back as 16-byte row
-    // pieces and stores whole 128-byte lines through a buffer resource
-    // based at the tile's first row.  The LDS regions reuse the stages: a
-    // barrier first lets every wave finish its last operand reads.
-    constexpr int OBYTES = (!GATEUP && MODE == MOE_QUANT_NONE_BF16) ? 4 : 2;
-    constexpr int CW = GATEUP ? HALF : WCOLS;            // output columns per wave
-    constexpr int RB = CW * OBYTES;                       // bytes of one output row of the wave
-    constexpr int RBP = RB + 16;                          // padded LDS row stride
-    constexpr int LPR = RB / 16;                          // lanes per row on the way out
-    constexpr int RPI = 64 / LPR;                         // rows per store instruction
-    static_assert(64 % LPR == 0 && 32 % RPI == 0 && NW * 32 * RBP <= NS * STAGE, "epilogue layout");
-    __syncthreads();
-    uint8_t* reg = lds + wave * 32 * RBP;
-    const int ldb = static_cast<int>(p.out_ld) * OBYTES;          // bytes per output row
-    const __amdgpu_buffer_rsrc_t rsrc =
-        tile_rsrc(static_cast<uint8_t*>(p.out) + static_cast<int64_t>(m0) * p.out_ld * OBYTES);
-    const float* wsx = (MODE == MOE_QUANT_PTPC_FP8) ? p.w_scale + e * p.ws_expert : nullptr;
-    // first output column of this wave
-    const int col0 = GATEUP ? n0 + wn * HALF : n0 + wn * WCOLS;
-    // channel scales of this lane's columns: [tile][g] -> 4 consecutive columns
-    float4 swa[GATEUP ? TN / 2 : TN][4], swb[GATEUP ? TN / 2 : 1][4];
-#pragma unroll
-    for (int t = 0; t < (GATEUP ? TN / 2 : TN); ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int c = col0 + t * 32 + 8 * g + 4 * q;
-            if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
-                swa[t][g] = *reinterpret_cast<const float4*>(wsx + c);
-                if constexpr (GATEUP) swb[t][g] = *reinterpret_cast<const float4*>(wsx + p.I + c);
-            } else {
-                swa[t][g] = float4{1.0f, 1.0f, 1.0f, 1.0f};
-                if constexpr (GATEUP) swb[t][g] = float4{1.0f, 1.0f, 1.0f, 1.0f};
-            }
-        }
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        const float rs = s_rowscale[arow + tm * 32 + r32];
-        // pack this row tile into the wave's region
-#pragma unroll
+    // (called at the end of each main-loop variant, so that no variant's
+    // accumulators meet another's at a join point)
+    auto epilogue = [&]() __attribute__((always_inline)) {
+        // The MFMAs take the weight rows as their first operand, so lane
+        // (r32, q) holds row r32 of each 32-row tile and, in register
+        // i = 4g + j, output column 8g + 4q + j of each 32-column tile: four
+        // consecutive columns per g.  Per row tile, each wave packs them into
+        // 8 (bf16) or 16 (fp32) bytes, writes them row-major into its own LDS
+        // region (rows padded by 16 bytes), reads them back as 16-byte row
+        // pieces and stores whole 128-byte lines through a buffer resource
+        // based at the tile's first row.  The LDS regions reuse the stages: a
+        // barrier first lets every wave finish its last operand reads.
+        constexpr int OBYTES = (!GATEUP && MODE == MOE_QUANT_NONE_BF16) ? 4 : 2;
+        constexpr int CW = GATEUP ? HALF : WCOLS;            // output columns per wave
+        constexpr int RB = CW * OBYTES;                       // bytes of one output row of the wave
+        constexpr int RBP = RB + 16;                          // padded LDS row stride
+        constexpr int LPR = RB / 16;                          // lanes per row on the way out
+        constexpr int RPI = 64 / LPR;                         // rows per store instruction
+        static_assert(64 % LPR == 0 && 32 % RPI == 0 && NW * 32 * RBP <= NS * STAGE, "epilogue layout");
+        __syncthreads();
+        uint8_t* reg = lds + wave * 32 * RBP;
+        const int ldb = static_cast<int>(p.out_ld) * OBYTES;          // bytes per output row
+        const __amdgpu_buffer_rsrc_t rsrc =
+            tile_rsrc(static_cast<uint8_t*>(p.out) + static_cast<int64_t>(m0) * p.out_ld * OBYTES);
+        const float* wsx = (MODE == MOE_QUANT_PTPC_FP8) ? p.w_scale + e * p.ws_expert : nullptr;
+        // first output column of this wave
+        const int col0 = GATEUP ? n0 + wn * HALF : n0 + wn * WCOLS;
+        // channel scales of this lane's columns: [tile][g] -> 4 consecutive columns
+        float4 swa[GATEUP ? TN / 2 : TN][4], swb[GATEUP ? TN / 2 : 1][4];
+    #pragma unroll
         for (int t = 0; t < (GATEUP ? TN / 2 : TN); ++t)
-#pragma unroll
+    #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                float v[4];
-                const float4 sa = swa[t][g];
-                const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if constexpr (GATEUP) {
-                        const float4 sb = swb[t][g];
-                        const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
-                        v[j] = silu_mul(acc[tm][t][4 * g + j] * rs * sav[j], acc[tm][t + TN / 2][4 * g + j] * rs * sbv[j]);
+                const int c = col0 + t * 32 + 8 * g + 4 * q;
+                if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
+                    swa[t][g] = *reinterpret_cast<const float4*>(wsx + c);
+                    if constexpr (GATEUP) swb[t][g] = *reinterpret_cast<const float4*>(wsx + p.I + c);
+                } else {
+                    swa[t][g] = float4{1.0f, 1.0f, 1.0f, 1.0f};
+                    if constexpr (GATEUP) swb[t][g] = float4{1.0f, 1.0f, 1.0f, 1.0f};
+                }
+            }
+    #pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const float rs = s_rowscale[arow + tm * 32 + r32];
+            // pack this row tile into the wave's region
+    #pragma unroll
+            for (int t = 0; t < (GATEUP ? TN / 2 : TN); ++t)
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+                    const float4 sa = swa[t][g];
+                    const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (GATEUP) {
+                            const float4 sb = swb[t][g];
+                            const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
+                            v[j] = silu_mul(acc[tm][t][4 * g + j] * rs * sav[j], acc[tm][t + TN / 2][4 * g + j] * rs * sbv[j]);
+                        } else {
+                            v[j] = acc[tm][t][4 * g + j] * rs * sav[j];
+                        }
+                    }
+                    uint8_t* dst = reg + r32 * RBP + (t * 32 + 8 * g + 4 * q) * OBYTES;
+                    if constexpr (OBYTES == 2) {
+                        const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+                        const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+                        *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
                     } else {
-                        v[j] = acc[tm][t][4 * g + j] * rs * sav[j];
+                        *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
                     }
                 }
-                uint8_t* dst = reg + r32 * RBP + (t * 32 + 8 * g + 4 * q) * OBYTES;
-                if constexpr (OBYTES == 2) {
-                    const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-                    const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-                    *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
-                } else {
-                    *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
-                }
+            // read back 16-byte row pieces and store whole lines (the wave's
+            // LDS operations complete in order, so the next row tile's writes
+            // cannot overtake these reads)
+    #pragma unroll
+            for (int it = 0; it < 32 / RPI; ++it) {
+                const int row = it * RPI + lane / LPR, ch = lane % LPR;
+                const u32x4 d = *reinterpret_cast<const u32x4*>(reg + row * RBP + ch * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(d, rsrc, (arow + tm * 32 + row) * ldb + col0 * OBYTES + ch * 16, 0, 0);
             }
-        // read back 16-byte row pieces and store whole lines (the wave's
-        // LDS operations complete in order, so the next row tile's writes
-        // cannot overtake these reads)
-#pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
-            const int row = it * RPI + lane / LPR, ch = lane % LPR;
-            const u32x4 d = *reinterpret_cast<const u32x4*>(reg + row * RBP + ch * 16);
-            __builtin_amdgcn_raw_buffer_store_b128(d, rsrc, (arow + tm * 32 + row) * ldb + col0 * OBYTES + ch * 16, 0, 0);
         }
-    }
+    };
+    static_for<TM + 1>([&](auto TAc) {
+        if (ta == decltype(TAc)::value) {
+            run(TAc);
+            epilogue();
+        }
+    });
 }
 
 template <int MODE, bool GATEUP, int TN>
@@ -499,9 +557,7 @@ static int32_t launch_bm(int block_m, const GemmArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 32, TN>), grid, dim3(nw_of(32) * 64), 0, s, a);
         return moe_launch_status();
     }
-    // the blockwise mode keeps its partial sums and scales in registers: row
-    // blocks above 32 would spill
-    if constexpr (MODE != MOE_QUANT_BLOCK128_FP8) {
+    {
         if (block_m == 64) {
             hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 64, TN>), grid, dim3(nw_of(64) * 64), 0, s, a);
             return moe_launch_status();
@@ -535,17 +591,19 @@ static int32_t launch_mode(int quant, int tn, int block_m, const GemmArgs& a, hi
 }
 
 int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
-                             const int* sorted_ids, const int* offsets, void* act, hipStream_t s);
+                             const int* sorted_ids, const int* offsets, const int* counts, void* act,
+                             hipStream_t s);
 int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T,
-                           const int* offsets, void* out_perm, hipStream_t s);
+                           const int* offsets, const int* counts, void* out_perm, hipStream_t s);
 
 int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T, int block_m,
                            int64_t max_rows, const int* sorted_ids, const int* block_expert, const int* offsets,
-                           void* act, hipStream_t s) {
-    if (block_m == 16) return stream_gateup_launch(L, a, a_scale, T, sorted_ids, offsets, act, s);
+                           const int* counts, void* act, hipStream_t s) {
+    if (block_m == 16) return stream_gateup_launch(L, a, a_scale, T, sorted_ids, offsets, counts, act, s);
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     GemmArgs g{};
     g.offsets = offsets;
+    g.counts = counts;
     g.a = static_cast<const uint8_t*>(a);
     g.a_ld = static_cast<int64_t>(L->D) * elem;
     g.a_scale = a_scale;
@@ -573,12 +631,13 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
 }
 
 int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T, int block_m,
-                         int64_t max_rows, const int* block_expert, const int* offsets, void* out_perm,
-                         hipStream_t s) {
-    if (block_m == 16) return stream_down_launch(L, act, act_scale, T, offsets, out_perm, s);
+                         int64_t max_rows, const int* block_expert, const int* offsets, const int* counts,
+                         void* out_perm, hipStream_t s) {
+    if (block_m == 16) return stream_down_launch(L, act, act_scale, T, offsets, counts, out_perm, s);
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     GemmArgs g{};
     g.offsets = offsets;
+    g.counts = counts;
     g.a = static_cast<const uint8_t*>(act);
     g.a_ld = static_cast<int64_t>(L->I) * elem;
     g.a_scale = act_scale;

@@ -6,9 +6,9 @@
 // low concurrency; the MI355X MoRI page notes that small-batch TP decode
 // gives tall-skinny expert GEMMs).  Design:
 //   - the work is (active expert x slice of weight rows) items, one wave per
-//     item; the expert's rows (at most 16*MT, every expert holds at most T
-//     rows) are all handled by the wave that streams the slice, so each
-//     weight byte is read once;
+//     item; the wave that streams the slice handles the expert's rows, up
+//     to 16*MT at a time, so each weight byte is read once per 16*MT rows
+//     (once in total for the small batches this path is chosen for);
 //   - the grid is persistent (the workgroups that fit at once); each
 //     workgroup lists the active experts (offsets[e+1] > offsets[e]) in LDS
 //     and its waves walk the items so that every CU gets the same number of
@@ -37,6 +37,7 @@ struct StreamArgs {
     const int* sorted_ids;     // gate_up: flat ids; down: NULL (rows direct)
     int topk, TK, sentinel;
     const int* offsets;        // [E'+1] padded (multiples of 16)
+    const int* counts;         // [E'] routed rows per expert (NULL: every row of a segment is live)
     const uint8_t* w;
     int64_t w_expert_bytes;
     const float* w_scale;
@@ -93,13 +94,15 @@ __device__ __forceinline__ int src_row(const StreamArgs& p, bool gateup, int row
 // MT: 16-row activation tiles (rows per expert <= 16*MT).  PF: K steps in
 // flight.  The steady-state loop has no data-dependent branch, so the
 // compiler can wait for exactly the step it is about to use.
-// One item: expert E, weight slice SL (COLS_W output columns), on this wave.
+// One item: expert E, weight slice SL (COLS_W output columns), rows
+// [R0, R0 + 16*MT) of the expert's segment, on this wave.
 template <int MODE, bool GATEUP, int TN, int MT, int PF>
-__device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, int lane) {
+__device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, int lane, int r0) {
     constexpr bool BLOCKQ = MODE == MOE_QUANT_BLOCK128_FP8;
     constexpr int COLS_W = GATEUP ? TN / 2 * 16 : TN * 16;     // output columns per wave
-    const int row0 = p.offsets[e];
-    const int cnt = p.offsets[e + 1] - row0;                    // padded rows of this expert
+    const int row0 = p.offsets[e] + r0;
+    const int cnt = min(p.offsets[e + 1] - row0, 16 * MT);     // padded rows of this chunk
+    const int live = p.counts ? p.offsets[e] + p.counts[e] - row0 : cnt;   // rows before the pads
     const int c0 = sl * COLS_W;                                 // first output column of this wave
     const int r16 = lane & 15, kq = (lane >> 4) * 16;
 
@@ -133,7 +136,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
             bool v = false;
             const int src = r < cnt ? src_row(p, GATEUP, row0 + r, v) : 0;
             esrc[m][i] = v ? src : (GATEUP ? 0 : row0);
-            emask[m][i] = v ? 1.0f : 0.0f;
+            emask[m][i] = v && r < live ? 1.0f : 0.0f;
         }
 
     v4f acc[MT][TN];
@@ -283,13 +286,18 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
     const int n_items = base * p.nslice;
     const int G = gridDim.x;
     for (int i = blockIdx.x + G * wave; i < n_items; i += 4 * G) {
-        const int j = i / p.nslice, e = s_act[j];
-        // experts with at most 16 rows take the one-tile path (half the
-        // activation loads and registers); each path is branch-free inside
-        if (MT > 1 && p.offsets[e + 1] - p.offsets[e] <= 16)
-            stream_item<MODE, GATEUP, TN, 1, PF>(p, e, i - j * p.nslice, lane);
-        else
-            stream_item<MODE, GATEUP, TN, MT, PF>(p, e, i - j * p.nslice, lane);
+        const int j = i / p.nslice, e = s_act[j], sl = i - j * p.nslice;
+        const int rows = p.offsets[e + 1] - p.offsets[e];
+        // experts with at most 16 (32) rows take the one-tile (two-tile) path:
+        // fewer activation loads, registers and MFMAs; more rows than 16*MT
+        // are handled in chunks.  Each path is branch-free inside.
+        if (MT > 1 && rows <= 16) {
+            stream_item<MODE, GATEUP, TN, 1, PF>(p, e, sl, lane, 0);
+        } else if (MT > 2 && rows <= 32) {
+            stream_item<MODE, GATEUP, TN, 2, PF>(p, e, sl, lane, 0);
+        } else {
+            for (int r0 = 0; r0 < rows; r0 += 16 * MT) stream_item<MODE, GATEUP, TN, MT, PF>(p, e, sl, lane, r0);
+        }
     }
 }
 
@@ -350,7 +358,8 @@ static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, 
 
 
 int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
-                             const int* sorted_ids, const int* offsets, void* act, hipStream_t s) {
+                             const int* sorted_ids, const int* offsets, const int* counts, void* act,
+                             hipStream_t s) {
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     StreamArgs g{};
     g.a = static_cast<const uint8_t*>(a);
@@ -362,6 +371,7 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
     g.TK = T * L->top_k;
     g.sentinel = T * (L->top_k + L->n_shared);
     g.offsets = offsets;
+    g.counts = counts;
     g.w = static_cast<const uint8_t*>(L->w13);
     g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
     g.w_scale = L->w13_scale;
@@ -376,7 +386,7 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
 }
 
 int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T,
-                           const int* offsets, void* out_perm, hipStream_t s) {
+                           const int* offsets, const int* counts, void* out_perm, hipStream_t s) {
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     StreamArgs g{};
     g.a = static_cast<const uint8_t*>(act);
@@ -385,6 +395,7 @@ int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float
     g.a_scale_ld = L->I / 128;
     g.sorted_ids = nullptr;
     g.offsets = offsets;
+    g.counts = counts;
     g.w = static_cast<const uint8_t*>(L->w2);
     g.w_expert_bytes = static_cast<int64_t>(L->D) * L->I * elem;
     g.w_scale = L->w2_scale;

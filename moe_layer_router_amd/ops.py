@@ -189,18 +189,19 @@ class MoELayer:
         return self._ws
 
     # ---- the step entries that need the layer
-    def gateup_silu(self, a, a_scale, T: int, block_m: int, perm: dict) -> torch.Tensor:
+    def gateup_silu(self, a, a_scale, T: int, block_m: int, perm: dict, use_counts: bool = True) -> torch.Tensor:
         act = _empty((perm["max_rows"], self.I), _BF16, a)
         L.check("moe_grouped_gemm_gateup_silu", L.lib().moe_grouped_gemm_gateup_silu(
             ctypes.byref(self.desc), _ptr(a), _ptr(a_scale), T, block_m, _ptr(perm["sorted_ids"]),
-            _ptr(perm["block_expert"]), _ptr(perm["offsets"]), _ptr(act), _stream()))
+            _ptr(perm["block_expert"]), _ptr(perm["offsets"]), _ptr(perm["counts"]) if use_counts else None,
+            _ptr(act), _stream()))
         return act
 
-    def down(self, act, act_scale, T: int, block_m: int, perm: dict) -> torch.Tensor:
+    def down(self, act, act_scale, T: int, block_m: int, perm: dict, use_counts: bool = True) -> torch.Tensor:
         out = _empty((perm["max_rows"], self.D), _F32 if self.quant == "bf16" else _BF16, act)
         L.check("moe_grouped_gemm_down", L.lib().moe_grouped_gemm_down(
             ctypes.byref(self.desc), _ptr(act), _ptr(act_scale), T, block_m, _ptr(perm["block_expert"]),
-            _ptr(perm["offsets"]), _ptr(out), _stream()))
+            _ptr(perm["offsets"]), _ptr(perm["counts"]) if use_counts else None, _ptr(out), _stream()))
         return out
 
     def forward(self, x: torch.Tensor, logits: Optional[torch.Tensor] = None, block_m: int = 0,

@@ -85,9 +85,15 @@ def test_layer_validation_and_workspace():
     # unsupported shapes / block sizes
     assert lib.moe_forward_workspace_size(ctypes.byref(_desc(I=200)), 100, 64) == 0
     assert lib.moe_forward_workspace_size(ctypes.byref(d), 100, 48) == 0
-    assert lib.moe_forward_workspace_size(ctypes.byref(_desc(quant=2)), 100, 64) == 0
-    assert lib.moe_forward_workspace_size(ctypes.byref(d), 100, 16) == 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(_desc(quant=2)), 100, 128) > 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(_desc(quant=2)), 100, 256) > 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(d), 100, 16) > 0
     assert lib.moe_forward_workspace_size(ctypes.byref(d), 64, 16) > 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(d), 100, 8) == 0
+    # the automatic block size streams weights while the mean rows per expert stay small
+    assert lib.moe_default_block_m(ctypes.byref(d), 64) == 16
+    assert lib.moe_default_block_m(ctypes.byref(_desc(E=128, top_k=8)), 256) == 32
+    assert lib.moe_default_block_m(ctypes.byref(_desc(E=128, top_k=8)), 8192) == 256
     assert lib.moe_forward(ctypes.byref(_desc(I=200)), None, None, 4, 0, None, None, 0, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_forward(ctypes.byref(_desc(w13=None)), None, None, 4, 0, None, None, 0, None) \
         == L.MOE_ERR_INVALID_ARG

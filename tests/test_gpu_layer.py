@@ -46,9 +46,12 @@ def _check_exact(inter, ref, quant):
                                           ("qwen3_235b_prefill_ptpc_r", 256), ("bf16_multi_tile_r", 256),
                                           ("qwen3_30b_a3b_ptpc_i384", 0),
                                           ("qwen3_235b_decode_ptpc", 0), ("deepseek_r1_block_fp8_r", 0),
-                                          ("deepseek_r1_block_fp8_r", 32), ("deepseek_r1_block_fp8_small", 0),
+                                          ("deepseek_r1_block_fp8_r", 32), ("deepseek_r1_block_fp8_r", 64),
+                                          ("deepseek_r1_block_fp8_r", 128), ("deepseek_r1_block_fp8_r", 256),
+                                          ("deepseek_r1_block_fp8_small", 0),
                                           ("qwen3_235b_decode_ptpc_t64", 0), ("qwen3_235b_decode_ptpc", 32),
-                                          ("bf16_small_t20", 0)])
+                                          ("bf16_small_t20", 0), ("qwen3_235b_prefill_ptpc_r", 16),
+                                          ("deepseek_r1_block_fp8_r", 16)])
 def test_forward_matches_oracle(name, block_m):
     w = REDUCED[name]
     say("forward", name, block_m)

@@ -212,8 +212,11 @@ def test_quant_weights(quant):
                                           ("qwen3_235b_prefill_ptpc_r", 128), ("qwen3_235b_prefill_ptpc_r", 64),
                                           ("qwen3_235b_prefill_ptpc_r", 256), ("bf16_multi_tile_r", 256),
                                           ("qwen3_30b_a3b_ptpc_i384", 64), ("qwen3_30b_a3b_ptpc_i384", 256),
-                                          ("deepseek_r1_block_fp8_r", 32),
+                                          ("deepseek_r1_block_fp8_r", 32), ("deepseek_r1_block_fp8_r", 64),
+                                          ("deepseek_r1_block_fp8_r", 128), ("deepseek_r1_block_fp8_r", 256),
                                           ("tiny_bf16", 16), ("bf16_small_t20", 16), ("qwen3_235b_decode_ptpc", 16),
+                                          ("qwen3_30b_a3b_ptpc", 16), ("qwen3_235b_prefill_ptpc_r", 16),
+                                          ("deepseek_r1_block_fp8_r", 16), ("bf16_multi_tile_r", 16),
                                           ("qwen3_235b_decode_ptpc_t64", 16), ("deepseek_r1_block_fp8_small", 16)])
 def test_gateup_silu_entry(name, block_m):
     """act rows of the gate/up GEMM vs the oracle's, from the same x, routing
@@ -251,8 +254,11 @@ def test_gateup_silu_entry(name, block_m):
                                           ("qwen3_235b_prefill_ptpc_r", 256), ("bf16_multi_tile_r", 256),
                                           ("qwen3_30b_a3b_ptpc_i384", 128), ("qwen3_30b_a3b_ptpc_i384", 256),
                                           ("qwen3_30b_a3b_ptpc", 64), ("deepseek_r1_block_fp8_r", 32),
+                                          ("deepseek_r1_block_fp8_r", 64), ("deepseek_r1_block_fp8_r", 128),
+                                          ("deepseek_r1_block_fp8_r", 256),
                                           ("tiny_bf16", 16), ("qwen3_235b_decode_ptpc", 16),
-                                          ("qwen3_235b_decode_ptpc_t64", 16), ("deepseek_r1_block_fp8_small", 16)])
+                                          ("qwen3_235b_decode_ptpc_t64", 16), ("deepseek_r1_block_fp8_small", 16),
+                                          ("qwen3_30b_a3b_ptpc", 16), ("qwen3_235b_prefill_ptpc_r", 16)])
 def test_down_entry(name, block_m):
     """out_perm of the down GEMM on a synthetic act buffer (same values on both
     sides), quantized per row / 1x128 by each side."""
@@ -273,10 +279,13 @@ def test_down_entry(name, block_m):
     torch.cuda.synchronize()
     act_np = synth.bf16_to_f32_np(act)
     offs = perm["offsets"].cpu().numpy()
+    cnts = perm["counts"].cpu().numpy()
     got = out.float().cpu().numpy()
     errs = []
     for e in range(w.E + w.n_shared):
-        lo, hi = int(offs[e]), int(offs[e + 1])
+        lo, hi = int(offs[e]), int(offs[e]) + int(cnts[e])
+        # pad rows of the segment come out 0 (their act here is not)
+        assert np.all(got[hi:int(offs[e + 1])] == 0)
         if hi == lo:
             continue
         _, w2 = c.bank.dequantized(e)
@@ -290,6 +299,41 @@ def test_down_entry(name, block_m):
     g = np.concatenate([a for a, _ in errs])
     r = np.concatenate([b for _, b in errs])
     assert rel_l2(g, r) < (1e-5 if w.quant == "bf16" else 2e-3)
+
+
+@pytest.mark.parametrize("name,block_m", [("qwen3_235b_prefill_ptpc_r", 256), ("qwen3_235b_prefill_ptpc_r", 128),
+                                          ("deepseek_r1_block_fp8_r", 256), ("bf16_multi_tile_r", 256),
+                                          ("qwen3_30b_a3b_ptpc", 64), ("qwen3_30b_a3b_ptpc", 16),
+                                          ("qwen3_235b_prefill_ptpc_r", 16)])
+def test_gemm_counts_skip_pad_tiles(name, block_m):
+    """With expert_counts the LDS-tiled GEMMs skip the 32-row tiles that hold
+    only pads; every row up to the padded total must come out bitwise equal
+    to the run without counts (pad rows 0 in both)."""
+    w = REDUCED[name]
+    say("counts", name, block_m)
+    c = build_case(w)
+    logits = mlr.router_logits(c.x, c.router_w) if w.router == "gemm" else c.logits
+    ids, _ = (mlr.route_topk(logits, w.k) if w.scoring == "softmax" else
+              mlr.route_topk(logits, w.k, w.scoring, w.n_groups, w.topk_groups, None, True, w.route_scale))
+    perm = mlr.permute_align(ids, w.E, w.n_shared, block_m)
+    group = 128 if w.quant == "block128_fp8" else 0
+    a, sa = (c.x, None) if w.quant == "bf16" else mlr.quant_ptpc_fp8(c.x, group)
+    act1 = c.layer.gateup_silu(a, sa, w.T, block_m, perm, use_counts=True)
+    act0 = c.layer.gateup_silu(a, sa, w.T, block_m, perm, use_counts=False)
+    torch.cuda.synchronize()
+    total = int(perm["offsets"][-1].item())
+    counts = perm["counts"].cpu().numpy()
+    assert np.sum((-(-counts // block_m)) * block_m - counts) > 0, "the case must have pad rows"
+    real = perm["sorted_ids"][:total] != w.T * (w.k + w.n_shared)
+    # routed rows bitwise; pad rows are zeros (of either sign) both ways
+    assert torch.equal(act1[:total][real].view(torch.int16), act0[:total][real].view(torch.int16))
+    assert bool((act1[:total][~real] == 0).all()) and bool((act0[:total][~real] == 0).all())
+    b, sb = (act1, None) if w.quant == "bf16" else mlr.quant_ptpc_fp8(act1, group)
+    o1 = c.layer.down(b, sb, w.T, block_m, perm, use_counts=True)
+    o0 = c.layer.down(b, sb, w.T, block_m, perm, use_counts=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:total][real], o0[:total][real])
+    assert bool((o1[:total][~real] == 0).all()) and bool((o0[:total][~real] == 0).all())
 
 
 @pytest.mark.parametrize("T,k,ns,D,dt", [(64, 2, 0, 256, 0), (300, 8, 1, 1024, 1), (17, 8, 0, 7168, 1)])
