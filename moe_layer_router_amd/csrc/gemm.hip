@@ -60,8 +60,12 @@ constexpr int kLdsBudget = 150 * 1024;
 // LDS reads in flight to feed its MFMAs from the 128 x 256 tile below 256
 // rows; the 256-row tile runs 8 waves (2 per SIMD, 2 x 4, each 128 x 64),
 // which doubles the LDS read rate the CU sustains.  Row tiles of 128 use a
-// 2 x 2 grid of 4 waves, smaller ones 1 x 4.
-constexpr int nw_of(int bm) { return bm == 256 ? 8 : 4; }
+// 2 x 2 grid of 4 waves, smaller ones 1 x 4.  In the blockwise mode (a
+// layer whose experts each see ~150 rows, so its weight tiles are used by
+// one row block and stream from HBM) the 128-row tile also runs 8 waves
+// (2 x 4, each 64 x 64): a 128 x 256 tile whose 48 KB stages fit 3 deep in
+// LDS, so the weight copies get two steps to land instead of one.
+constexpr int nw_of(int mode, int bm) { return bm == 256 || (bm == 128 && mode == MOE_QUANT_BLOCK128_FP8) ? 8 : 4; }
 constexpr int wm_of(int bm) { return bm >= 128 ? 2 : 1; }
 
 // 32-row weight tiles per wave: 4 for PTPC where the weight rows divide into
@@ -69,7 +73,7 @@ constexpr int wm_of(int bm) { return bm >= 128 ? 2 : 1; }
 // bf16 and blockwise modes keep more live registers per tile, and the
 // 8-wave tile holds 128 x 64 per wave)
 static int tn_of(int mode, int weight_rows, int bm) {
-    if (bm == 256) return 2;
+    if (nw_of(mode, bm) == 8) return 2;
     return mode == MOE_QUANT_PTPC_FP8 && weight_rows % ((4 / wm_of(bm)) * 128) == 0 ? 4 : 2;
 }
 
@@ -142,9 +146,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(void* base) {
 }
 
 template <int MODE, bool GATEUP, int BM, int TN>
-__global__ void __launch_bounds__(nw_of(BM) * 64, 1) grouped_gemm_kernel(const GemmArgs p) {
+__global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(const GemmArgs p) {
     constexpr int ELEM = MODE == MOE_QUANT_NONE_BF16 ? 2 : 1;
-    constexpr int NW = nw_of(BM), NT = NW * 64;
+    constexpr int NW = nw_of(MODE, BM), NT = NW * 64;
     constexpr int WM = wm_of(BM), WN = NW / WM;
     constexpr int TM = BM / (32 * WM);
     constexpr int WCOLS = TN * 32;              // weight rows per wave
@@ -554,22 +558,24 @@ template <int MODE, bool GATEUP, int TN>
 static int32_t launch_bm(int block_m, const GemmArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(ceil_div(a.n_tiles, 8) * 8));
     if (block_m == 32) {
-        hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 32, TN>), grid, dim3(nw_of(32) * 64), 0, s, a);
+        hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 32, TN>), grid, dim3(nw_of(MODE, 32) * 64), 0, s, a);
         return moe_launch_status();
     }
     {
         if (block_m == 64) {
-            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 64, TN>), grid, dim3(nw_of(64) * 64), 0, s, a);
+            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 64, TN>), grid, dim3(nw_of(MODE, 64) * 64), 0, s,
+                               a);
             return moe_launch_status();
         }
-        if (block_m == 128) {
-            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 128, TN>), grid, dim3(nw_of(128) * 64), 0, s, a);
+        if (block_m == 128 && (TN == 2 || nw_of(MODE, 128) == 4)) {
+            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 128, TN>), grid, dim3(nw_of(MODE, 128) * 64), 0, s,
+                               a);
             return moe_launch_status();
         }
         if constexpr (TN == 2) {   // tn_of gives the 256-row tile 2 weight tiles per wave
             if (block_m == 256) {
-                hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 256, TN>), grid, dim3(nw_of(256) * 64), 0, s,
-                                   a);
+                hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 256, TN>), grid, dim3(nw_of(MODE, 256) * 64), 0,
+                                   s, a);
                 return moe_launch_status();
             }
         }
@@ -624,7 +630,7 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
     g.out = act;
     g.out_ld = L->I;
     const int tn = tn_of(L->quant, 2 * L->I, block_m);
-    g.n_ntiles = L->I / ((nw_of(block_m) / wm_of(block_m)) * tn * 16);
+    g.n_ntiles = L->I / ((nw_of(L->quant, block_m) / wm_of(block_m)) * tn * 16);
     g.n_tiles = static_cast<int>(max_rows / block_m) * g.n_ntiles;
     g.n_exp = L->E + L->n_shared;
     return launch_mode<true>(L->quant, tn, block_m, g, s);
@@ -655,7 +661,7 @@ int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* 
     g.out = out_perm;
     g.out_ld = L->D;
     const int tn = tn_of(L->quant, L->D, block_m);
-    g.n_ntiles = L->D / ((nw_of(block_m) / wm_of(block_m)) * tn * 32);
+    g.n_ntiles = L->D / ((nw_of(L->quant, block_m) / wm_of(block_m)) * tn * 32);
     g.n_tiles = static_cast<int>(max_rows / block_m) * g.n_ntiles;
     g.n_exp = L->E + L->n_shared;
     return launch_mode<false>(L->quant, tn, block_m, g, s);
