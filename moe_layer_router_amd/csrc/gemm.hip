@@ -62,9 +62,9 @@ constexpr int kLdsBudget = 150 * 1024;
 // which doubles the LDS read rate the CU sustains.  Row tiles of 128 use a
 // 2 x 2 grid of 4 waves, smaller ones 1 x 4.  In the blockwise mode (a
 // layer whose experts each see ~150 rows, so its weight tiles are used by
-// one row block and stream from HBM) the 128-row tile also runs 8 waves
-// (2 x 4, each 64 x 64): a 128 x 256 tile whose 48 KB stages fit 3 deep in
-// LDS, so the weight copies get two steps to land instead of one.
+// one or two row blocks and stream from HBM) the 128-row tile also runs 8
+// waves (2 x 4, each 64 x 64): a 128 x 256 tile whose 48 KB stages fit 3
+// deep in LDS, so the weight copies get two steps to land instead of one.
 constexpr int nw_of(int mode, int bm) { return bm == 256 || (bm == 128 && mode == MOE_QUANT_BLOCK128_FP8) ? 8 : 4; }
 constexpr int wm_of(int bm) { return bm >= 128 ? 2 : 1; }
 
