@@ -115,9 +115,11 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // be wave-uniform.  Issued as inline asm so that the only waits on them are
 // the explicit vmcnt_wait below (the compiler would otherwise drain every
 // outstanding copy before each LDS read).  The main loop issues no other
-// vector-memory instruction, so vmcnt counts exactly these copies.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+// vector-memory instruction, so vmcnt counts exactly these copies.  The
+// 16-byte copies take a wave-uniform 64-bit base (scalar registers) plus a
+// 32-bit per-lane offset, which keeps one VGPR per copy stream.
+__device__ __forceinline__ void dma16(uint32_t off, const void* base, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_addr) {
@@ -174,6 +176,8 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     // blockwise: row scales of a stage (wave w copies rows 64w .. 64w + 63)
     __shared__ __attribute__((aligned(16))) float s_ascale[BLOCKQ ? NS : 1][BLOCKQ ? 64 * NW : 1];
     __shared__ int s_tok[BM];
+    // PTPC: channel scales of the tile's output columns (gate_up: gate, then up)
+    __shared__ __attribute__((aligned(16))) float s_chs[MODE == MOE_QUANT_PTPC_FP8 ? (GATEUP ? 2 : 1) * TILE_N : 1];
     __shared__ float s_wscale[BLOCKQ ? WN * TN : 1][BLOCKQ ? 128 : 1];   // blockwise: weight scales of the tile
 
     // tile order: expert-major, weight tile, then row block; each XCD takes
@@ -212,18 +216,23 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         if constexpr (MODE == MOE_QUANT_PTPC_FP8) rs = rs == 0.0f ? 0.0f : p.a_scale[tok];
         s_rowscale[tid] = rs;
     }
+    if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
+        const float* ws = p.w_scale + e * p.ws_expert;
+        for (int i = tid; i < (GATEUP ? 2 : 1) * TILE_N; i += NT)
+            s_chs[i] = ws[i < TILE_N ? n0 + i : p.I + n0 + i - TILE_N];
+    }
     __syncthreads();
 
     // Copy j of a wave fills 8 LDS rows of block wave + NW*j: lane i writes
     // row 8*blk + i/8, physical chunk i%8, which holds logical chunk
     // (i%8) ^ swizzle(row) of that row.
     const int crow = lane >> 3, cphys = lane & 7;
-    const uint8_t* a_src[A_IN];
+    uint32_t a_src[A_IN];                                   // byte offsets within the activations
 #pragma unroll
     for (int j = 0; j < A_IN; ++j) {
         const int r = (wave + NW * j) * 8 + crow;
         const int c = cphys ^ ((r >> 1) & 7);
-        a_src[j] = p.a + static_cast<int64_t>(s_tok[r]) * p.a_ld + c * 16;
+        a_src[j] = static_cast<uint32_t>(static_cast<int64_t>(s_tok[r]) * p.a_ld + c * 16);
     }
     // weight tile row t (LDS row BM + t) is row t % WCOLS of wave column t / WCOLS
     // (gate rows first, then up rows)
@@ -255,10 +264,10 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         const int64_t ko = static_cast<int64_t>(S) * kRow;
         const uint32_t st = lds0 + buf * STAGE;
         if constexpr (d < A_IN) {
-            dma16(a_src[d] + ko, __builtin_amdgcn_readfirstlane(st + (wave + NW * d) * 8 * kRow));
+            dma16(a_src[d], p.a + ko, __builtin_amdgcn_readfirstlane(st + (wave + NW * d) * 8 * kRow));
         } else if constexpr (d < A_IN + B_IN) {
             constexpr int j = d - A_IN;
-            dma16(wexp + b_src[j] + ko, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
+            dma16(b_src[j], wexp + ko, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
         } else {
             dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 64 * NW + wave * 64) * 4));
         }
@@ -487,24 +496,16 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         const int ldb = static_cast<int>(p.out_ld) * OBYTES;          // bytes per output row
         const __amdgpu_buffer_rsrc_t rsrc =
             tile_rsrc(static_cast<uint8_t*>(p.out) + static_cast<int64_t>(m0) * p.out_ld * OBYTES);
-        const float* wsx = (MODE == MOE_QUANT_PTPC_FP8) ? p.w_scale + e * p.ws_expert : nullptr;
         // first output column of this wave
         const int col0 = GATEUP ? n0 + wn * HALF : n0 + wn * WCOLS;
-        // channel scales of this lane's columns: [tile][g] -> 4 consecutive columns
-        float4 swa[GATEUP ? TN / 2 : TN][4], swb[GATEUP ? TN / 2 : 1][4];
-    #pragma unroll
-        for (int t = 0; t < (GATEUP ? TN / 2 : TN); ++t)
-    #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c = col0 + t * 32 + 8 * g + 4 * q;
-                if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
-                    swa[t][g] = *reinterpret_cast<const float4*>(wsx + c);
-                    if constexpr (GATEUP) swb[t][g] = *reinterpret_cast<const float4*>(wsx + p.I + c);
-                } else {
-                    swa[t][g] = float4{1.0f, 1.0f, 1.0f, 1.0f};
-                    if constexpr (GATEUP) swb[t][g] = float4{1.0f, 1.0f, 1.0f, 1.0f};
-                }
-            }
+        // channel scales of this lane's columns (tile t, group g: four
+        // consecutive columns), read from LDS where they are used
+        auto chs = [&](int t, int g, bool up) {
+            if constexpr (MODE == MOE_QUANT_PTPC_FP8)
+                return *reinterpret_cast<const float4*>(&s_chs[(up ? TILE_N : 0) + col0 - n0 + t * 32 + 8 * g + 4 * q]);
+            else
+                return float4{1.0f, 1.0f, 1.0f, 1.0f};
+        };
     #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
             const float rs = s_rowscale[arow + tm * 32 + r32];
@@ -514,12 +515,12 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     float v[4];
-                    const float4 sa = swa[t][g];
+                    const float4 sa = chs(t, g, false);
                     const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
     #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         if constexpr (GATEUP) {
-                            const float4 sb = swb[t][g];
+                            const float4 sb = chs(t, g, true);
                             const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
                             v[j] = silu_mul(acc[tm][t][4 * g + j] * rs * sav[j], acc[tm][t + TN / 2][4 * g + j] * rs * sbv[j]);
                         } else {
@@ -607,6 +608,9 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
                            const int* counts, void* act, hipStream_t s) {
     if (block_m == 16) return stream_gateup_launch(L, a, a_scale, T, sorted_ids, offsets, counts, act, s);
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    // the copies address activations and one expert's weights with 32-bit offsets
+    if (static_cast<int64_t>(T) * L->D * elem >= (1LL << 32) || 2LL * L->I * L->D * elem >= (1LL << 32))
+        return MOE_ERR_UNSUPPORTED;
     GemmArgs g{};
     g.offsets = offsets;
     g.counts = counts;
@@ -641,6 +645,8 @@ int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* 
                          void* out_perm, hipStream_t s) {
     if (block_m == 16) return stream_down_launch(L, act, act_scale, T, offsets, counts, out_perm, s);
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    if (max_rows * L->I * elem >= (1LL << 32) || static_cast<int64_t>(L->D) * L->I * elem >= (1LL << 32))
+        return MOE_ERR_UNSUPPORTED;
     GemmArgs g{};
     g.offsets = offsets;
     g.counts = counts;
