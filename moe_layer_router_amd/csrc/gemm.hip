@@ -22,7 +22,8 @@
 // what bounds the copy rate per CU.  LDS rows are 128 bytes with their
 // 16-byte chunks XOR-swizzled by row (applied on the global side) so that the
 // MFMA operand reads are free of bank conflicts.  NS (2 or 3) LDS stages form
-// a ring; the copies of step S + NS - 1 go out while step S is computed.
+// a ring; the copies of step S + NS go out in the second half of step S, as
+// soon as stage S is released.
 //
 // Compute.  Each 128-byte step is two 64-byte half-steps of 32x32 MFMAs
 // (v_mfma_f32_32x32x64_f8f6f4 or two v_mfma_f32_32x32x16_bf16).  Lane l
@@ -34,7 +35,9 @@
 // (pinned with scheduling barriers) so that a memory instruction stalled at
 // issue overlaps a running MFMA.  One wait + barrier per 128-byte step.
 //
-// Pad rows read a real row and are zeroed by a row mask in the epilogue.
+// Pad rows read a real row and are zeroed by a row mask in the epilogue;
+// 32-row tiles made only of pads (known from the expert's row count) get no
+// operand reads and no MFMAs.
 // Tiles are ordered expert by expert, weight tile by weight tile, row block
 // fastest, and each XCD (workgroup id mod 8) takes a contiguous range of
 // that order, so the row blocks of one expert that share a weight tile run
@@ -166,7 +169,6 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     constexpr int A_IN = BM / (8 * NW);         // copies (8 rows x 128 B) of A per wave per step
     constexpr int B_IN = NROWS / (8 * NW);      // copies of B per wave per step
     constexpr int N_BIG = A_IN + B_IN + (BLOCKQ ? 1 : 0);   // copies per wave per step
-    constexpr int NB1 = N_BIG / 2, NB2 = N_BIG - NB1;       // issued in the two half-steps
     static_assert(TM >= 1 && A_IN >= 1 && B_IN >= 1 && BM % (8 * NW) == 0 && NROWS % (8 * NW) == 0 && BM <= 256 &&
                       2 * STAGE <= kLdsBudget && (!BLOCKQ || BM <= 64 * NW),
                   "tile shape");
@@ -410,13 +412,11 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
             }
         };
 
-        // Prologue: steps 0 .. NS-2 and the first NB1 copies of step NS-1 go
-        // out; wait for step 0, then read the fragments of its first half.
-        for (int S = 0; S < NS - 1; ++S)
+        // Prologue: steps 0 .. NS-1 go out (every stage is free); wait for
+        // step 0, then read the fragments of its first half.
+        for (int S = 0; S < NS; ++S)
             if (S < nbig) issue(S);
-        const bool pro_more = NS - 1 < nbig;
-        if (pro_more) static_for<NB1>([&](auto D) { issue_one(D, NS - 1, (NS - 1) % NS); });
-        if (pro_more) vmcnt_wait<(NS - 2) * N_BIG + NB1>();
+        if (NS <= nbig) vmcnt_wait<(NS - 1) * N_BIG>();
         else vmcnt_wait<0>();
         __syncthreads();
         static_for<NL>([&](auto L) { load_one(std::integral_constant<int, 0>{}, L, 0, 0); });
@@ -429,12 +429,14 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
 
         // Step S (stage S % NS, landed and published):
         //   first half: MFMAs from set 0; read the second half of S into set
-        //     1; issue the last NB2 copies of step S + NS - 1 (into the stage
-        //     of step S - 1, released by the previous barrier); wait until
-        //     step S + 1 has landed (copies issued after it may stay in
-        //     flight) and barrier: publishes S + 1 and releases stage S.
+        //     1; wait until step S + 1 has landed (copies issued after it may
+        //     stay in flight) and barrier: publishes S + 1 and releases stage
+        //     S.
         //   second half: MFMAs from set 1; read the first half of S + 1 into
-        //     set 0; issue the first NB1 copies of step S + NS (into stage S).
+        //     set 0; issue all copies of step S + NS (into stage S), so each
+        //     step's copies have NS - 1 whole steps to land (issuing half of
+        //     them a half-step later, as a way to spread the copies over
+        //     both halves, left those only half a step and was 5 % slower).
         using X0 = std::integral_constant<int, 0>;
         using X1 = std::integral_constant<int, 1>;
         using First = std::integral_constant<bool, true>;
@@ -444,8 +446,8 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
             const bool next = S + 1 < nbig;
             const bool cp2 = S + NS - 1 < nbig, cp1 = S + NS < nbig;
             step_scales(buf, S);
-            half_step(X0{}, First{}, std::integral_constant<int, NB1>{}, std::integral_constant<int, NB2>{}, true,
-                      buf, 1, cp2, S + NS - 1);
+            half_step(X0{}, First{}, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, true,
+                      buf, 1, false, 0);
             if (next) {
                 if (cp2) vmcnt_wait<(NS - 2) * N_BIG>();
                 else vmcnt_wait<0>();
@@ -455,7 +457,7 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
             // the last step (they then read an idle stage into registers no
             // MFMA uses): a branch around them would make the compiler wait
             // for every outstanding LDS read before the MFMAs that follow
-            half_step(X1{}, Second{}, std::integral_constant<int, 0>{}, std::integral_constant<int, NB1>{}, true,
+            half_step(X1{}, Second{}, std::integral_constant<int, 0>{}, std::integral_constant<int, N_BIG>{}, true,
                       (S + 1) % NS, 0, cp1, S + NS);
         }
         vmcnt_wait<0>();
