@@ -4,9 +4,11 @@ One step = one pass of the whole routed-expert path over one batch of
 synthetic input, resident in HBM: top-k routing -> permutation -> x
 quantization -> gate/up grouped GEMM with SwiGLU -> act quantization -> down
 grouped GEMM -> weighted combine (plus the router projection when the
-workload has one).  The timed loop calls the C-ABI step entries in the order
-moe_forward runs them, with HIP events around the two grouped GEMMs (the
-dominant kernels); the fused moe_forward entry is timed too as a cross-check.
+workload has one).  The timed loop calls the fused moe_forward entry; a
+second loop calls the C-ABI step entries one by one (the same kernels, with
+routing and x quantization as separate launches) with HIP events around the
+two grouped GEMMs, for the per-kernel figures and the roofline of the
+dominant kernel, and checks that both paths give the same bits.
 
 Prints ONE JSON line.  Default workload: the Qwen3-235B-A22B-shaped prefill
 layer (T=8192, D=4096, E=128, top-8, I=1536, PTPC-FP8).
@@ -113,6 +115,21 @@ class Steps:
             ev[3].record()
         L.check("combine", lib.moe_unpermute_combine(p["out_perm"], 1 if fp8 else 0, p["inv_perm"], p["topk_w"],
                                                      self.T, w.k, w.n_shared, w.D, self.y.data_ptr(), s))
+
+
+def gateup_bytes(w, ids_np):
+    """Algorithmic HBM bytes of one gate/up launch: W13 codes and scales of
+    the experts the batch uses, the activation rows read once, act written once."""
+    import numpy as np
+    used = len(np.unique(ids_np)) + w.n_shared
+    elem = 2 if w.quant == "bf16" else 1
+    wb = 2 * w.I * w.D * elem
+    if w.quant == "ptpc_fp8":
+        wb += 4 * 2 * w.I
+    elif w.quant == "block128_fp8":
+        wb += 4 * (2 * w.I // 128) * (w.D // 128)
+    ab = w.T * w.D * elem + (0 if w.quant == "bf16" else 4 * w.T * (1 if w.quant == "ptpc_fp8" else w.D // 128))
+    return used * wb + ab + w.T * (w.k + w.n_shared) * w.I * 2
 
 
 def active_expert_bytes(w, ids_np):
@@ -258,33 +275,38 @@ def main():
     st = Steps(case.layer, w, case.x, case.logits, args.block_m)
     log("block_m", st.B, "max_rows", st.lay["max_rows"])
 
+    # the timed steps: the fused entry
+    y_fused = torch.empty_like(st.y)
+    ws = case.layer.workspace(w.T, args.block_m)
+    fwd = lambda: case.layer.forward(case.x, case.logits, block_m=args.block_m, y=y_fused, workspace=ws)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.steps):
+        fwd()
+    f1.record()
+    torch.cuda.synchronize()
+    ms = f0.elapsed_time(f1) / args.steps
+
+    # the step entries, HIP events around the grouped GEMMs
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
         st.run(ev[i])
     t_end.record()
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
+    steps_ms = t_start.elapsed_time(t_end) / args.steps
     gu_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     dn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
-    log(f"step {ms:.3f} ms  gate_up {gu_ms:.3f} ms  down {dn_ms:.3f} ms")
-
-    # the fused entry on the same inputs
-    y_fused = case.layer.forward(case.x, case.logits, block_m=args.block_m)
-    torch.cuda.synchronize()
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record()
-    for _ in range(args.steps):
-        case.layer.forward(case.x, case.logits, block_m=args.block_m, y=y_fused)
-    f1.record()
-    torch.cuda.synchronize()
-    fused_ms = f0.elapsed_time(f1) / args.steps
+    log(f"step {ms:.3f} ms (step entries {steps_ms:.3f} ms)  gate_up {gu_ms:.3f} ms  down {dn_ms:.3f} ms")
     same = bool(torch.equal(y_fused.view(torch.int16), st.y.view(torch.int16)))
+    ids = case.layer.intermediates(w.T, args.block_m, ws)["topk_ids"].cpu().numpy()
 
     rows = w.T * (w.k + w.n_shared)
     flops = w.flops()
@@ -293,20 +315,34 @@ def main():
     peak = PEAK_TFLOPS[w.quant]
     tflops = flops / (ms * 1e-3) / 1e12
     gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
+    # the gate/up launch is MFMA-bound when its flops per algorithmic byte
+    # exceed the ridge (peak flops / 8 TB/s), else HBM-bound
+    gu_bytes = gateup_bytes(w, ids)
+    if gu_flops / gu_bytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "kernel": "grouped_gemm_gateup_silu", "achieved": round(gu_tf, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(gu_tf / peak, 4)}
+    else:
+        gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "grouped_gemm_gateup_silu", "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof.update(traffic=measured_traffic(w.name), avg_launch_ms=round(gu_ms, 4), flops_per_launch=gu_flops,
+                bytes_per_launch=int(gu_bytes))
+    layer_bytes = active_expert_bytes(w, ids)[0] + w.T * w.D * (2 + 2) + (0 if case.logits is None else 4 * w.T * w.E)
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3" if w.quant != "bf16" else "bf16", "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "top_k": w.k, "I": w.I,
                    "n_shared": w.n_shared, "quant": w.quant, "scoring": w.scoring, "block_m": st.B},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_gateup_silu", "achieved": round(gu_tf, 1),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(gu_tf / peak, 4), "traffic": measured_traffic(w.name),
-                     "avg_launch_ms": round(gu_ms, 4), "flops_per_launch": gu_flops},
+        "roofline": roof,
         "kernels": {"gateup_ms": round(gu_ms, 4), "down_ms": round(dn_ms, 4),
                     "down_tflops": round(dn_flops / (dn_ms * 1e-3) / 1e12, 1),
                     "gemms_frac_of_peak": round((gu_flops + dn_flops) / ((gu_ms + dn_ms) * 1e-3) / 1e12 / peak, 4),
                     "rest_ms": round(ms - gu_ms - dn_ms, 4)},
-        "fused_ms_per_step": round(fused_ms, 4), "fused_equals_steps": same,
+        "layer": {"tflops": round(tflops, 1), "frac_mfma": round(tflops / peak, 4), "algorithmic_bytes": int(layer_bytes),
+                  "GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+                  "frac_hbm": round(layer_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "step_entries_ms_per_step": round(steps_ms, 4), "step_entries_equal_fused": same,
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
     }
     if not args.no_decode and w.name != "qwen3_235b_decode_ptpc":

@@ -17,6 +17,8 @@ int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const 
 int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, uint8_t* q, float* scale,
                             hipStream_t s);
 bool front_small_ok(int T, int k, int n_shared);
+int32_t front_route_quant_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int* ids,
+                                 float* w, uint8_t* xq, float* xs, hipStream_t s);
 int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int block_m,
                            int max_rows, int* ids, float* w, int* counts, int* offsets, int* sorted, int* bexp,
                            int* inv, uint8_t* xq, float* xs, hipStream_t s);
@@ -335,16 +337,15 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
                                      fp8 ? static_cast<float*>(at(o.xs)) : nullptr, s)) != MOE_OK)
             return st;
     } else {
-        if ((st = route_topk_launch(logits, T, E, k, L->scoring, L->n_groups, L->topk_groups, L->sel_bias,
-                                    L->renormalize, L->route_scale, ids, w, s)) != MOE_OK)
+        // routing and x quantization in one launch (one workgroup per token),
+        // then the multi-kernel permutation
+        if ((st = front_route_quant_launch(L, x_bf16, logits, T, ids, w,
+                                           fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr,
+                                           fp8 ? static_cast<float*>(at(o.xs)) : nullptr, s)) != MOE_OK)
             return st;
         if ((st = permute_align_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
                                        static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, at(o.scratch),
                                        s)) != MOE_OK)
-            return st;
-        if (fp8 && (st = quant_rows_launch(static_cast<const uint16_t*>(x_bf16), T, L->D, group, nullptr,
-                                           static_cast<uint8_t*>(at(o.xq)), static_cast<float*>(at(o.xs)), s)) !=
-                       MOE_OK)
             return st;
     }
     void* act = at(o.act);

@@ -1,4 +1,5 @@
-// Front end for small batches (decode), in two launches.
+// Front end: routing and FP8 quantization of x in one launch (any batch);
+// for small batches (decode) the permutation in a second one.
 //
 // At a few dozen tokens the routing, the three permutation steps and the FP8
 // quantization of x each move a few KB; as five separate launches they cost
@@ -9,6 +10,7 @@
 //     the token (route_token, shared with the routing kernel), wave 1
 //     quantizes its x row (the row-quantization arithmetic), in parallel and
 //     spread over T CUs;
+//     (larger batches use it too, followed by the multi-kernel permutation);
 //   permute_small_kernel: one workgroup.  A token's k picks are distinct
 //     experts and T <= 64, so every expert's rows are a 64-bit mask of
 //     tokens (LDS atomicOr); a row's rank in its expert's segment is the
@@ -224,6 +226,40 @@ bool front_small_ok(int T, int k, int n_shared) {
     return T >= 1 && T <= kFrontMaxT && T * (k + n_shared) <= kFrontMaxRows;
 }
 
+static void front_tokens(const moe_layer_desc* L, const FrontArgs& a, hipStream_t s) {
+    const int group = L->quant == MOE_QUANT_NONE_BF16 ? -1 : (L->quant == MOE_QUANT_BLOCK128_FP8 ? 128 : 0);
+    const int epl = static_cast<int>(ceil_div(L->E, 64));
+    if (epl <= 1) front_scoring<1>(L->scoring, group, a, s);
+    else if (epl <= 2) front_scoring<2>(L->scoring, group, a, s);
+    else if (epl <= 4) front_scoring<4>(L->scoring, group, a, s);
+    else if (epl <= 8) front_scoring<8>(L->scoring, group, a, s);
+    else front_scoring<16>(L->scoring, group, a, s);
+}
+
+// Routing and x quantization only (ids, w, xq, xs), for any T >= 1.
+int32_t front_route_quant_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int* ids,
+                                 float* w, uint8_t* xq, float* xs, hipStream_t s) {
+    FrontArgs a{};
+    a.logits = logits;
+    a.x = static_cast<const uint16_t*>(x);
+    a.T = T;
+    a.D = L->D;
+    a.E = L->E;
+    a.k = L->top_k;
+    a.n_shared = L->n_shared;
+    a.n_groups = L->n_groups;
+    a.topk_groups = L->topk_groups;
+    a.sel_bias = L->sel_bias;
+    a.renormalize = L->renormalize;
+    a.route_scale = L->route_scale;
+    a.ids = ids;
+    a.w = w;
+    a.xq = xq;
+    a.xs = xs;
+    front_tokens(L, a, s);
+    return moe_launch_status();
+}
+
 int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int block_m,
                            int max_rows, int* ids, float* w, int* counts, int* offsets, int* sorted, int* bexp,
                            int* inv, uint8_t* xq, float* xs, hipStream_t s) {
@@ -251,13 +287,7 @@ int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* 
     a.inv = inv;
     a.xq = xq;
     a.xs = xs;
-    const int group = L->quant == MOE_QUANT_NONE_BF16 ? -1 : (L->quant == MOE_QUANT_BLOCK128_FP8 ? 128 : 0);
-    const int epl = static_cast<int>(ceil_div(L->E, 64));
-    if (epl <= 1) front_scoring<1>(L->scoring, group, a, s);
-    else if (epl <= 2) front_scoring<2>(L->scoring, group, a, s);
-    else if (epl <= 4) front_scoring<4>(L->scoring, group, a, s);
-    else if (epl <= 8) front_scoring<8>(L->scoring, group, a, s);
-    else front_scoring<16>(L->scoring, group, a, s);
+    front_tokens(L, a, s);
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kFrontWaves * 64), 0, s, a);
     return moe_launch_status();
 }
