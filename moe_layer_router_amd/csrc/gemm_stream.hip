@@ -299,7 +299,9 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
 // 16-row weight tiles per wave (gate/up: a gate and an up tile) and K steps
 // in flight per wave.  One tile per wave for down spreads its items more
 // evenly over the waves but halves the bytes each wave keeps in flight, and
-// measured slower (Qwen3-235B decode 178 -> 196 us).
+// measured slower (Qwen3-235B decode 178 -> 196 us); so did splitting only
+// the items of the last, partial round (177 -> 181 us): the waves share HBM
+// bandwidth, and the few that run a last round get more of it.
 template <bool GATEUP>
 constexpr int stream_tn() { return 2; }
 constexpr int kStreamPF = 4;
