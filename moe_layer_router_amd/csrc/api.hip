@@ -260,10 +260,8 @@ int32_t moe_default_block_m(const moe_layer_desc* L, int32_t T) {
     const int64_t per_expert = rows / (L->E + L->n_shared);
     if (T <= kStreamMaxT) return 16;
     // 32-row tiles of pads are skipped, so a tall tile costs little beyond
-    // the expert's rows and reads each weight tile once per 256 rows; the
-    // blockwise mode's 128-row tile is 128 x 256 with three LDS stages,
-    // better where each weight tile streams from HBM for a few hundred rows
-    if (per_expert >= 96) return L->quant == MOE_QUANT_BLOCK128_FP8 && per_expert < 320 ? 128 : 256;
+    // the expert's rows and reads each weight tile once per 256 rows
+    if (per_expert >= 96) return 256;
     if (per_expert >= 48) return 128;
     return 32;
 }
