@@ -6,11 +6,10 @@
 // (plus the shared row) are gathered through the inverse permutation and
 // reduced in registers, j = 0..k-1 then shared, fp32 accumulate, one bf16
 // rounding -- each out_perm row is read once and y written once.
-#include "common.h"
+#include "quant_dev.h"
 
 namespace moe {
 
-struct alignas(16) u16x8 { uint16_t v[8]; };
 struct alignas(16) f32x4 { float v[4]; };
 
 // OUT_BF16: out_perm rows are bf16 (else fp32).  Workgroup (t, y) owns
@@ -43,8 +42,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ o
     for (int j = 0; j < NR; ++j) {
         if (r[j] >= 0) {
             if (OUT_BF16) {
-                const u16x8 v = reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(out_perm) +
-                                                               static_cast<int64_t>(r[j]) * D)[c];
+                // each expert-output row is read once: non-temporal
+                const bf16x8 v = ld_once(reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(out_perm) +
+                                                                         static_cast<int64_t>(r[j]) * D) + c);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[j][i] = bf16_to_f32(v.v[i]);
             } else {
@@ -77,10 +77,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ o
             for (int i = 0; i < 8; ++i) acc[i] += o[j][i];
         }
     }
-    u16x8 out;
+    bf16x8 out;
 #pragma unroll
     for (int i = 0; i < 8; ++i) out.v[i] = f32_to_bf16(acc[i]);
-    reinterpret_cast<u16x8*>(y + static_cast<int64_t>(t) * D)[c] = out;
+    reinterpret_cast<bf16x8*>(y + static_cast<int64_t>(t) * D)[c] = out;
 }
 
 template <bool OUT_BF16>

@@ -29,7 +29,7 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int c = lane + 64 * i;
-        if (c < nvec) v[i] = xr[c];
+        if (c < nvec) v[i] = ld_once(xr + c);
     }
     uint2* qr = reinterpret_cast<uint2*>(q + row * K);
     if (GROUP == 0) {

@@ -8,6 +8,14 @@ namespace moe {
 
 struct alignas(16) bf16x8 { uint16_t v[8]; };
 
+// A 16-byte load of data read once (rows that are quantized or combined and
+// not read again): marked non-temporal, so it does not displace reused data
+// in the caches.
+__device__ __forceinline__ bf16x8 ld_once(const bf16x8* p) {
+    typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
+}
+
 // Eight codes with the packed hardware conversion (v_cvt_pk_fp8_f32, round to
 // nearest even) after clamping to +-448.  Over every finite fp32 input this
 // gives the same code as f32_to_e4m3 (common.h), the encoder written from
