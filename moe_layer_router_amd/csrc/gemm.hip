@@ -545,7 +545,11 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
             for (int it = 0; it < 32 / RPI; ++it) {
                 const int row = it * RPI + lane / LPR, ch = lane % LPR;
                 const u32x4 d = *reinterpret_cast<const u32x4*>(reg + row * RBP + ch * 16);
-                __builtin_amdgcn_raw_buffer_store_b128(d, rsrc, (arow + tm * 32 + row) * ldb + col0 * OBYTES + ch * 16, 0, 0);
+                // non-temporal (cache policy bit 1): the output is read once, by
+                // the next kernel, and should not displace the operands that
+                // running tiles share through L2 (down GEMM 0.549 -> 0.537 ms,
+                // blockwise layer 1.17 -> 1.11 ms)
+                __builtin_amdgcn_raw_buffer_store_b128(d, rsrc, (arow + tm * 32 + row) * ldb + col0 * OBYTES + ch * 16, 0, 2);
             }
         }
     };
