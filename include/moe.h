@@ -68,6 +68,10 @@ extern "C" {
 #define MOE_QUANT_PTPC_FP8      1  /* e4m3 per-token x per-output-channel       */
 #define MOE_QUANT_BLOCK128_FP8  2  /* e4m3 1x128 activations, 128x128 weights   */
 
+/* weight_layout (moe_layer_desc) / layout (moe_quant_weight_fp8) */
+#define MOE_WEIGHTS_ROWS        0  /* row-major                                 */
+#define MOE_WEIGHTS_BLOCKED     1  /* 16 rows x 128 bytes per contiguous block  */
+
 /* Limits of this build (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS   1024  /* E + n_shared                                 */
 #define MOE_MAX_TOPK        16
@@ -85,6 +89,14 @@ extern "C" {
  *              quant 2: [E+n_shared, 2I/128, D/128] fp32 per 128x128 block;
  *              quant 0: NULL.
  *   w2: [E+n_shared, D, I]; w2_scale: [E+n_shared, D] or [.., D/128, I/128].
+ *   weight_layout: order of the bytes of each [N, K] weight matrix (w13:
+ *              N = 2I, K = D; w2: N = D, K = I):
+ *              MOE_WEIGHTS_ROWS    row-major, K contiguous;
+ *              MOE_WEIGHTS_BLOCKED blocks of 16 rows x 128 bytes, the byte
+ *              (n, b) of a row at ((n/16) * (K_bytes/128) + b/128) * 2048 +
+ *              (n%16) * 128 + b%128 -- the unit the expert GEMMs read per
+ *              step, contiguous in memory.  FP8 modes only (N % 16 == 0 and
+ *              K a multiple of 128 there); moe_quant_weight_fp8 writes it.
  *   router_w: [E, D] fp32 router gate, used by moe_forward when it is given
  *             no logits (may be NULL otherwise).
  *   sel_bias: [E] fp32 selection-only bias of grouped-sigmoid routing or NULL.
@@ -94,6 +106,7 @@ typedef struct moe_layer_desc {
     int32_t scoring, n_groups, topk_groups, renormalize;
     float route_scale;
     int32_t quant;
+    int32_t weight_layout;
     const void* w13;
     const float* w13_scale;
     const void* w2;
@@ -195,10 +208,11 @@ int32_t moe_quant_ptpc_fp8(const void* x_bf16, int64_t M, int32_t K, int32_t gro
  * is output channel n).  quant 1 (PTPC): one scale per row, scale
  * [n_mats, N]; quant 2: one scale per 128x128 block, scale
  * [n_mats, N/128, K/128] (N, K multiples of 128).  Same arithmetic as
- * moe_quant_ptpc_fp8.
+ * moe_quant_ptpc_fp8.  layout: MOE_WEIGHTS_ROWS or MOE_WEIGHTS_BLOCKED
+ * (N % 16 == 0, K % 128 == 0) for the codes q; scales are always as above.
  */
 int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int32_t K,
-                             int32_t quant, uint8_t* q, float* scale, void* stream);
+                             int32_t quant, int32_t layout, uint8_t* q, float* scale, void* stream);
 
 /*
  * Grouped GEMM gate/up with fused SwiGLU (GMM V2 item of the Qwen 3.5 page).

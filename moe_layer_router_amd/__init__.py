@@ -6,4 +6,5 @@ ABI in ``include/moe.h``; this package only marshals torch tensors to it.
 
 from ._lib import MoEError, lib  # noqa: F401
 from .ops import (LayerWeights, MoELayer, permute_align, permute_max_rows,  # noqa: F401
-                  quant_ptpc_fp8, quant_weight_fp8, route_topk, router_logits, unpermute_combine)
+                  quant_ptpc_fp8, quant_weight_fp8, route_topk, router_logits, unblock_weights,
+                  unpermute_combine)

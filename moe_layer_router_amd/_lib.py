@@ -17,13 +17,15 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 SCORING_SOFTMAX, SCORING_SIGMOID_GROUPED = 0, 1
 QUANT_NONE_BF16, QUANT_PTPC_FP8, QUANT_BLOCK128_FP8 = 0, 1, 2
 QUANT_CODES = {"bf16": QUANT_NONE_BF16, "ptpc_fp8": QUANT_PTPC_FP8, "block128_fp8": QUANT_BLOCK128_FP8}
+WEIGHTS_ROWS, WEIGHTS_BLOCKED = 0, 1
+LAYOUT_CODES = {"rows": WEIGHTS_ROWS, "blocked": WEIGHTS_BLOCKED}
 
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("D", c_int32), ("I", c_int32), ("E", c_int32), ("top_k", c_int32), ("n_shared", c_int32),
                 ("scoring", c_int32), ("n_groups", c_int32), ("topk_groups", c_int32),
                 ("renormalize", c_int32), ("route_scale", c_float), ("quant", c_int32),
-                ("w13", c_void_p), ("w13_scale", c_void_p), ("w2", c_void_p), ("w2_scale", c_void_p),
+                ("weight_layout", c_int32), ("w13", c_void_p), ("w13_scale", c_void_p), ("w2", c_void_p), ("w2_scale", c_void_p),
                 ("router_w", c_void_p), ("sel_bias", c_void_p)]
 
 
@@ -45,8 +47,8 @@ SIGNATURES = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_quant_ptpc_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                      c_void_p]),
-    "moe_quant_weight_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p,
-                                       c_void_p]),
+    "moe_quant_weight_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                       c_void_p, c_void_p]),
     "moe_grouped_gemm_gateup_silu": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_int32,
                                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_grouped_gemm_down": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_int32, c_void_p,

@@ -12,9 +12,11 @@ size_t permute_scratch_bytes(int T, int k, int n_shared, int E);
 int32_t permute_align_launch(const int* ids, int T, int k, int E, int n_shared, int block_m, int max_rows,
                              int* counts, int* offsets, int* sorted_ids, int* block_expert, int* inv_perm,
                              void* scratch, hipStream_t s);
+int32_t quant_wrows_launch(const uint16_t* w, int64_t M, int K, bool blocked, uint8_t* q, float* scale,
+                           hipStream_t s);
 int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const int* valid_rows, uint8_t* q,
                           float* scale, hipStream_t s);
-int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, uint8_t* q, float* scale,
+int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, bool blocked, uint8_t* q, float* scale,
                             hipStream_t s);
 bool front_small_ok(int T, int k, int n_shared);
 int32_t front_route_quant_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int* ids,
@@ -79,6 +81,8 @@ int32_t check_layer(const moe_layer_desc* L) {
                   L->quant == MOE_QUANT_BLOCK128_FP8);
     MOE_CHECK_ARG(L->w13 != nullptr && L->w2 != nullptr);
     if (L->quant != MOE_QUANT_NONE_BF16) MOE_CHECK_ARG(L->w13_scale != nullptr && L->w2_scale != nullptr);
+    MOE_CHECK_ARG(L->weight_layout == MOE_WEIGHTS_ROWS || L->weight_layout == MOE_WEIGHTS_BLOCKED);
+    MOE_CHECK_SUP(L->weight_layout == MOE_WEIGHTS_ROWS || L->quant != MOE_QUANT_NONE_BF16);
     // column tiles of the grouped GEMMs: 128 act columns, 256 output columns
     MOE_CHECK_SUP(L->I % 128 == 0 && L->D % 256 == 0);
     MOE_CHECK_SUP(L->D <= 16384 && L->I <= 16384);
@@ -194,20 +198,24 @@ int32_t moe_quant_ptpc_fp8(const void* x_bf16, int64_t M, int32_t K, int32_t gro
                              as_stream(stream));
 }
 
-int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int32_t K, int32_t quant, uint8_t* q,
-                             float* scale, void* stream) {
+int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int32_t K, int32_t quant,
+                             int32_t layout, uint8_t* q, float* scale, void* stream) {
     MOE_CHECK_ARG(n_mats >= 0 && N > 0 && K > 0);
     MOE_CHECK_ARG(quant == MOE_QUANT_PTPC_FP8 || quant == MOE_QUANT_BLOCK128_FP8);
+    MOE_CHECK_ARG(layout == MOE_WEIGHTS_ROWS || layout == MOE_WEIGHTS_BLOCKED);
+    const bool blocked = layout == MOE_WEIGHTS_BLOCKED;
+    if (blocked) MOE_CHECK_SUP(N % 16 == 0 && K % 128 == 0);
     if (n_mats == 0) return MOE_OK;
     MOE_CHECK_ARG(w_bf16 && q && scale);
     if (quant == MOE_QUANT_PTPC_FP8) {
         MOE_CHECK_SUP(K % 8 == 0 && K <= 16384);
-        return quant_rows_launch(static_cast<const uint16_t*>(w_bf16), n_mats * N, K, 0, nullptr, q, scale,
-                                 as_stream(stream));
+        return quant_wrows_launch(static_cast<const uint16_t*>(w_bf16), n_mats * N, K, blocked, q, scale,
+                                  as_stream(stream));
     }
     MOE_CHECK_SUP(N % 128 == 0 && K % 128 == 0);
     MOE_CHECK_SUP(n_mats * (N / 128) * (K / 128) < (1LL << 31));
-    return quant_wblock_launch(static_cast<const uint16_t*>(w_bf16), n_mats, N, K, q, scale, as_stream(stream));
+    return quant_wblock_launch(static_cast<const uint16_t*>(w_bf16), n_mats, N, K, blocked, q, scale,
+                               as_stream(stream));
 }
 
 int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a, const float* a_scale, int32_t T,

@@ -91,6 +91,7 @@ struct GemmArgs {
     const int* offsets;        // [E'+1] padded expert offsets
     const int* counts;         // [E'] routed rows per expert (NULL: every row of a segment is live)
     const uint8_t* w;          // [E', Nw, K] weights
+    int w_blocked;             // weights in blocks of 16 rows x 128 bytes (else row-major)
     int64_t w_expert_bytes;
     const float* w_scale;      // PTPC: [E', Nw]; block: [E', Nw/128, K/128]
     int64_t ws_expert;         // floats per expert
@@ -247,7 +248,10 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         const int c = cphys ^ (((BM + t) >> 1) & 7);
         const int w = t / WCOLS, jj = t % WCOLS;
         const int wr = GATEUP ? (jj < HALF ? n0 + w * HALF + jj : p.I + n0 + w * HALF + jj - HALF) : n0 + t;
-        b_src[j] = static_cast<uint32_t>(wr * wrow_bytes + c * 16);
+        // blocked weights: the 8 rows of a copy are half of one contiguous
+        // 2 KB block (16 rows x one 128-byte step)
+        b_src[j] = static_cast<uint32_t>(p.w_blocked ? (wr >> 4) * (wrow_bytes / kRow) * 2048 + (wr & 15) * kRow + c * 16
+                                                     : wr * wrow_bytes + c * 16);
     }
     // blockwise: wave w copies the scales of rows 64w .. 64w+63 (rows past BM
     // read row 0 into unused slots)
@@ -264,12 +268,13 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     auto issue_one = [&](auto D, int S, int buf) {
         constexpr int d = decltype(D)::value;
         const int64_t ko = static_cast<int64_t>(S) * kRow;
+        const int64_t kw = static_cast<int64_t>(S) * (p.w_blocked ? 2048 : kRow);   // step offset in the weights
         const uint32_t st = lds0 + buf * STAGE;
         if constexpr (d < A_IN) {
             dma16(a_src[d], p.a + ko, __builtin_amdgcn_readfirstlane(st + (wave + NW * d) * 8 * kRow));
         } else if constexpr (d < A_IN + B_IN) {
             constexpr int j = d - A_IN;
-            dma16(b_src[j], wexp + ko, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
+            dma16(b_src[j], wexp + kw, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
         } else {
             dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 64 * NW + wave * 64) * 4));
         }
@@ -630,6 +635,7 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
     g.sentinel = T * (L->top_k + L->n_shared);
     g.block_expert = block_expert;
     g.w = static_cast<const uint8_t*>(L->w13);
+    g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
     g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
     g.w_scale = L->w13_scale;
     g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? 2LL * L->I
@@ -663,6 +669,7 @@ int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* 
     g.sorted_ids = nullptr;
     g.block_expert = block_expert;
     g.w = static_cast<const uint8_t*>(L->w2);
+    g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
     g.w_expert_bytes = static_cast<int64_t>(L->D) * L->I * elem;
     g.w_scale = L->w2_scale;
     g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? static_cast<int64_t>(L->D)

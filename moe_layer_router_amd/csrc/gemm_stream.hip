@@ -39,6 +39,7 @@ struct StreamArgs {
     const int* offsets;        // [E'+1] padded (multiples of 16)
     const int* counts;         // [E'] routed rows per expert (NULL: every row of a segment is live)
     const uint8_t* w;
+    int w_blocked;             // weights in blocks of 16 rows x 128 bytes (else row-major)
     int64_t w_expert_bytes;
     const float* w_scale;
     int64_t ws_expert;
@@ -108,7 +109,10 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
         wn0[t] = GATEUP ? (t < TN / 2 ? c0 + t * 16 : p.I + c0 + (t - TN / 2) * 16) : c0 + t * 16;
-        bp[t] = wexp + (wn0[t] + r16) * wrow + kq;
+        // blocked weights: a tile's 16 rows x 128 bytes of one step are one
+        // contiguous 2 KB block
+        bp[t] = p.w_blocked ? wexp + static_cast<int64_t>(wn0[t] >> 4) * (wrow / 128) * 2048 + r16 * 128 + kq
+                            : wexp + (wn0[t] + r16) * wrow + kq;
     }
     // operand rows: row r16 of each M tile; rows past the segment or on a pad
     // slot read a valid row and are zeroed by the epilogue's row mask
@@ -152,8 +156,9 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
         int ks = s + kbeg;
         ks = ks >= nk ? ks - nk : ks;
         const int64_t ko = static_cast<int64_t>(ks) * 128;
+        const int64_t kw = static_cast<int64_t>(ks) * (p.w_blocked ? 2048 : 128);   // step offset in the weights
 #pragma unroll
-        for (int t = 0; t < TN; ++t) bq[j][t] = ld32(bp[t] + ko);
+        for (int t = 0; t < TN; ++t) bq[j][t] = ld32(bp[t] + kw);
 #pragma unroll
         for (int m = 0; m < MT; ++m) aqr[j][m] = ld32(ap[m] + ko);
         if constexpr (BLOCKQ) {
@@ -369,6 +374,7 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
     g.offsets = offsets;
     g.counts = counts;
     g.w = static_cast<const uint8_t*>(L->w13);
+    g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
     g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
     g.w_scale = L->w13_scale;
     g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? 2LL * L->I
@@ -393,6 +399,7 @@ int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float
     g.offsets = offsets;
     g.counts = counts;
     g.w = static_cast<const uint8_t*>(L->w2);
+    g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
     g.w_expert_bytes = static_cast<int64_t>(L->D) * L->I * elem;
     g.w_scale = L->w2_scale;
     g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? static_cast<int64_t>(L->D)

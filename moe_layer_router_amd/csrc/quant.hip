@@ -65,8 +65,48 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
     }
 }
 
+// Byte offset of code (row, k) of a [rows, K] code matrix: row-major, or in
+// blocks of 16 rows x 128 bytes (the order the expert GEMMs read; 8-byte
+// pieces at k % 8 == 0 never straddle a block).
+__device__ __forceinline__ int64_t code_off(int64_t row, int k, int K, bool blocked) {
+    if (!blocked) return row * K + k;
+    return ((row >> 4) * (K >> 7) + (k >> 7)) * 2048 + (row & 15) * 128 + (k & 127);
+}
+
+// Weight rows [M, K] (PTPC: one scale per row), one wave per row, codes in
+// the requested layout.
+template <int NV>
+__global__ void __launch_bounds__(256) quant_wrows_kernel(const uint16_t* __restrict__ w, int64_t M, int K,
+                                                          bool blocked, uint8_t* __restrict__ q,
+                                                          float* __restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const int nvec = K >> 3;
+    const bf16x8* wr = reinterpret_cast<const bf16x8*>(w + row * K);
+    bf16x8 v[NV];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nvec) {
+            v[i] = wr[c];
+            m = fmaxf(m, amax8(v[i]));
+        }
+    }
+    m = wave_max(m);
+    float sc, inv;
+    scale_pair(m, sc, inv);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nvec) *reinterpret_cast<uint2*>(q + code_off(row, 8 * c, K, blocked)) = quant8(v[i], inv);
+    }
+    if (lane == 0) scale[row] = sc;
+}
+
 // One 128x128 weight block per workgroup: 256 threads x 8 vectors of 8.
-__global__ void __launch_bounds__(256) quant_wblock_kernel(const uint16_t* __restrict__ w, int N, int K,
+__global__ void __launch_bounds__(256) quant_wblock_kernel(const uint16_t* __restrict__ w, int N, int K, bool blocked,
                                                            uint8_t* __restrict__ q, float* __restrict__ scale) {
     __shared__ float s_max[4];
     const int nbk = K / 128, nbn = N / 128;
@@ -92,7 +132,8 @@ __global__ void __launch_bounds__(256) quant_wblock_kernel(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = (tid >> 4) + 16 * i, c = tid & 15;
-        *reinterpret_cast<uint2*>(q + base + static_cast<int64_t>(r) * K + 8 * c) = quant8(v[i], inv);
+        const int64_t row = mat * N + static_cast<int64_t>(bn) * 128 + r;
+        *reinterpret_cast<uint2*>(q + code_off(row, bk * 128 + 8 * c, K, blocked)) = quant8(v[i], inv);
     }
     if (tid == 0) scale[blk] = sc;
 }
@@ -119,11 +160,24 @@ int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const 
     return moe_launch_status();
 }
 
-int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, uint8_t* q, float* scale,
+int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, bool blocked, uint8_t* q, float* scale,
                             hipStream_t s) {
     const int64_t nblk = n_mats * (N / 128) * (K / 128);
     if (nblk == 0) return MOE_OK;
-    hipLaunchKernelGGL(quant_wblock_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, w, N, K, q, scale);
+    hipLaunchKernelGGL(quant_wblock_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, w, N, K, blocked, q,
+                       scale);
+    return moe_launch_status();
+}
+
+int32_t quant_wrows_launch(const uint16_t* w, int64_t M, int K, bool blocked, uint8_t* q, float* scale,
+                           hipStream_t s) {
+    if (M == 0) return MOE_OK;
+    const int nv = static_cast<int>(ceil_div(K / 8, 64));
+    const dim3 g(static_cast<unsigned>(ceil_div(M, 4))), b(256);
+    if (nv <= 4) hipLaunchKernelGGL((quant_wrows_kernel<4>), g, b, 0, s, w, M, K, blocked, q, scale);
+    else if (nv <= 8) hipLaunchKernelGGL((quant_wrows_kernel<8>), g, b, 0, s, w, M, K, blocked, q, scale);
+    else if (nv <= 16) hipLaunchKernelGGL((quant_wrows_kernel<16>), g, b, 0, s, w, M, K, blocked, q, scale);
+    else hipLaunchKernelGGL((quant_wrows_kernel<32>), g, b, 0, s, w, M, K, blocked, q, scale);
     return moe_launch_status();
 }
 

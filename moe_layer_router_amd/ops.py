@@ -99,16 +99,25 @@ def quant_ptpc_fp8(x: torch.Tensor, group: int = 0, valid_rows: Optional[torch.T
     return q, s
 
 
-def quant_weight_fp8(w: torch.Tensor, quant: str):
-    """w: [n_mats, N, K] bf16 -> codes [n_mats, N, K], scales per row or 128x128 block."""
+def quant_weight_fp8(w: torch.Tensor, quant: str, layout: str = "blocked"):
+    """w: [n_mats, N, K] bf16 -> codes (n_mats x N x K bytes, row-major or in
+    16-row x 128-byte blocks; the tensor keeps the [n_mats, N, K] shape),
+    scales per row or 128x128 block."""
     n, N, K = w.shape
     _need(w, _BF16, "w")
     code = L.QUANT_CODES[quant]
     q = _empty((n, N, K), _U8, w)
     s = _empty((n, N) if code == L.QUANT_PTPC_FP8 else (n, N // 128, K // 128), _F32, w)
-    L.check("moe_quant_weight_fp8", L.lib().moe_quant_weight_fp8(_ptr(w), n, N, K, code, _ptr(q), _ptr(s),
-                                                                  _stream()))
+    L.check("moe_quant_weight_fp8", L.lib().moe_quant_weight_fp8(_ptr(w), n, N, K, code, L.LAYOUT_CODES[layout],
+                                                                  _ptr(q), _ptr(s), _stream()))
     return q, s
+
+
+def unblock_weights(q: torch.Tensor) -> torch.Tensor:
+    """Row-major view (a copy) of codes [..., N, K] stored in 16-row x
+    128-byte blocks."""
+    *lead, N, K = q.shape
+    return q.reshape(*lead, N // 16, K // 128, 16, 128).transpose(-3, -2).reshape(*lead, N, K)
 
 
 # ---------------------------------------------------------------- the layer
@@ -128,10 +137,12 @@ class MoELayer:
 
     def __init__(self, D: int, I: int, E: int, top_k: int, weights: LayerWeights, quant: str = "bf16",
                  n_shared: int = 0, scoring: str = "softmax", n_groups: int = 1, topk_groups: int = 1,
-                 renormalize: bool = True, route_scale: float = 1.0):
+                 renormalize: bool = True, route_scale: float = 1.0, weight_layout: Optional[str] = None):
         self.D, self.I, self.E, self.top_k, self.n_shared = D, I, E, top_k, n_shared
         self.quant = quant
         self.weights = weights
+        # FP8 codes from quant_weight_fp8 are blocked by default; bf16 weights are row-major
+        self.weight_layout = weight_layout or ("rows" if quant == "bf16" else "blocked")
         Ep = E + n_shared
         wdt = _BF16 if quant == "bf16" else _U8
         _need(weights.w13, wdt, "w13", (Ep, 2 * I, D))
@@ -150,24 +161,27 @@ class MoELayer:
                                 scoring=L.SCORING_SOFTMAX if scoring == "softmax" else L.SCORING_SIGMOID_GROUPED,
                                 n_groups=n_groups, topk_groups=topk_groups, renormalize=int(renormalize),
                                 route_scale=float(route_scale), quant=L.QUANT_CODES[quant],
-                                w13=_ptr(weights.w13), w13_scale=_ptr(weights.w13_scale), w2=_ptr(weights.w2),
+                                weight_layout=L.LAYOUT_CODES[self.weight_layout], w13=_ptr(weights.w13), w13_scale=_ptr(weights.w13_scale), w2=_ptr(weights.w2),
                                 w2_scale=_ptr(weights.w2_scale), router_w=_ptr(weights.router_w),
                                 sel_bias=_ptr(weights.sel_bias))
         self._ws: Optional[torch.Tensor] = None
 
     @classmethod
     def from_masters(cls, w13_bf16: torch.Tensor, w2_bf16: torch.Tensor, quant: str, router_w=None,
-                     sel_bias=None, **kw) -> "MoELayer":
+                     sel_bias=None, weight_layout: Optional[str] = None, **kw) -> "MoELayer":
         """Build the layer from bf16 master weights, quantizing them on the GPU
-        (per output channel or per 128x128 block) for the FP8 modes."""
+        (per output channel or per 128x128 block) for the FP8 modes, codes in
+        16-row x 128-byte blocks unless weight_layout is "rows"."""
         Ep, I2, D = w13_bf16.shape
         if quant == "bf16":
             w = LayerWeights(w13_bf16.contiguous(), w2_bf16.contiguous(), router_w=router_w, sel_bias=sel_bias)
+            weight_layout = "rows"
         else:
-            q13, s13 = quant_weight_fp8(w13_bf16.contiguous(), quant)
-            q2, s2 = quant_weight_fp8(w2_bf16.contiguous(), quant)
+            weight_layout = weight_layout or "blocked"
+            q13, s13 = quant_weight_fp8(w13_bf16.contiguous(), quant, weight_layout)
+            q2, s2 = quant_weight_fp8(w2_bf16.contiguous(), quant, weight_layout)
             w = LayerWeights(q13, q2, s13, s2, router_w=router_w, sel_bias=sel_bias)
-        return cls(D=D, I=I2 // 2, weights=w, quant=quant, **kw)
+        return cls(D=D, I=I2 // 2, weights=w, quant=quant, weight_layout=weight_layout, **kw)
 
     # ---- host-side sizes
     def default_block_m(self, T: int) -> int:

@@ -62,7 +62,8 @@ class Case:
         return None if self.logits is None else self.logits.cpu().numpy()
 
 
-def build_case(w: synth.Workload, device="cuda", cache_experts: bool = True, keep_masters: bool = True) -> Case:
+def build_case(w: synth.Workload, device="cuda", cache_experts: bool = True, keep_masters: bool = True,
+               weight_layout=None) -> Case:
     import moe_layer_router_amd as mlr
     x = synth.gen_x(w, device)
     logits = synth.gen_logits(w, device)
@@ -70,7 +71,8 @@ def build_case(w: synth.Workload, device="cuda", cache_experts: bool = True, kee
     w13, w2 = synth.gen_masters(w, device)
     layer = mlr.MoELayer.from_masters(w13, w2, w.quant, router_w=router_w, E=w.E, top_k=w.k,
                                       n_shared=w.n_shared, scoring=w.scoring, n_groups=w.n_groups,
-                                      topk_groups=w.topk_groups, route_scale=w.route_scale)
+                                      topk_groups=w.topk_groups, route_scale=w.route_scale,
+                                      weight_layout=weight_layout)
     spec = spec_of(w)
 
     def master(e):

@@ -52,7 +52,7 @@ def test_max_rows_rejects_bad_input():
 
 def _desc(**kw):
     d = dict(D=512, I=256, E=16, top_k=4, n_shared=0, scoring=0, n_groups=1, topk_groups=1, renormalize=1,
-             route_scale=1.0, quant=1, w13=1 << 20, w13_scale=1 << 21, w2=1 << 22, w2_scale=1 << 23,
+             route_scale=1.0, quant=1, weight_layout=1, w13=1 << 20, w13_scale=1 << 21, w2=1 << 22, w2_scale=1 << 23,
              router_w=None, sel_bias=None)
     d.update(kw)
     return L.LayerDesc(**d)
@@ -99,6 +99,15 @@ def test_layer_validation_and_workspace():
         == L.MOE_ERR_INVALID_ARG
     assert lib.moe_forward(ctypes.byref(_desc(quant=7)), None, None, 4, 0, None, None, 0, None) \
         == L.MOE_ERR_INVALID_ARG
+    # weight layouts: blocked needs an FP8 mode; unknown layouts are rejected
+    assert lib.moe_forward_workspace_size(ctypes.byref(_desc(weight_layout=0)), 100, 64) > 0
+    assert lib.moe_forward_workspace_size(ctypes.byref(_desc(quant=0, weight_layout=1, w13_scale=None,
+                                                             w2_scale=None)), 100, 64) == 0
+    assert lib.moe_forward(ctypes.byref(_desc(weight_layout=2)), None, None, 4, 0, None, None, 0, None) \
+        == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quant_weight_fp8(None, 1, 24, 128, 1, 1, None, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quant_weight_fp8(None, 1, 32, 128, 1, 3, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quant_weight_fp8(None, 1, 32, 128, 1, 1, None, None, None) == L.MOE_ERR_INVALID_ARG
     # no logits and no router weight
     assert lib.moe_forward(ctypes.byref(d), 1 << 24, None, 4, 0, 1 << 25, 1 << 26, 1 << 30, None) \
         == L.MOE_ERR_INVALID_ARG
@@ -115,7 +124,7 @@ def test_layer_validation_and_workspace():
 
 def test_workspace_layout_is_disjoint_and_aligned():
     lib = L.lib()
-    for d, T in [(_desc(), 300), (_desc(quant=0, w13_scale=None, w2_scale=None), 64),
+    for d, T in [(_desc(), 300), (_desc(quant=0, weight_layout=0, w13_scale=None, w2_scale=None), 64),
                  (_desc(quant=2, n_shared=1, scoring=1, n_groups=4, topk_groups=2, route_scale=2.5), 77)]:
         lay = L.WsLayout()
         assert lib.moe_workspace_layout(ctypes.byref(d), T, 0, ctypes.byref(lay)) == L.MOE_OK

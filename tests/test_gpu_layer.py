@@ -85,6 +85,23 @@ def test_forward_is_deterministic_and_row_independent():
     assert torch.equal(y1[perm].view(torch.int16), y3.view(torch.int16))
 
 
+@pytest.mark.parametrize("name,block_m", [("qwen3_235b_prefill_ptpc_r", 0), ("qwen3_235b_prefill_ptpc_r", 16),
+                                          ("deepseek_r1_block_fp8_r", 0), ("deepseek_r1_block_fp8_r", 16),
+                                          ("qwen3_30b_a3b_ptpc", 32)])
+def test_row_major_weights_match_blocked(name, block_m):
+    """The same codes stored row-major or in 16-row x 128-byte blocks give
+    bitwise the same layer output (only the addresses differ)."""
+    w = REDUCED[name]
+    say("weight layouts", name, block_m)
+    cb = build_case(w)
+    cr = build_case(w, weight_layout="rows")
+    assert cb.layer.weight_layout == "blocked" and cr.layer.weight_layout == "rows"
+    yb = cb.layer.forward(cb.x, cb.logits, block_m=block_m)
+    yr = cr.layer.forward(cr.x, cr.logits, block_m=block_m)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.int16), yr.view(torch.int16))
+
+
 def test_forward_small_batches_and_empty():
     w = REDUCED["deepseek_r1_block_fp8_r"]
     c = build_case(w)
@@ -158,5 +175,6 @@ def test_full_size_sampled_tokens(name):
     if w.quant != "bf16":
         for e in sorted(set(int(v) for v in ids_ref[toks].reshape(-1)))[:4]:
             q13, s13, q2, s2 = c.bank.quantized(e)
-            assert np.array_equal(c.layer.weights.w13[e].cpu().numpy(), q13)
+            assert c.layer.weight_layout == "blocked"
+            assert np.array_equal(mlr.unblock_weights(c.layer.weights.w13[e]).cpu().numpy(), q13)
             assert np.array_equal(c.layer.weights.w2_scale[e].cpu().numpy().view(np.uint32), s2.view(np.uint32))

@@ -190,15 +190,24 @@ def test_quant_valid_rows_leaves_the_rest():
     assert np.all(q[37:].cpu().numpy() == 0xAB) and np.all(s[37:].cpu().numpy() == -5.0)
 
 
-@pytest.mark.parametrize("quant", ["ptpc_fp8", "block128_fp8"])
-def test_quant_weights(quant):
-    say("quant weights", quant)
+@pytest.mark.parametrize("quant,layout", [("ptpc_fp8", "rows"), ("block128_fp8", "rows"),
+                                          ("ptpc_fp8", "blocked"), ("block128_fp8", "blocked")])
+def test_quant_weights(quant, layout):
+    """Codes and scales bit-exact against the oracle; blocked codes are the
+    row-major ones moved as whole 16-row x 128-byte blocks."""
+    say("quant weights", quant, layout)
     w = synth.get("deepseek_r1_block_fp8").replace(D=1024, I=256, E=3)
     w13, _ = synth.gen_masters(w, "cuda")
     w13[1, :128, :128] *= 1000.0
     w13[2, 128:256, 256:384] = 0.0
-    q, s = mlr.quant_weight_fp8(w13, quant)
+    q, s = mlr.quant_weight_fp8(w13, quant, layout)
     torch.cuda.synchronize()
+    if layout == "blocked":
+        raw = q.cpu().numpy().reshape(-1)
+        n, N, K = w13.shape
+        # block (g, kb) of matrix e is bytes [2048 j, 2048 j + 2048) with j = (e*N/16 + g) * K/128 + kb
+        blocks = raw.reshape(n * N // 16, K // 128, 16, 128)
+        q = torch.from_numpy(np.ascontiguousarray(blocks.transpose(0, 2, 1, 3)).reshape(n, N, K))
     for e in range(3):
         m = synth.bf16_to_f32_np(w13[e])
         rq, rs = O.quant_rows(m) if quant == "ptpc_fp8" else O.quant_weight_blocks(m)
