@@ -349,13 +349,13 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
 #pragma unroll
                 for (int tm = 0; tm < TA; ++tm) {
                     const float a = s_ascale[buf][arow + tm * 32 + r32];
-                    ra[tm] = pa[tm] / a;
+                    ra[tm] = pa[tm] * __builtin_amdgcn_rcpf(a);   // ratio to 1 ulp; the chain stays ~1e-6
                     pa[tm] = a;
                 }
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
                     const float w = s_wscale[wn * TN + tn][kb];
-                    rw[tn] = pw[tn] / w;
+                    rw[tn] = pw[tn] * __builtin_amdgcn_rcpf(w);
                     pw[tn] = w;
                 }
             }
