@@ -306,7 +306,16 @@ def main():
     dn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
     log(f"step {ms:.3f} ms (step entries {steps_ms:.3f} ms)  gate_up {gu_ms:.3f} ms  down {dn_ms:.3f} ms")
     same = bool(torch.equal(y_fused.view(torch.int16), st.y.view(torch.int16)))
-    ids = case.layer.intermediates(w.T, args.block_m, ws)["topk_ids"].cpu().numpy()
+    inter = case.layer.intermediates(w.T, args.block_m, ws)
+    ids = inter["topk_ids"].cpu().numpy()
+    counts = inter["counts"].cpu().numpy()
+    routed = counts[:w.E]
+    # expert load of the batch (the gating load the pages monitor) and the
+    # rows the grouped GEMMs run after padding and 32-row pad-tile skipping
+    load = {"active_experts": int((routed > 0).sum()), "rows_per_expert_mean": round(float(routed.mean()), 1),
+            "rows_per_expert_max": int(routed.max()), "rows_per_expert_min": int(routed.min()),
+            "padded_rows": int(inter["offsets"][-1].item()),
+            "computed_rows": int((-(-counts // 32) * 32).sum()) if st.B > 16 else int(counts.sum())}
 
     rows = w.T * (w.k + w.n_shared)
     flops = w.flops()
@@ -342,6 +351,7 @@ def main():
         "layer": {"tflops": round(tflops, 1), "frac_mfma": round(tflops / peak, 4), "algorithmic_bytes": int(layer_bytes),
                   "GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
                   "frac_hbm": round(layer_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "routing": load,
         "step_entries_ms_per_step": round(steps_ms, 4), "step_entries_equal_fused": same,
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
     }
