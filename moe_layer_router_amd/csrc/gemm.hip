@@ -37,7 +37,7 @@
 //
 // Pad rows read a real row and are zeroed by a row mask in the epilogue;
 // 32-row tiles made only of pads (known from the expert's row count) get no
-// operand reads and no MFMAs.
+// operand reads and no MFMAs, and with two stages no activation copies.
 // Tiles are ordered expert by expert, weight tile by weight tile, row block
 // fastest, and each XCD (workgroup id mod 8) takes a contiguous range of
 // that order, so the row blocks of one expert that share a weight tile run
@@ -253,6 +253,19 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         b_src[j] = static_cast<uint32_t>(p.w_blocked ? (wr >> 4) * (wrow_bytes / kRow) * 2048 + (wr & 15) * kRow + c * 16
                                                      : wr * wrow_bytes + c * 16);
     }
+    // With two stages every in-loop wait is for all outstanding copies, so a
+    // wave may leave out the copies of its 8-row groups that lie in 32-row
+    // tiles made only of pads (no MFMA reads them); only the prologue's wait
+    // depends on how many copies a step issues.
+    constexpr bool SKIP_DEAD = NS == 2;
+    const int live32 = min(BM, (live + 31) & ~31);
+    bool a_need[A_IN];
+    int n_dead = 0;
+#pragma unroll
+    for (int j = 0; j < A_IN; ++j) {
+        a_need[j] = __builtin_amdgcn_readfirstlane((wave + NW * j) * 8 < live32 ? 1 : 0) != 0;
+        n_dead += a_need[j] ? 0 : 1;
+    }
     // blockwise: wave w copies the scales of rows 64w .. 64w+63 (rows past BM
     // read row 0 into unused slots)
     const float* sc_src = nullptr;
@@ -271,7 +284,8 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         const int64_t kw = static_cast<int64_t>(S) * (p.w_blocked ? 2048 : kRow);   // step offset in the weights
         const uint32_t st = lds0 + buf * STAGE;
         if constexpr (d < A_IN) {
-            dma16(a_src[d], p.a + ko, __builtin_amdgcn_readfirstlane(st + (wave + NW * d) * 8 * kRow));
+            if (!SKIP_DEAD || a_need[d])
+                dma16(a_src[d], p.a + ko, __builtin_amdgcn_readfirstlane(st + (wave + NW * d) * 8 * kRow));
         } else if constexpr (d < A_IN + B_IN) {
             constexpr int j = d - A_IN;
             dma16(b_src[j], wexp + kw, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
@@ -307,7 +321,9 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
 
     // Row tiles of this wave that hold at least one routed row: 32-row tiles
     // made only of pads get no operand reads and no MFMAs (their
-    // accumulators stay 0).  The wave still issues its share of the copies.
+    // accumulators stay 0).  The wave still issues its share of the weight
+    // copies (other waves read them), and of the activation copies unless
+    // SKIP_DEAD leaves out those of pad-only tiles.
     const int ta = __builtin_amdgcn_readfirstlane(min(TM, max(0, (live - arow + 31) >> 5)));
 
     // The main loop for TA live row tiles (TA is uniform over the tile's K
@@ -421,8 +437,18 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         // step 0, then read the fragments of its first half.
         for (int S = 0; S < NS; ++S)
             if (S < nbig) issue(S);
-        if (NS <= nbig) vmcnt_wait<(NS - 1) * N_BIG>();
-        else vmcnt_wait<0>();
+        if (NS <= nbig) {
+            // wait for step 0; the copies of steps 1 .. NS-1 may stay in flight
+            if constexpr (SKIP_DEAD) {
+                static_for<A_IN + 1>([&](auto Dc) {
+                    if (n_dead == decltype(Dc)::value) vmcnt_wait<(NS - 1) * (N_BIG - decltype(Dc)::value)>();
+                });
+            } else {
+                vmcnt_wait<(NS - 1) * N_BIG>();
+            }
+        } else {
+            vmcnt_wait<0>();
+        }
         __syncthreads();
         static_for<NL>([&](auto L) { load_one(std::integral_constant<int, 0>{}, L, 0, 0); });
         if constexpr (BLOCKQ) {
