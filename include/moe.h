@@ -92,10 +92,12 @@ extern "C" {
  *   weight_layout: order of the bytes of each [N, K] weight matrix (w13:
  *              N = 2I, K = D; w2: N = D, K = I):
  *              MOE_WEIGHTS_ROWS    row-major, K contiguous;
- *              MOE_WEIGHTS_BLOCKED blocks of 16 rows x 128 bytes, the byte
- *              (n, b) of a row at ((n/16) * (K_bytes/128) + b/128) * 2048 +
- *              (n%16) * 128 + b%128 -- the unit the expert GEMMs read per
- *              step, contiguous in memory.  FP8 modes only (N % 16 == 0 and
+ *              MOE_WEIGHTS_BLOCKED blocks of 16 rows x 128 bytes (the unit
+ *              the expert GEMMs read per step), the byte (n, b) of a row at
+ *              ((n/16) * (K_bytes/128) + b/128) * 2048 + o(n%16, b%128)
+ *              with o(r, c) = (r/2 + 8 * (c/64)) * 128 +
+ *              ((r%2) * 4 + (c%64)/16) * 16 + c%16: each 128-byte line of
+ *              a block holds one 64-byte K half of two consecutive rows.  FP8 modes only (N % 16 == 0 and
  *              K a multiple of 128 there); moe_quant_weight_fp8 writes it.
  *   router_w: [E, D] fp32 router gate, used by moe_forward when it is given
  *             no logits (may be NULL otherwise).

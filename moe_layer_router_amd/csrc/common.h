@@ -76,6 +76,18 @@ __device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Blocked FP8 weights (MOE_WEIGHTS_BLOCKED): a [N, K] code matrix is stored
+// as blocks of 16 rows x 128 bytes (one K step of the expert GEMMs), block
+// (n / 16, b / 128) at ((n / 16) * (K / 128) + b / 128) * 2048.  Inside a
+// block, each 128-byte line holds one 64-byte K half of two consecutive
+// rows: byte (r, b) at line (r / 2) + 8 * (b / 64), 16-byte piece
+// (r % 2) * 4 + (b % 64) / 16.  The prefill GEMM's copy of 8 rows x 128
+// bytes and the decode GEMM's load of 16 rows x 4 pieces (one MFMA operand
+// half) then both read 8 whole lines.
+__host__ __device__ constexpr int blocked_byte(int r, int b) {
+    return ((r >> 1) + 8 * (b >> 6)) * 128 + ((r & 1) * 4 + ((b >> 4) & 3)) * 16 + (b & 15);
+}
+
 }  // namespace moe
 
 // ---------------------------------------------------------------- host side

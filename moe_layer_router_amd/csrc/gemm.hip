@@ -248,9 +248,9 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         const int c = cphys ^ (((BM + t) >> 1) & 7);
         const int w = t / WCOLS, jj = t % WCOLS;
         const int wr = GATEUP ? (jj < HALF ? n0 + w * HALF + jj : p.I + n0 + w * HALF + jj - HALF) : n0 + t;
-        // blocked weights: the 8 rows of a copy are half of one contiguous
-        // 2 KB block (16 rows x one 128-byte step)
-        b_src[j] = static_cast<uint32_t>(p.w_blocked ? (wr >> 4) * (wrow_bytes / kRow) * 2048 + (wr & 15) * kRow + c * 16
+        // blocked weights: the 8 rows of a copy are half of one 2 KB block
+        // (16 rows x one 128-byte step), 8 whole lines of it
+        b_src[j] = static_cast<uint32_t>(p.w_blocked ? (wr >> 4) * (wrow_bytes / kRow) * 2048 + blocked_byte(wr & 15, c * 16)
                                                      : wr * wrow_bytes + c * 16);
     }
     // With two stages every in-loop wait is for all outstanding copies, so a

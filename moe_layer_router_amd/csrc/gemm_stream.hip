@@ -68,12 +68,13 @@ __device__ __forceinline__ void mfma16(const u32x8& a, const u32x8& b, v4f& acc)
 }
 
 // A lane's 32 operand bytes of one 128-byte K step: bytes [16q, 16q+16) and
-// [64+16q, 64+16q+16) with q = lane / 16, so each of the two load
-// instructions covers 64 contiguous bytes of every row it touches.  Activation
-// and weight operands use the same mapping, so the MFMA pairs matching K.
-__device__ __forceinline__ u32x8 ld32(const uint8_t* p) {
+// [64+16q, 64+16q+16) of its row, q = lane / 16; the second piece is HI
+// bytes after the first (64 in a row-major row; 1024 in a blocked weight
+// block, where each of the two loads then reads 8 whole lines).  Activation
+// and weight operands use the same K mapping, so the MFMA pairs matching K.
+__device__ __forceinline__ u32x8 ld32(const uint8_t* p, int hi_off) {
     const u32x4_s lo = *reinterpret_cast<const u32x4_s*>(p);
-    const u32x4_s hi = *reinterpret_cast<const u32x4_s*>(p + 64);
+    const u32x4_s hi = *reinterpret_cast<const u32x4_s*>(p + hi_off);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -111,7 +112,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
         wn0[t] = GATEUP ? (t < TN / 2 ? c0 + t * 16 : p.I + c0 + (t - TN / 2) * 16) : c0 + t * 16;
         // blocked weights: a tile's 16 rows x 128 bytes of one step are one
         // contiguous 2 KB block
-        bp[t] = p.w_blocked ? wexp + static_cast<int64_t>(wn0[t] >> 4) * (wrow / 128) * 2048 + r16 * 128 + kq
+        bp[t] = p.w_blocked ? wexp + static_cast<int64_t>(wn0[t] >> 4) * (wrow / 128) * 2048 + blocked_byte(r16, kq)
                             : wexp + (wn0[t] + r16) * wrow + kq;
     }
     // operand rows: row r16 of each M tile; rows past the segment or on a pad
@@ -145,6 +146,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
         for (int t = 0; t < TN; ++t) acc[m][t] = v4f{0, 0, 0, 0};
 
     const int nk = static_cast<int>(wrow / 128);
+    const int whi = p.w_blocked ? blocked_byte(0, 64) - blocked_byte(0, 0) : 64;   // second operand piece
     // Each item starts its K sweep at its own step (wrapping around), so the
     // waves spread over the byte offsets of the weight rows.  The K order is
     // fixed by the item (expert, slice): results stay deterministic.
@@ -158,9 +160,9 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
         const int64_t ko = static_cast<int64_t>(ks) * 128;
         const int64_t kw = static_cast<int64_t>(ks) * (p.w_blocked ? 2048 : 128);   // step offset in the weights
 #pragma unroll
-        for (int t = 0; t < TN; ++t) bq[j][t] = ld32(bp[t] + kw);
+        for (int t = 0; t < TN; ++t) bq[j][t] = ld32(bp[t] + kw, whi);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) aqr[j][m] = ld32(ap[m] + ko);
+        for (int m = 0; m < MT; ++m) aqr[j][m] = ld32(ap[m] + ko, 64);
         if constexpr (BLOCKQ) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)

@@ -66,11 +66,11 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
 }
 
 // Byte offset of code (row, k) of a [rows, K] code matrix: row-major, or in
-// blocks of 16 rows x 128 bytes (the order the expert GEMMs read; 8-byte
-// pieces at k % 8 == 0 never straddle a block).
+// blocks of 16 rows x 128 bytes (blocked_byte; 8-byte pieces at k % 8 == 0
+// never straddle a 16-byte piece).
 __device__ __forceinline__ int64_t code_off(int64_t row, int k, int K, bool blocked) {
     if (!blocked) return row * K + k;
-    return ((row >> 4) * (K >> 7) + (k >> 7)) * 2048 + (row & 15) * 128 + (k & 127);
+    return ((row >> 4) * (K >> 7) + (k >> 7)) * 2048 + blocked_byte(static_cast<int>(row & 15), k & 127);
 }
 
 // Weight rows [M, K] (PTPC: one scale per row), one wave per row, codes in

@@ -114,10 +114,15 @@ def quant_weight_fp8(w: torch.Tensor, quant: str, layout: str = "blocked"):
 
 
 def unblock_weights(q: torch.Tensor) -> torch.Tensor:
-    """Row-major view (a copy) of codes [..., N, K] stored in 16-row x
-    128-byte blocks."""
+    """Row-major copy of codes [..., N, K] stored in 16-row x 128-byte blocks
+    (inside a block: K half h, line l, row parity p, 16-byte piece c, byte
+    -> row 2l + p, byte 64h + 16c + byte)."""
     *lead, N, K = q.shape
-    return q.reshape(*lead, N // 16, K // 128, 16, 128).transpose(-3, -2).reshape(*lead, N, K)
+    b = q.reshape(*lead, N // 16, K // 128, 2, 8, 2, 4, 16)
+    nd = b.dim()
+    # [.., g, kb, h, l, p, c, x] -> [.., g, l, p, kb, h, c, x]
+    perm = list(range(nd - 7)) + [nd - 7, nd - 4, nd - 3, nd - 6, nd - 5, nd - 2, nd - 1]
+    return b.permute(*perm).reshape(*lead, N, K)
 
 
 # ---------------------------------------------------------------- the layer

@@ -133,3 +133,26 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert len(set(offs)) == len(offs)
         assert lay.total == lib.moe_forward_workspace_size(ctypes.byref(d), T, 0)
         assert lay.max_rows == O.permute_max_rows(T, d.top_k, d.E, d.n_shared, lay.block_m)
+
+
+def test_unblock_weights_inverts_the_blocked_byte_order():
+    """unblock_weights (host side) undoes the blocked code layout the header
+    documents: blocks of 16 rows x 128 bytes, each line holding one 64-byte
+    K half of two consecutive rows."""
+    torch = pytest.importorskip("torch")
+    from moe_layer_router_amd import unblock_weights
+    rng = np.random.default_rng(5)
+    n, N, K = 2, 48, 384
+    rowmajor = rng.integers(0, 256, size=(n, N, K), dtype=np.uint8)
+    blocked = np.zeros(n * N * K, np.uint8)
+    for e in range(n):
+        for r in range(N):
+            for k in range(K):
+                r16, c = r % 16, k % 128
+                j = (e * (N // 16) + r // 16) * (K // 128) + k // 128
+                o = (r16 // 2 + 8 * (c // 64)) * 128 + ((r16 % 2) * 4 + (c % 64) // 16) * 16 + c % 16
+                blocked[j * 2048 + o] = rowmajor[e, r, k]
+    got = unblock_weights(torch.from_numpy(blocked.reshape(n, N, K)))
+    assert np.array_equal(got.numpy(), rowmajor)
+    # the first line of a block holds bytes 0..63 of rows 0 and 1
+    assert np.array_equal(blocked[:64], rowmajor[0, 0, :64]) and np.array_equal(blocked[64:128], rowmajor[0, 1, :64])

@@ -205,9 +205,16 @@ def test_quant_weights(quant, layout):
     if layout == "blocked":
         raw = q.cpu().numpy().reshape(-1)
         n, N, K = w13.shape
-        # block (g, kb) of matrix e is bytes [2048 j, 2048 j + 2048) with j = (e*N/16 + g) * K/128 + kb
-        blocks = raw.reshape(n * N // 16, K // 128, 16, 128)
-        q = torch.from_numpy(np.ascontiguousarray(blocks.transpose(0, 2, 1, 3)).reshape(n, N, K))
+        # the documented byte order: block (g, kb) of matrix e starts at byte
+        # 2048 j, j = (e*N/16 + g) * K/128 + kb; inside it code (r, c) sits at
+        # (r//2 + 8*(c//64))*128 + ((r%2)*4 + (c%64)//16)*16 + c%16
+        e_, r_, k_ = np.meshgrid(np.arange(n), np.arange(N), np.arange(K), indexing="ij")
+        r16, c = r_ % 16, k_ % 128
+        pos = (((e_ * (N // 16) + r_ // 16) * (K // 128) + k_ // 128) * 2048
+               + (r16 // 2 + 8 * (c // 64)) * 128 + ((r16 % 2) * 4 + (c % 64) // 16) * 16 + c % 16)
+        rowmajor = torch.from_numpy(raw[pos])
+        assert torch.equal(mlr.unblock_weights(q).cpu(), rowmajor)
+        q = rowmajor
     for e in range(3):
         m = synth.bf16_to_f32_np(w13[e])
         rq, rs = O.quant_rows(m) if quant == "ptpc_fp8" else O.quant_weight_blocks(m)
