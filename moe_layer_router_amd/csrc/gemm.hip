@@ -204,11 +204,19 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     // rows of the block that hold routed rows (the expert's pads follow them)
     const int live = p.counts ? min(BM, max(0, p.offsets[e] + p.counts[e] - m0)) : BM;
 
+    // Row tokens go to LDS before the copies can start.  The PTPC row and
+    // channel scales are only needed by the epilogue: their loads go out
+    // here but land in LDS after the main loop, so the copies do not wait
+    // for them.
+    constexpr bool PTPC = MODE == MOE_QUANT_PTPC_FP8;
+    constexpr int CHN = PTPC ? (GATEUP ? 2 : 1) * TILE_N : 0;    // channel scales of the tile
+    constexpr int CH_PER = (CHN + NT - 1) / NT;
+    float rs = 0.0f, rsv = 0.0f, chv[CH_PER > 0 ? CH_PER : 1];
     if (tid < BM) {
         // rows past `live` are pads: down reads the block's first row for
         // them (no HBM traffic for pad rows) and masks them out
         int tok = tid < live ? m0 + tid : m0;
-        float rs = tid < live ? 1.0f : 0.0f;
+        rs = tid < live ? 1.0f : 0.0f;
         if (p.sorted_ids) {
             const int f = p.sorted_ids[m0 + tid];
             const bool pad = f == p.sentinel;
@@ -216,14 +224,28 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
             rs = pad ? 0.0f : 1.0f;
         }
         s_tok[tid] = tok;
-        if constexpr (MODE == MOE_QUANT_PTPC_FP8) rs = rs == 0.0f ? 0.0f : p.a_scale[tok];
-        s_rowscale[tid] = rs;
+        if constexpr (PTPC) rsv = p.a_scale[tok];
+        else s_rowscale[tid] = rs;
     }
-    if constexpr (MODE == MOE_QUANT_PTPC_FP8) {
+    if constexpr (PTPC) {
         const float* ws = p.w_scale + e * p.ws_expert;
-        for (int i = tid; i < (GATEUP ? 2 : 1) * TILE_N; i += NT)
-            s_chs[i] = ws[i < TILE_N ? n0 + i : p.I + n0 + i - TILE_N];
+#pragma unroll
+        for (int j = 0; j < CH_PER; ++j) {
+            const int i = tid + j * NT;
+            chv[j] = i < CHN ? ws[i < TILE_N ? n0 + i : p.I + n0 + i - TILE_N] : 0.0f;
+        }
     }
+    auto publish_scales = [&]() __attribute__((always_inline)) {
+        if constexpr (PTPC) {
+            // (the empty asm keeps the compiler from applying the row mask,
+            // and so waiting for the load, back where the load is issued)
+            asm volatile("" : "+v"(rsv));
+            if (tid < BM) s_rowscale[tid] = rs == 0.0f ? 0.0f : rsv;
+#pragma unroll
+            for (int j = 0; j < CH_PER; ++j)
+                if (tid + j * NT < CHN) s_chs[tid + j * NT] = chv[j];
+        }
+    };
     __syncthreads();
 
     // Copy j of a wave fills 8 LDS rows of block wave + NW*j: lane i writes
@@ -524,6 +546,7 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         constexpr int LPR = RB / 16;                          // lanes per row on the way out
         constexpr int RPI = 64 / LPR;                         // rows per store instruction
         static_assert(64 % LPR == 0 && 32 % RPI == 0 && NW * 32 * RBP <= NS * STAGE, "epilogue layout");
+        publish_scales();
         __syncthreads();
         uint8_t* reg = lds + wave * 32 * RBP;
         const int ldb = static_cast<int>(p.out_ld) * OBYTES;          // bytes per output row
