@@ -1,9 +1,9 @@
 """Layer shapes and seeded input draws.
 
-Five layer shapes stand in for the serving workloads the pages discuss
-(Qwen3-30B-A3B and Qwen3-235B-A22B MoE layers with PTPC-FP8, and the
-DeepSeek-R1 MoE layer with blockwise FP8, hidden 7168 and top-8 routing),
-plus a tiny bf16 layer.  No dataset or trained weight is used: every tensor is
+Layer shapes that stand in for the serving workloads the pages discuss
+(Qwen3-30B-A3B and Qwen3-235B-A22B MoE layers with PTPC-FP8, the
+DeepSeek-R1 MoE layer with blockwise FP8, hidden 7168 and top-8 routing, and
+a 512-expert top-10 layer with a shared expert), plus a tiny bf16 layer.  No dataset or trained weight is used: every tensor is
 a seeded draw from ``torch.Generator`` on the device the caller names, so the
 HIP path and the oracle see the same values (the GPU-side tests copy what the
 oracle needs back to the host).
@@ -91,6 +91,11 @@ WORKLOADS = {
         Workload("deepseek_r1_block_fp8", 5, T=4096, D=7168, E=256, k=8, I=2048,
                  quant="block128_fp8", scoring="sigmoid_grouped", n_groups=8,
                  topk_groups=4, route_scale=2.5, n_shared=1),
+        # 512 small experts, top-10 (a k that is not a power of two) plus one
+        # always-on shared expert: the expert layout of the Qwen 3.5 TPU
+        # page, at an 8192-token prefill (81,920 routed rows)
+        Workload("e512_top10_shared_ptpc", 6, T=8192, D=4096, E=512, k=10, I=1024,
+                 quant="ptpc_fp8", n_shared=1, logit_recipe="normal"),
     ]
 }
 

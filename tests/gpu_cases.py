@@ -30,6 +30,8 @@ REDUCED = {
     # weight rows that do not split into 4 x 128 per wave column (2I = 768,
     # D = 1280): the PTPC kernels fall back to 64-row wave tiles
     "qwen3_30b_a3b_ptpc_i384": synth.get("qwen3_30b_a3b_ptpc").replace(T=200, D=1280, I=384, E=16),
+    # 512-expert top-10 layer with a shared expert, reduced: top-10 of 64
+    "e512_top10_shared_r": synth.get("e512_top10_shared_ptpc").replace(T=500, D=1024, I=256, E=64),
 }
 
 

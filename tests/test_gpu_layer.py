@@ -51,7 +51,8 @@ def _check_exact(inter, ref, quant):
                                           ("deepseek_r1_block_fp8_small", 0),
                                           ("qwen3_235b_decode_ptpc_t64", 0), ("qwen3_235b_decode_ptpc", 32),
                                           ("bf16_small_t20", 0), ("qwen3_235b_prefill_ptpc_r", 16),
-                                          ("deepseek_r1_block_fp8_r", 16)])
+                                          ("deepseek_r1_block_fp8_r", 16), ("e512_top10_shared_r", 0),
+                                          ("e512_top10_shared_r", 128), ("e512_top10_shared_r", 16)])
 def test_forward_matches_oracle(name, block_m):
     w = REDUCED[name]
     say("forward", name, block_m)
@@ -138,7 +139,7 @@ def test_forward_zero_tokens_rows_and_one_hot_routing():
 # --------------------------------------------------------------- full sizes
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "qwen3_30b_a3b_ptpc", "qwen3_235b_prefill_ptpc",
-                                  "qwen3_235b_decode_ptpc", "deepseek_r1_block_fp8"])
+                                  "qwen3_235b_decode_ptpc", "deepseek_r1_block_fp8", "e512_top10_shared_ptpc"])
 def test_full_size_sampled_tokens(name):
     """The full workload in the launch configuration the bench times: routing,
     permutation and x codes compared whole; y on sampled tokens, which the
