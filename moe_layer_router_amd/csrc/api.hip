@@ -15,7 +15,7 @@ int32_t permute_align_launch(const int* ids, int T, int k, int E, int n_shared, 
 int32_t quant_wrows_launch(const uint16_t* w, int64_t M, int K, bool blocked, uint8_t* q, float* scale,
                            hipStream_t s);
 int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const int* valid_rows, uint8_t* q,
-                          float* scale, hipStream_t s);
+                          float* scale, hipStream_t s, bool blocked = false);
 int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, bool blocked, uint8_t* q, float* scale,
                             hipStream_t s);
 bool front_small_ok(int T, int k, int n_shared);
@@ -29,7 +29,7 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
                            const int* counts, void* act, hipStream_t s);
 int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T, int block_m,
                          int64_t max_rows, const int* block_expert, const int* offsets, const int* counts,
-                         void* out_perm, hipStream_t s);
+                         void* out_perm, hipStream_t s, bool act_blocked = false);
 int32_t combine_launch(const void* out_perm, int out_dtype, const int* inv_perm, const float* topk_w, int T,
                        int k, int n_shared, int D, uint16_t* y, hipStream_t s);
 }  // namespace moe
@@ -361,16 +361,21 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
         return st;
     const void* act_in = act;
     const float* act_scale = nullptr;
+    // the streaming down GEMM reads act codes stored in 16-row x 128-byte
+    // blocks (whole lines per load, as for the weights); max_rows is a
+    // multiple of 16 there
+    const bool aq_blocked = fp8 && block_m == 16;
     if (fp8) {
         if ((st = quant_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, group, offsets + Ep,
-                                    static_cast<uint8_t*>(at(o.aq)), static_cast<float*>(at(o.as)), s)) != MOE_OK)
+                                    static_cast<uint8_t*>(at(o.aq)), static_cast<float*>(at(o.as)), s, aq_blocked)) !=
+            MOE_OK)
             return st;
         act_in = at(o.aq);
         act_scale = static_cast<float*>(at(o.as));
     }
     void* outp = at(o.out_perm);
-    if ((st = gemm_down_launch(L, act_in, act_scale, T, block_m, o.max_rows, bexp, offsets, counts, outp, s)) !=
-        MOE_OK)
+    if ((st = gemm_down_launch(L, act_in, act_scale, T, block_m, o.max_rows, bexp, offsets, counts, outp, s,
+                               aq_blocked)) != MOE_OK)
         return st;
     return combine_launch(outp, fp8 ? 1 : 0, inv, w, T, k, L->n_shared, L->D, static_cast<uint16_t*>(y_bf16), s);
 }

@@ -661,7 +661,7 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
                              const int* sorted_ids, const int* offsets, const int* counts, void* act,
                              hipStream_t s);
 int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T,
-                           const int* offsets, const int* counts, void* out_perm, hipStream_t s);
+                           const int* offsets, const int* counts, void* out_perm, hipStream_t s, bool act_blocked);
 
 int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T, int block_m,
                            int64_t max_rows, const int* sorted_ids, const int* block_expert, const int* offsets,
@@ -703,8 +703,9 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
 
 int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T, int block_m,
                          int64_t max_rows, const int* block_expert, const int* offsets, const int* counts,
-                         void* out_perm, hipStream_t s) {
-    if (block_m == 16) return stream_down_launch(L, act, act_scale, T, offsets, counts, out_perm, s);
+                         void* out_perm, hipStream_t s, bool act_blocked) {
+    if (block_m == 16) return stream_down_launch(L, act, act_scale, T, offsets, counts, out_perm, s, act_blocked);
+    if (act_blocked) return MOE_ERR_UNSUPPORTED;   // only the streaming kernel reads blocked act codes
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     if (max_rows * L->I * elem >= (1LL << 32) || static_cast<int64_t>(L->D) * L->I * elem >= (1LL << 32))
         return MOE_ERR_UNSUPPORTED;

@@ -32,6 +32,7 @@ typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
 struct StreamArgs {
     const uint8_t* a;          // gate_up: x / xq [T, K]; down: act / aq [R, K]
     int64_t a_ld;              // bytes per row
+    int a_blocked;             // down: act codes in 16-row x 128-byte blocks (R a multiple of 16)
     const float* a_scale;      // PTPC: per row; block: [rows, K/128]
     int a_scale_ld;
     const int* sorted_ids;     // gate_up: flat ids; down: NULL (rows direct)
@@ -123,7 +124,9 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
         const int r = m * 16 + r16;
         bool v = false;
         const int src = r < cnt ? src_row(p, GATEUP, row0 + r, v) : 0;
-        ap[m] = p.a + static_cast<int64_t>(v ? src : (GATEUP ? 0 : row0)) * p.a_ld + kq;
+        const int64_t ar = v ? src : (GATEUP ? 0 : row0);
+        ap[m] = p.a_blocked ? p.a + (ar >> 4) * (p.a_ld / 128) * 2048 + blocked_byte(static_cast<int>(ar & 15), kq)
+                            : p.a + ar * p.a_ld + kq;
     }
     // accumulator rows: (lane / 16) * 4 + i of each tile
     int esrc[MT][4];
@@ -147,6 +150,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
 
     const int nk = static_cast<int>(wrow / 128);
     const int whi = p.w_blocked ? blocked_byte(0, 64) - blocked_byte(0, 0) : 64;   // second operand piece
+    const int ahi = p.a_blocked ? blocked_byte(0, 64) - blocked_byte(0, 0) : 64;
     // Each item starts its K sweep at its own step (wrapping around), so the
     // waves spread over the byte offsets of the weight rows.  The K order is
     // fixed by the item (expert, slice): results stay deterministic.
@@ -157,12 +161,12 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
     auto fill = [&](int j, int s) {
         int ks = s + kbeg;
         ks = ks >= nk ? ks - nk : ks;
-        const int64_t ko = static_cast<int64_t>(ks) * 128;
+        const int64_t ko = static_cast<int64_t>(ks) * (p.a_blocked ? 2048 : 128);   // step offset in the rows
         const int64_t kw = static_cast<int64_t>(ks) * (p.w_blocked ? 2048 : 128);   // step offset in the weights
 #pragma unroll
         for (int t = 0; t < TN; ++t) bq[j][t] = ld32(bp[t] + kw, whi);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) aqr[j][m] = ld32(ap[m] + ko, 64);
+        for (int m = 0; m < MT; ++m) aqr[j][m] = ld32(ap[m] + ko, ahi);
         if constexpr (BLOCKQ) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -390,11 +394,12 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
 }
 
 int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T,
-                           const int* offsets, const int* counts, void* out_perm, hipStream_t s) {
+                           const int* offsets, const int* counts, void* out_perm, hipStream_t s, bool act_blocked) {
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     StreamArgs g{};
     g.a = static_cast<const uint8_t*>(act);
     g.a_ld = static_cast<int64_t>(L->I) * elem;
+    g.a_blocked = act_blocked && elem == 1;
     g.a_scale = act_scale;
     g.a_scale_ld = L->I / 128;
     g.sorted_ids = nullptr;

@@ -14,10 +14,19 @@
 
 namespace moe {
 
+// Byte offset of code (row, k) of a [rows, K] code matrix: row-major, or in
+// blocks of 16 rows x 128 bytes (blocked_byte; 8-byte pieces at k % 8 == 0
+// never straddle a 16-byte piece).
+__device__ __forceinline__ int64_t code_off(int64_t row, int k, int K, bool blocked) {
+    if (!blocked) return row * K + k;
+    return ((row >> 4) * (K >> 7) + (k >> 7)) * 2048 + blocked_byte(static_cast<int>(row & 15), k & 127);
+}
+
 // NV: vectors of 8 per lane (K = 512 * NV at most).  GROUP: 0 (row) or 128.
+// Codes row-major, or (BLOCKED, rows a multiple of 16) in the blocked order.
 template <int NV, int GROUP>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
-                                                         const int* __restrict__ valid_rows,
+                                                         const int* __restrict__ valid_rows, bool blocked,
                                                          uint8_t* __restrict__ q, float* __restrict__ scale) {
     const int lane = threadIdx.x & 63;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -31,7 +40,7 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
         const int c = lane + 64 * i;
         if (c < nvec) v[i] = ld_once(xr + c);
     }
-    uint2* qr = reinterpret_cast<uint2*>(q + row * K);
+    auto put = [&](int c, uint2 v) { *reinterpret_cast<uint2*>(q + code_off(row, 8 * c, K, blocked)) = v; };
     if (GROUP == 0) {
         float m = 0.0f;
 #pragma unroll
@@ -43,7 +52,7 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int c = lane + 64 * i;
-            if (c < nvec) qr[c] = quant8(v[i], inv);
+            if (c < nvec) put(c, quant8(v[i], inv));
         }
         if (lane == 0) scale[row] = sc;
     } else {
@@ -58,19 +67,11 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
             float sc, inv;
             scale_pair(m, sc, inv);
             if (c < nvec) {
-                qr[c] = quant8(v[i], inv);
+                put(c, quant8(v[i], inv));
                 if ((lane & 15) == 0) scale[row * ngroups + (c >> 4)] = sc;
             }
         }
     }
-}
-
-// Byte offset of code (row, k) of a [rows, K] code matrix: row-major, or in
-// blocks of 16 rows x 128 bytes (blocked_byte; 8-byte pieces at k % 8 == 0
-// never straddle a 16-byte piece).
-__device__ __forceinline__ int64_t code_off(int64_t row, int k, int K, bool blocked) {
-    if (!blocked) return row * K + k;
-    return ((row >> 4) * (K >> 7) + (k >> 7)) * 2048 + blocked_byte(static_cast<int>(row & 15), k & 127);
 }
 
 // Weight rows [M, K] (PTPC: one scale per row), one wave per row, codes in
@@ -140,23 +141,23 @@ __global__ void __launch_bounds__(256) quant_wblock_kernel(const uint16_t* __res
 
 template <int GROUP>
 static void launch_rows(int nv, dim3 g, hipStream_t s, const uint16_t* x, int64_t M, int K, const int* valid,
-                        uint8_t* q, float* sc) {
+                        bool blocked, uint8_t* q, float* sc) {
     const dim3 b(256);
-    if (nv <= 1) hipLaunchKernelGGL((quant_rows_kernel<1, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
-    else if (nv <= 2) hipLaunchKernelGGL((quant_rows_kernel<2, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
-    else if (nv <= 4) hipLaunchKernelGGL((quant_rows_kernel<4, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
-    else if (nv <= 8) hipLaunchKernelGGL((quant_rows_kernel<8, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
-    else if (nv <= 16) hipLaunchKernelGGL((quant_rows_kernel<16, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
-    else hipLaunchKernelGGL((quant_rows_kernel<32, GROUP>), g, b, 0, s, x, M, K, valid, q, sc);
+    if (nv <= 1) hipLaunchKernelGGL((quant_rows_kernel<1, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
+    else if (nv <= 2) hipLaunchKernelGGL((quant_rows_kernel<2, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
+    else if (nv <= 4) hipLaunchKernelGGL((quant_rows_kernel<4, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
+    else if (nv <= 8) hipLaunchKernelGGL((quant_rows_kernel<8, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
+    else if (nv <= 16) hipLaunchKernelGGL((quant_rows_kernel<16, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
+    else hipLaunchKernelGGL((quant_rows_kernel<32, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
 }
 
 int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const int* valid_rows, uint8_t* q,
-                          float* scale, hipStream_t s) {
+                          float* scale, hipStream_t s, bool blocked) {
     if (M == 0) return MOE_OK;
     const int nv = static_cast<int>(ceil_div(K / 8, 64));
     const dim3 g(static_cast<unsigned>(ceil_div(M, 4)));
-    if (group == 0) launch_rows<0>(nv, g, s, x, M, K, valid_rows, q, scale);
-    else launch_rows<128>(nv, g, s, x, M, K, valid_rows, q, scale);
+    if (group == 0) launch_rows<0>(nv, g, s, x, M, K, valid_rows, blocked, q, scale);
+    else launch_rows<128>(nv, g, s, x, M, K, valid_rows, blocked, q, scale);
     return moe_launch_status();
 }
 

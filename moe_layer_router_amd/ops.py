@@ -261,7 +261,10 @@ class MoELayer:
         if self.quant != "bf16":
             out["xq"] = view("xq", T * D, _U8, (T, D))
             out["xs"] = view("xs", T * (D // 128 if blk else 1), _F32, (T, D // 128) if blk else (T,))
-            out["aq"] = view("aq", R * I, _U8, (R, I))
+            aq = view("aq", R * I, _U8, (R, I))
+            # the streaming down GEMM (block_m 16) takes act codes in the
+            # blocked order; shown row-major here
+            out["aq"] = unblock_weights(aq) if B == 16 else aq
             out["as"] = view("as_", R * (I // 128 if blk else 1), _F32, (R, I // 128) if blk else (R,))
         out["max_rows"], out["block_m"] = R, B
         return out
