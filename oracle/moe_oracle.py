@@ -66,6 +66,8 @@ __all__ = [
     "permute_max_rows", "permute_align",
     "LayerSpec", "ExpertBank", "expert_gateup_silu", "expert_down", "combine",
     "moe_forward", "moe_forward_tokens", "relative_l2",
+    "E2M1_MAGNITUDES", "e2m1_value", "e2m1_encode", "mxfp4_quant", "mxfp4_payload", "mxfp4_unpack",
+    "fp8_block_payload", "fp8_block_unpack", "ep_payload_bytes",
 ]
 
 E4M3_MAX = 448.0          # largest finite OCP e4m3fn magnitude (S.1111.110)
@@ -202,6 +204,110 @@ def quant_weight_blocks(w, blk: int = 128) -> Tuple[np.ndarray, np.ndarray]:
     codes, scale = _quant_groups(tiles.reshape(-1, blk * blk))
     codes = codes.reshape(N // blk, K // blk, blk, blk).transpose(0, 2, 1, 3).reshape(N, K)
     return codes, scale.reshape(N // blk, K // blk)
+
+
+# --------------------------------------------------------------------------
+# Expert-parallel payloads   [MI355X-MORI] "Hybrid FP4/FP8 quantized
+# all-to-all": tokens go out to their experts as MXFP4 (dispatch) and expert
+# outputs come back as FP8 with one fp32 scale per 128 elements (combine);
+# for hidden size 7168 the round trip falls from 28,672 to 11,200 bytes per
+# token.  MXFP4 is the OCP Microscaling (MX) v1.0 format: blocks of 32
+# elements share one E8M0 power-of-two scale; elements are FP4 E2M1
+# (1 sign, 2 exponent bits with bias 1, 1 mantissa bit).
+# --------------------------------------------------------------------------
+
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)   # codes 0..7 (bit 3: sign)
+
+
+def e2m1_value(codes) -> np.ndarray:
+    """float64 value of FP4 E2M1 codes (low 4 bits; bit 3 is the sign)."""
+    c = np.asarray(codes, dtype=np.uint8) & 0xF
+    exp, man = (c >> 1) & 3, (c & 1).astype(np.float64)
+    mag = np.where(exp == 0, man * 0.5, (1.0 + man * 0.5) * np.exp2(exp.astype(np.float64) - 1.0))
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_encode(q) -> np.ndarray:
+    """Nearest E2M1 code of each value (ties to the even mantissa bit),
+    saturating to +-6; the sign bit follows the sign of the input (-0 -> 8).
+    Inputs are finite."""
+    q = np.asarray(q, dtype=np.float64)
+    a = np.abs(q)
+    mags = np.asarray(E2M1_MAGNITUDES)
+    dist = np.abs(a[..., None] - mags)                       # [.., 8]
+    best = dist.min(axis=-1, keepdims=True)
+    # among the nearest magnitudes take the one whose mantissa bit (code & 1) is 0
+    cand = dist == best
+    even = cand & (np.arange(8) % 2 == 0)
+    idx = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    idx = np.where(a > 6.0, 7, idx)
+    return (idx | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
+
+
+def mxfp4_quant(x, block: int = 32) -> Tuple[np.ndarray, np.ndarray]:
+    """MXFP4 quantization of the rows of ``x`` [M, K] (K a multiple of 32).
+
+    Per block of 32: amax = max|x|; shared exponent e = floor(log2(amax)) - 2
+    (2 is the exponent of E2M1's largest value, 6 = 1.5 * 2^2), clamped to
+    [-127, 127]; each element is x / 2^e encoded to E2M1 (round to nearest,
+    ties to even, saturating); the scale code is the E8M0 byte e + 127.  An
+    all-zero block gets scale code 0 and zero codes.
+    Returns (codes uint8 [M, K] in 0..15, scale codes uint8 [M, K/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    if K % block:
+        raise ValueError("K must be a multiple of the block size")
+    b = x.reshape(M, K // block, block)
+    amax = np.max(np.abs(b), axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))           # amax = m * 2^ex, m in [0.5, 1)
+    e = np.clip(ex - 1 - 2, -127, 127)
+    e = np.where(amax > 0, e, -127)
+    q = b / np.exp2(e.astype(np.float64))[:, :, None]          # exact: a power-of-two divisor
+    codes = e2m1_encode(q).reshape(M, K)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mxfp4_payload(x) -> np.ndarray:
+    """Dispatch payload of each row of ``x`` [M, K]: K/2 bytes of E2M1 codes
+    (element 2i in the low nibble of byte i, 2i+1 in the high nibble), then
+    K/32 E8M0 scale bytes.  Returns uint8 [M, K/2 + K/32]."""
+    codes, sc = mxfp4_quant(x)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return np.concatenate([packed, sc], axis=1)
+
+
+def mxfp4_unpack(payload, K: int) -> np.ndarray:
+    """float64 values of a dispatch payload [M, K/2 + K/32]: code value *
+    2^(scale code - 127)."""
+    p = np.asarray(payload, dtype=np.uint8)
+    codes = np.empty((p.shape[0], K), np.uint8)
+    codes[:, 0::2] = p[:, :K // 2] & 0xF
+    codes[:, 1::2] = p[:, :K // 2] >> 4
+    e = p[:, K // 2:K // 2 + K // 32].astype(np.float64) - 127.0
+    return e2m1_value(codes) * np.repeat(np.exp2(e), 32, axis=1)
+
+
+def fp8_block_payload(x) -> np.ndarray:
+    """Combine payload of each row of ``x`` [M, K]: the K e4m3fn codes of its
+    1x128 blockwise quantization, then its K/128 fp32 scales (little-endian
+    bytes).  Returns uint8 [M, K + 4 K/128]."""
+    codes, sc = quant_rows(x, 128)
+    return np.concatenate([codes, np.ascontiguousarray(sc.astype("<f4")).view(np.uint8)], axis=1)
+
+
+def fp8_block_unpack(payload, K: int) -> np.ndarray:
+    """bf16 values (as float32) of a combine payload: fp32(code value *
+    scale), one fp32 product, then rounded to bf16."""
+    p = np.asarray(payload, dtype=np.uint8)
+    v = e4m3_value(p[:, :K]).astype(np.float32)
+    sc = np.ascontiguousarray(p[:, K:K + 4 * (K // 128)]).view("<f4").astype(np.float32)
+    y = (v * np.repeat(sc, 128, axis=1)).astype(np.float32)
+    return bf16_round(y)
+
+
+def ep_payload_bytes(D: int) -> Dict[str, int]:
+    """Bytes per token of the dispatch and combine payloads for hidden size D."""
+    return {"bf16": 2 * D, "mxfp4": D // 2 + D // 32, "fp8_block": D + 4 * (D // 128)}
 
 
 _E4M3_TABLE = None
