@@ -232,6 +232,35 @@ def cpu_baseline(case, y_gpu, tokens):
                        f"{dt:.1f} s", seconds=round(dt, 2)), ok, err
 
 
+def time_payloads(torch, mlr, x, steps, warmup):
+    """Pack and unpack of the expert-parallel payloads (MXFP4 dispatch, FP8
+    blockwise combine) of the workload's x rows: HIP events on the current
+    stream; bytes = bf16 rows + payload rows per call."""
+    T, D = x.shape
+    res = {"T": T, "D": D}
+    for fmt in ("mxfp4", "fp8_block"):
+        n = mlr.ep_payload_bytes(D, fmt)
+        p = torch.empty((T, n), dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        r = {"row_bytes": n}
+        for name, fn in (("pack", lambda: mlr.ep_pack(x, fmt, out=p)), ("unpack", lambda: mlr.ep_unpack(p, D, fmt, out=y))):
+            for _ in range(warmup):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / steps * 1e3
+            gbs = (T * D * 2 + T * n) / (us * 1e-6) / 1e9
+            r[name + "_us"] = round(us, 2)
+            r[name + "_GBps"] = round(gbs, 1)
+            r[name + "_hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+        res[fmt] = r
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +384,9 @@ def main():
         "step_entries_ms_per_step": round(steps_ms, 4), "step_entries_equal_fused": same,
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
     }
+    if w.D % 128 == 0:
+        log("expert-parallel payloads")
+        out["ep_payload"] = time_payloads(torch, mlr, case.x, args.steps, args.warmup)
     if not args.no_decode and w.name != "qwen3_235b_decode_ptpc":
         log("decode leg")
         out["decode"] = time_decode(torch, mlr, synth, max(args.steps, 100), args.warmup)

@@ -72,6 +72,10 @@ extern "C" {
 #define MOE_WEIGHTS_ROWS        0  /* row-major                                 */
 #define MOE_WEIGHTS_BLOCKED     1  /* 16 rows x 128 bytes per contiguous block  */
 
+/* expert-parallel payload formats (moe_ep_payload_bytes / pack / unpack) */
+#define MOE_PAYLOAD_MXFP4       0  /* dispatch: FP4 E2M1 + E8M0 per 32          */
+#define MOE_PAYLOAD_FP8_BLOCK   1  /* combine: e4m3fn + fp32 scale per 128      */
+
 /* Limits of this build (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS   1024  /* E + n_shared                                 */
 #define MOE_MAX_TOPK        16
@@ -285,6 +289,38 @@ int32_t moe_workspace_layout(const moe_layer_desc* L, int32_t T, int32_t block_m
 int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* logits_or_null,
                     int32_t T, int32_t block_m, void* y_bf16, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * Expert-parallel payloads ("Win on TCO ... MoRI", "Hybrid FP4/FP8 quantized
+ * all-to-all": MXFP4 for dispatch, FP8 with one fp32 scale per 128 elements
+ * for combine; 28,672 -> 11,200 bytes per token at hidden size 7168).  The
+ * exchange between GPUs is not part of this library; these entries build and
+ * read the per-token payload rows on one GPU.
+ *
+ * moe_ep_payload_bytes: host-only; bytes of one payload row for D elements,
+ * or -1 when D is not a positive multiple of 128 or the format is unknown.
+ *   MOE_PAYLOAD_MXFP4: D/2 bytes of FP4 E2M1 codes (OCP Microscaling v1.0;
+ *     element 2i in the low nibble of byte i), then D/32 E8M0 scale bytes,
+ *     one per block of 32 elements: exponent e = floor(log2(amax)) - 2
+ *     clamped to [-127, 127] (byte e + 127; an all-zero block has byte 0),
+ *     elements x / 2^e rounded to the nearest E2M1 value, ties to the even
+ *     mantissa, saturating to +-6, sign of zero kept.
+ *   MOE_PAYLOAD_FP8_BLOCK: D e4m3fn codes of the 1x128 blockwise
+ *     quantization (as moe_quant_ptpc_fp8 with group 128), then D/128 fp32
+ *     scales (little-endian).
+ * moe_ep_pack_payload: x [T, D] bf16 -> payload [T, row bytes] (rows
+ *   contiguous).  Inputs must be finite.
+ * moe_ep_unpack_payload: payload -> x [T, D] bf16: MXFP4 elements exactly
+ *   (code value * 2^(e) is a bf16 value); FP8 as bf16(fp32(code value *
+ *   scale)).
+ * Errors: NULL pointers or T < 0 -> MOE_ERR_INVALID_ARG; D not a positive
+ * multiple of 128 (or above 65536) or an unknown format -> MOE_ERR_UNSUPPORTED.
+ */
+int64_t moe_ep_payload_bytes(int32_t D, int32_t format);
+int32_t moe_ep_pack_payload(const void* x_bf16, int32_t T, int32_t D, int32_t format,
+                            uint8_t* payload, void* stream);
+int32_t moe_ep_unpack_payload(const uint8_t* payload, int32_t T, int32_t D, int32_t format,
+                              void* x_bf16, void* stream);
 
 #ifdef __cplusplus
 }

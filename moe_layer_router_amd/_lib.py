@@ -19,6 +19,8 @@ QUANT_NONE_BF16, QUANT_PTPC_FP8, QUANT_BLOCK128_FP8 = 0, 1, 2
 QUANT_CODES = {"bf16": QUANT_NONE_BF16, "ptpc_fp8": QUANT_PTPC_FP8, "block128_fp8": QUANT_BLOCK128_FP8}
 WEIGHTS_ROWS, WEIGHTS_BLOCKED = 0, 1
 LAYOUT_CODES = {"rows": WEIGHTS_ROWS, "blocked": WEIGHTS_BLOCKED}
+PAYLOAD_MXFP4, PAYLOAD_FP8_BLOCK = 0, 1
+PAYLOAD_CODES = {"mxfp4": PAYLOAD_MXFP4, "fp8_block": PAYLOAD_FP8_BLOCK}
 
 
 class LayerDesc(ctypes.Structure):
@@ -60,6 +62,9 @@ SIGNATURES = {
     "moe_workspace_layout": (c_int32, [POINTER(LayerDesc), c_int32, c_int32, POINTER(WsLayout)]),
     "moe_forward": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                               c_size_t, c_void_p]),
+    "moe_ep_payload_bytes": (c_int64, [c_int32, c_int32]),
+    "moe_ep_pack_payload": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "moe_ep_unpack_payload": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
 }
 
 _LIB = None

@@ -32,6 +32,9 @@ int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* 
                          void* out_perm, hipStream_t s, bool act_blocked = false);
 int32_t combine_launch(const void* out_perm, int out_dtype, const int* inv_perm, const float* topk_w, int T,
                        int k, int n_shared, int D, uint16_t* y, hipStream_t s);
+int64_t ep_payload_row_bytes(int D, int format);
+int32_t ep_pack_launch(const uint16_t* x, int T, int D, int format, uint8_t* payload, hipStream_t s);
+int32_t ep_unpack_launch(const uint8_t* payload, int T, int D, int format, uint16_t* x, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -378,6 +381,29 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
                                aq_blocked)) != MOE_OK)
         return st;
     return combine_launch(outp, fp8 ? 1 : 0, inv, w, T, k, L->n_shared, L->D, static_cast<uint16_t*>(y_bf16), s);
+}
+
+int64_t moe_ep_payload_bytes(int32_t D, int32_t format) {
+    if (D <= 0 || D % 128 || D > 65536) return -1;
+    return ep_payload_row_bytes(D, format);
+}
+
+int32_t moe_ep_pack_payload(const void* x_bf16, int32_t T, int32_t D, int32_t format, uint8_t* payload,
+                            void* stream) {
+    MOE_CHECK_ARG(T >= 0);
+    MOE_CHECK_SUP(moe_ep_payload_bytes(D, format) > 0);
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(x_bf16 && payload);
+    return ep_pack_launch(static_cast<const uint16_t*>(x_bf16), T, D, format, payload, as_stream(stream));
+}
+
+int32_t moe_ep_unpack_payload(const uint8_t* payload, int32_t T, int32_t D, int32_t format, void* x_bf16,
+                              void* stream) {
+    MOE_CHECK_ARG(T >= 0);
+    MOE_CHECK_SUP(moe_ep_payload_bytes(D, format) > 0);
+    if (T == 0) return MOE_OK;
+    MOE_CHECK_ARG(x_bf16 && payload);
+    return ep_unpack_launch(payload, T, D, format, static_cast<uint16_t*>(x_bf16), as_stream(stream));
 }
 
 }  // extern "C"

@@ -279,3 +279,36 @@ def unpermute_combine(out_perm: torch.Tensor, inv_perm: torch.Tensor, topk_w: to
                                                                     _ptr(topk_w), T, k, n_shared, D, _ptr(y),
                                                                     _stream()))
     return y
+
+
+# ---------------------------------------------------------------- expert-parallel payloads
+
+def ep_payload_bytes(D: int, fmt: str) -> int:
+    """Bytes of one payload row ("mxfp4" dispatch or "fp8_block" combine)."""
+    n = L.lib().moe_ep_payload_bytes(D, L.PAYLOAD_CODES[fmt])
+    if n < 0:
+        raise ValueError(f"no {fmt} payload for D={D} (D must be a positive multiple of 128)")
+    return n
+
+
+def ep_pack(x: torch.Tensor, fmt: str, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Payload rows [T, ep_payload_bytes(D, fmt)] uint8 of bf16 rows x [T, D]."""
+    T, D = x.shape
+    _need(x, _BF16, "x")
+    n = ep_payload_bytes(D, fmt)
+    p = out if out is not None else _empty((T, n), torch.uint8, x)
+    _need(p, torch.uint8, "payload", (T, n))
+    L.check("moe_ep_pack_payload", L.lib().moe_ep_pack_payload(_ptr(x), T, D, L.PAYLOAD_CODES[fmt], _ptr(p),
+                                                                _stream()))
+    return p
+
+
+def ep_unpack(payload: torch.Tensor, D: int, fmt: str, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 rows [T, D] of payload rows [T, ep_payload_bytes(D, fmt)]."""
+    T = payload.shape[0]
+    _need(payload, torch.uint8, "payload", (T, ep_payload_bytes(D, fmt)))
+    y = out if out is not None else _empty((T, D), _BF16, payload)
+    _need(y, _BF16, "x", (T, D))
+    L.check("moe_ep_unpack_payload", L.lib().moe_ep_unpack_payload(_ptr(payload), T, D, L.PAYLOAD_CODES[fmt],
+                                                                    _ptr(y), _stream()))
+    return y

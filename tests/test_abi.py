@@ -156,3 +156,22 @@ def test_unblock_weights_inverts_the_blocked_byte_order():
     assert np.array_equal(got.numpy(), rowmajor)
     # the first line of a block holds bytes 0..63 of rows 0 and 1
     assert np.array_equal(blocked[:64], rowmajor[0, 0, :64]) and np.array_equal(blocked[64:128], rowmajor[0, 1, :64])
+
+
+def test_ep_payload_sizes_and_validation():
+    """Payload row sizes match the oracle's closed forms (host-only call), and
+    bad arguments are rejected before anything is enqueued."""
+    lib = L.lib()
+    for D in (128, 4096, 7168, 16384):
+        b = O.ep_payload_bytes(D)
+        assert lib.moe_ep_payload_bytes(D, L.PAYLOAD_MXFP4) == b["mxfp4"]
+        assert lib.moe_ep_payload_bytes(D, L.PAYLOAD_FP8_BLOCK) == b["fp8_block"]
+    for D in (0, -128, 96, 7000, 65536 + 128):
+        assert lib.moe_ep_payload_bytes(D, L.PAYLOAD_MXFP4) == -1
+    assert lib.moe_ep_payload_bytes(4096, 7) == -1
+    assert lib.moe_ep_pack_payload(None, 4, 4096, L.PAYLOAD_MXFP4, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_ep_pack_payload(None, -1, 4096, L.PAYLOAD_MXFP4, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_ep_pack_payload(None, 4, 100, L.PAYLOAD_FP8_BLOCK, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ep_unpack_payload(None, 4, 4096, 3, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ep_pack_payload(None, 0, 4096, L.PAYLOAD_MXFP4, None, None) == L.MOE_OK
+    assert lib.moe_ep_unpack_payload(None, 0, 4096, L.PAYLOAD_FP8_BLOCK, None, None) == L.MOE_OK
