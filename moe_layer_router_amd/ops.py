@@ -7,6 +7,7 @@ the current HIP stream.
 
 from __future__ import annotations
 
+import copy
 import ctypes
 from dataclasses import dataclass
 from typing import Optional
@@ -187,6 +188,18 @@ class MoELayer:
             q2, s2 = quant_weight_fp8(w2_bf16.contiguous(), quant, weight_layout)
             w = LayerWeights(q13, q2, s13, s2, router_w=router_w, sel_bias=sel_bias)
         return cls(D=D, I=I2 // 2, weights=w, quant=quant, weight_layout=weight_layout, **kw)
+
+    def with_weights(self, weights: LayerWeights) -> "MoELayer":
+        """The same layer over other weight tensors of the same shapes, dtypes
+        and layout (e.g. copies of this layer's weights)."""
+        other = copy.copy(self)
+        other.weights = weights
+        other.desc = L.LayerDesc.from_buffer_copy(self.desc)
+        other.desc.w13, other.desc.w13_scale = _ptr(weights.w13), _ptr(weights.w13_scale)
+        other.desc.w2, other.desc.w2_scale = _ptr(weights.w2), _ptr(weights.w2_scale)
+        other.desc.router_w, other.desc.sel_bias = _ptr(weights.router_w), _ptr(weights.sel_bias)
+        other._ws = None
+        return other
 
     # ---- host-side sizes
     def default_block_m(self, T: int) -> int:
