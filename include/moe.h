@@ -231,8 +231,10 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
  * expert_counts (device, [E+n_shared], as moe_permute_align writes it; may
  * be NULL) lets the LDS-tiled kernels skip the 32-row tiles at the end of an
  * expert's segment that hold only pads; it must match expert_offsets.
- * Pad rows (sentinel) get act = 0; rows at or past expert_offsets[E'] are not
- * written.  block_m must equal the block_m of moe_permute_align and be one
+ * Pad rows (sentinel) get act = 0, except that with expert_counts the pad
+ * rows of those pad-only 32-row tiles are not written (the LDS-tiled
+ * kernels; their contents are then unspecified); rows at or past
+ * expert_offsets[E'] are not written.  block_m must equal the block_m of moe_permute_align and be one
  * of: 16 (weight-streaming kernels for small batches: each weight byte is
  * read once per 64 rows of its expert), 32, 64, 128 or 256 (LDS-tiled
  * kernels).  Shapes: I % 128 == 0 and D % 256 == 0.
@@ -246,9 +248,11 @@ int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
 /*
  * Grouped GEMM down: out_perm[r] = act[r] . W2[e]^T for the valid rows
  * (dequantized by the row scale(s) and the weight scales).  Same block_m,
- * expert_counts and shape rules as moe_grouped_gemm_gateup_silu.  Pad rows
- * of out_perm are written as 0; with expert_counts NULL that needs the pad
- * rows of act to hold zeros (moe_grouped_gemm_gateup_silu writes them so).  act: quant 0:
+ * expert_counts and shape rules as moe_grouped_gemm_gateup_silu.  With
+ * expert_counts the pad rows of act are never read and the pad rows of
+ * out_perm are 0, or unspecified in pad-only 32-row tiles (as for act); with
+ * expert_counts NULL every row of a segment is computed, so pad rows of
+ * out_perm are 0 only where the pad rows of act hold zeros.  act: quant 0:
  * bf16 [R, I]; quant 1/2: codes [R, I] with act_scale [R] or [R, I/128].
  * out_perm [R, D]: fp32 for quant 0, bf16 for quant 1/2.
  */

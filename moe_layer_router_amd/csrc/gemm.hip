@@ -37,7 +37,8 @@
 //
 // Pad rows read a real row and are zeroed by a row mask in the epilogue;
 // 32-row tiles made only of pads (known from the expert's row count) get no
-// operand reads and no MFMAs, and with two stages no activation copies.
+// operand reads, no MFMAs and no output stores, and with two stages no
+// activation copies.
 // Tiles are ordered expert by expert, weight tile by weight tile, row block
 // fastest, and each XCD (workgroup id mod 8) takes a contiguous range of
 // that order, so the row blocks of one expert that share a weight tile run
@@ -529,7 +530,11 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     // ------------------------------------------------------------ epilogue
     // (called at the end of each main-loop variant, so that no variant's
     // accumulators meet another's at a join point)
-    auto epilogue = [&]() __attribute__((always_inline)) {
+    // TA: this wave's row tiles that hold routed rows; the tiles after them
+    // hold only pads and are not written (their rows' contents are
+    // unspecified: nothing reads pad rows of act or out_perm)
+    auto epilogue = [&](auto TAc) __attribute__((always_inline)) {
+        constexpr int TA = decltype(TAc)::value;
         // The MFMAs take the weight rows as their first operand, so lane
         // (r32, q) holds row r32 of each 32-row tile and, in register
         // i = 4g + j, output column 8g + 4q + j of each 32-column tile: four
@@ -563,7 +568,7 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
                 return float4{1.0f, 1.0f, 1.0f, 1.0f};
         };
     #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
+        for (int tm = 0; tm < TA; ++tm) {
             const float rs = s_rowscale[arow + tm * 32 + r32];
             // pack this row tile into the wave's region
     #pragma unroll
@@ -610,7 +615,7 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     static_for<TM + 1>([&](auto TAc) {
         if (ta == decltype(TAc)::value) {
             run(TAc);
-            epilogue();
+            epilogue(TAc);
         }
     });
 }

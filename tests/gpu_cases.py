@@ -100,3 +100,20 @@ def rel_l2(a, b) -> float:
 def tol_of(quant: str) -> float:
     """Relative L2 bound on y: 2e-3 for the bf16 path, 1e-2 for the FP8 paths."""
     return 2e-3 if quant == "bf16" else 1e-2
+
+
+def zero_pad_rows(perm: dict, block_m: int, use_counts: bool = True) -> np.ndarray:
+    """Boolean mask over rows [0, offsets[-1]) of the pad rows a GEMM writes
+    as 0: every pad row for the streaming kernels (block_m 16) or without
+    expert counts; otherwise the pads inside a 32-row tile that also holds
+    routed rows (pad-only tiles are not written and their rows are
+    unspecified, as every pad row's contents are for the layer)."""
+    offs = perm["offsets"].cpu().numpy()
+    cnts = perm["counts"].cpu().numpy()
+    mask = np.zeros(int(offs[-1]), bool)
+    for e in range(len(cnts)):
+        lo, hi, end = int(offs[e]), int(offs[e]) + int(cnts[e]), int(offs[e + 1])
+        top = end if (block_m == 16 or not use_counts) else min(end, lo + -(-int(cnts[e]) // 32) * 32)
+        mask[hi:top] = True
+    return mask
+
