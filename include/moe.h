@@ -76,7 +76,7 @@ extern "C" {
 #define MOE_PAYLOAD_MXFP4       0  /* dispatch: FP4 E2M1 + E8M0 per 32          */
 #define MOE_PAYLOAD_FP8_BLOCK   1  /* combine: e4m3fn + fp32 scale per 128      */
 
-/* Limits of this build (MOE_ERR_UNSUPPORTED beyond them). */
+/* Limits of the library (MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS   1024  /* E + n_shared                                 */
 #define MOE_MAX_TOPK        16
 #define MOE_MAX_GROUPS      32
