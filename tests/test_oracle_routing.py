@@ -23,7 +23,7 @@ def _brute_topk(row, k):
     return [e for r in range(k) for e in range(E) if rank[e] == r]
 
 
-@pytest.mark.parametrize("seed,E,k", [(0, 8, 2), (1, 16, 4), (2, 128, 8), (3, 7, 7)])
+@pytest.mark.parametrize("seed,E,k", [(0, 8, 2), (1, 16, 4), (2, 128, 8), (3, 7, 7), (4, 512, 10)])
 def test_softmax_topk_ids_vs_rank_counting(seed, E, k):
     rng = np.random.default_rng(seed)
     logits = rng.standard_normal((20, E)).astype(np.float32)
