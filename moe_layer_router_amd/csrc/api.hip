@@ -15,7 +15,8 @@ int32_t permute_align_launch(const int* ids, int T, int k, int E, int n_shared, 
 int32_t quant_wrows_launch(const uint16_t* w, int64_t M, int K, bool blocked, uint8_t* q, float* scale,
                            hipStream_t s);
 int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const int* valid_rows, uint8_t* q,
-                          float* scale, hipStream_t s, bool blocked = false);
+                          float* scale, hipStream_t s, bool blocked = false, const int* skip_ids = nullptr,
+                          int skip_id = 0);
 int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, bool blocked, uint8_t* q, float* scale,
                             hipStream_t s);
 bool front_small_ok(int T, int k, int n_shared);
@@ -366,12 +367,14 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     const float* act_scale = nullptr;
     // the streaming down GEMM reads act codes stored in 16-row x 128-byte
     // blocks (whole lines per load, as for the weights); max_rows is a
-    // multiple of 16 there
+    // multiple of 16 there.  The tiled down GEMM never reads a pad row's
+    // codes or scale (it is given the expert counts), so pad rows are not
+    // quantized for it.
     const bool aq_blocked = fp8 && block_m == 16;
     if (fp8) {
         if ((st = quant_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, group, offsets + Ep,
-                                    static_cast<uint8_t*>(at(o.aq)), static_cast<float*>(at(o.as)), s, aq_blocked)) !=
-            MOE_OK)
+                                    static_cast<uint8_t*>(at(o.aq)), static_cast<float*>(at(o.as)), s, aq_blocked,
+                                    block_m == 16 ? nullptr : sorted, T * (k + L->n_shared))) != MOE_OK)
             return st;
         act_in = at(o.aq);
         act_scale = static_cast<float*>(at(o.as));

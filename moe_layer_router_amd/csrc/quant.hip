@@ -27,11 +27,13 @@ __device__ __forceinline__ int64_t code_off(int64_t row, int k, int K, bool bloc
 template <int NV, int GROUP>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
                                                          const int* __restrict__ valid_rows, bool blocked,
+                                                         const int* __restrict__ skip_ids, int skip_id,
                                                          uint8_t* __restrict__ q, float* __restrict__ scale) {
     const int lane = threadIdx.x & 63;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (row >= M) return;
     if (valid_rows && row >= *valid_rows) return;
+    if (skip_ids && skip_ids[row] == skip_id) return;     // a row nothing reads (a pad of the permutation)
     const int nvec = K >> 3;
     const bf16x8* xr = reinterpret_cast<const bf16x8*>(x + row * K);
     bf16x8 v[NV];
@@ -141,23 +143,28 @@ __global__ void __launch_bounds__(256) quant_wblock_kernel(const uint16_t* __res
 
 template <int GROUP>
 static void launch_rows(int nv, dim3 g, hipStream_t s, const uint16_t* x, int64_t M, int K, const int* valid,
-                        bool blocked, uint8_t* q, float* sc) {
+                        bool blocked, const int* skip_ids, int skip_id, uint8_t* q, float* sc) {
     const dim3 b(256);
-    if (nv <= 1) hipLaunchKernelGGL((quant_rows_kernel<1, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
-    else if (nv <= 2) hipLaunchKernelGGL((quant_rows_kernel<2, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
-    else if (nv <= 4) hipLaunchKernelGGL((quant_rows_kernel<4, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
-    else if (nv <= 8) hipLaunchKernelGGL((quant_rows_kernel<8, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
-    else if (nv <= 16) hipLaunchKernelGGL((quant_rows_kernel<16, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
-    else hipLaunchKernelGGL((quant_rows_kernel<32, GROUP>), g, b, 0, s, x, M, K, valid, blocked, q, sc);
+#define MOE_ROWS(NV) hipLaunchKernelGGL((quant_rows_kernel<NV, GROUP>), g, b, 0, s, x, M, K, valid, blocked, skip_ids, \
+                                        skip_id, q, sc)
+    if (nv <= 1) MOE_ROWS(1);
+    else if (nv <= 2) MOE_ROWS(2);
+    else if (nv <= 4) MOE_ROWS(4);
+    else if (nv <= 8) MOE_ROWS(8);
+    else if (nv <= 16) MOE_ROWS(16);
+    else MOE_ROWS(32);
+#undef MOE_ROWS
 }
 
+// skip_ids (may be NULL): rows whose skip_ids entry equals skip_id are left
+// unwritten
 int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const int* valid_rows, uint8_t* q,
-                          float* scale, hipStream_t s, bool blocked) {
+                          float* scale, hipStream_t s, bool blocked, const int* skip_ids, int skip_id) {
     if (M == 0) return MOE_OK;
     const int nv = static_cast<int>(ceil_div(K / 8, 64));
     const dim3 g(static_cast<unsigned>(ceil_div(M, 4)));
-    if (group == 0) launch_rows<0>(nv, g, s, x, M, K, valid_rows, blocked, q, scale);
-    else launch_rows<128>(nv, g, s, x, M, K, valid_rows, blocked, q, scale);
+    if (group == 0) launch_rows<0>(nv, g, s, x, M, K, valid_rows, blocked, skip_ids, skip_id, q, scale);
+    else launch_rows<128>(nv, g, s, x, M, K, valid_rows, blocked, skip_ids, skip_id, q, scale);
     return moe_launch_status();
 }
 
