@@ -198,3 +198,127 @@ def test_empty_batch():
     bank, _, _ = _bank(spec, 25)
     out = O.moe_forward(spec, bank, np.zeros((0, 128), np.float32), np.zeros((0, 8), np.float32))
     assert out["y"].shape == (0, 128)
+
+
+# ------------------------------------------------------------ FP8 storage points
+
+def _bf16_t(v: float) -> float:
+    """bf16 rounding through torch's own cast (independent of the oracle's codec)."""
+    return float(torch.tensor([v], dtype=torch.float32).to(torch.bfloat16).to(torch.float32)[0])
+
+
+def _fp8_dequant_groups(vals, group):
+    """Dequantized values of a list of fp32 values, quantized in consecutive
+    groups of ``group`` elements: scale = fp32(amax / 448), codes through
+    torch's float8_e4m3fn cast of fp32(v * fp32(448 / amax)); value = code * scale."""
+    out = []
+    for g0 in range(0, len(vals), group):
+        grp = [np.float32(v) for v in vals[g0:g0 + group]]
+        amax = max(abs(v) for v in grp)
+        if amax == 0:
+            scale, inv = 1.0, np.float32(1.0)
+        else:
+            scale, inv = float(np.float32(amax) / np.float32(448.0)), np.float32(448.0) / np.float32(amax)
+        t = torch.tensor([float(v * inv) for v in grp], dtype=torch.float32)
+        out += [c * scale for c in t.to(torch.float8_e4m3fn).to(torch.float64).tolist()]
+    return out
+
+
+def _fp8_weight(w, block):
+    """Dequantized weight [N][K] as nested lists: one scale per output row
+    (block None) or per block x block tile."""
+    N, K = w.shape
+    if block is None:
+        return [_fp8_dequant_groups(w[n].tolist(), K) for n in range(N)]
+    deq = [[0.0] * K for _ in range(N)]
+    for n0 in range(0, N, block):
+        for k0 in range(0, K, block):
+            tile = [float(w[n, k]) for n in range(n0, n0 + block) for k in range(k0, k0 + block)]
+            d = _fp8_dequant_groups(tile, block * block)
+            for i, n in enumerate(range(n0, n0 + block)):
+                deq[n][k0:k0 + block] = d[i * block:(i + 1) * block]
+    return deq
+
+
+def _py_layer_fp8(spec, x, logits, w13, w2, sel_bias=None):
+    """The FP8 layer token by token with Python loops, rounding at every
+    storage point the layer declares: x codes (per row, or per 1x128 group),
+    fp64 dot products, act = bf16(fp32(silu(g) * u)), act re-quantized (per
+    row, or per 1x128 group), expert output o = bf16(fp32(act . W2)), then
+    y = bf16(fp32(sum_j w_j o_j + o_shared)) with the sum in order j = 0..k-1
+    and the shared expert last.  Rounding goes through torch's casts."""
+    blk = 128 if spec.quant == "block128_fp8" else None
+    T = x.shape[0]
+    ids, w = (O.route_softmax_topk(logits, spec.top_k) if spec.scoring == "softmax" else
+              O.route_sigmoid_grouped(logits, spec.top_k, spec.n_groups, spec.topk_groups,
+                                      sel_bias, spec.route_scale))
+    W13 = {e: _fp8_weight(w13[e], blk) for e in range(spec.E + spec.n_shared)}
+    W2 = {e: _fp8_weight(w2[e], blk) for e in range(spec.E + spec.n_shared)}
+    y = np.zeros((T, spec.D), np.float32)
+    for t in range(T):
+        a = _fp8_dequant_groups(x[t].tolist(), blk or spec.D)
+        experts = [(int(e), float(wt)) for e, wt in zip(ids[t], w[t])]
+        if spec.n_shared:
+            experts.append((spec.E, 1.0))
+        acc = [0.0] * spec.D
+        for e, wt in experts:
+            act = []
+            for i in range(spec.I):
+                g = sum(a[d] * W13[e][i][d] for d in range(spec.D))
+                u = sum(a[d] * W13[e][spec.I + i][d] for d in range(spec.D))
+                act.append(_bf16_t(float(np.float32(g / (1.0 + np.exp(-g)) * u))))
+            aq = _fp8_dequant_groups(act, blk or spec.I)
+            for d in range(spec.D):
+                o = _bf16_t(float(np.float32(sum(aq[i] * W2[e][d][i] for i in range(spec.I)))))
+                acc[d] += wt * o
+        y[t] = [_bf16_t(float(np.float32(v))) for v in acc]
+    return y
+
+
+def test_tiny_ptpc_layer_top3_shared_vs_python_loops():
+    """PTPC-FP8, k = 3 plus a shared expert: every storage point (x codes, bf16
+    act, act codes, bf16 expert outputs, combine order) against the loops."""
+    spec = O.LayerSpec(D=16, I=8, E=6, top_k=3, n_shared=1, quant="ptpc_fp8")
+    bank, w13, w2 = _bank(spec, 31)
+    x = _x(7, 16, 32)
+    x[2] = 0.0                                    # amax 0 -> scale 1
+    logits = np.random.default_rng(33).standard_normal((7, 6)).astype(np.float32)
+    out = O.moe_forward(spec, bank, x, logits, block_m=4)
+    ref = _py_layer_fp8(spec, x, logits, w13, w2)
+    assert O.relative_l2(out["y"], ref) <= 1e-6
+    assert np.all(out["y"][2] == 0)
+
+
+def test_tiny_block_fp8_layer_grouped_shared_vs_python_loops():
+    """Blockwise FP8 (1x128 activations, 128x128 weights), grouped-sigmoid
+    top-2 of 4 groups, x 2.5, plus a shared expert, against the loops."""
+    spec = O.LayerSpec(D=256, I=128, E=4, top_k=2, n_shared=1, scoring="sigmoid_grouped",
+                       n_groups=2, topk_groups=1, route_scale=2.5, quant="block128_fp8")
+    bank, w13, w2 = _bank(spec, 34)
+    x = _x(3, 256, 35)
+    x[1, 128:] = 0.0                              # one all-zero 1x128 group
+    logits = np.random.default_rng(36).standard_normal((3, 4)).astype(np.float32)
+    out = O.moe_forward(spec, bank, x, logits, block_m=2)
+    ref = _py_layer_fp8(spec, x, logits, w13, w2)
+    assert O.relative_l2(out["y"], ref) <= 1e-6
+
+
+# ------------------------------------------------------------ the error metric
+
+def test_relative_l2_closed_forms():
+    """relative_l2(a, ref) = ||a - ref||_2 / ||ref||_2 (||a||_2 when ref is all
+    zero), on vectors whose norms are known exactly."""
+    ref = np.array([3.0, 4.0])                                   # ||ref|| = 5
+    assert O.relative_l2(ref, ref) == 0.0
+    assert O.relative_l2(np.array([3.0, 4.0 + 5e-3]), ref) == pytest.approx(1e-3, rel=1e-12)
+    assert O.relative_l2(np.array([0.0, 0.0]), ref) == pytest.approx(1.0, rel=1e-15)
+    assert O.relative_l2(-ref, ref) == pytest.approx(2.0, rel=1e-15)
+    # 2-D arrays: the norm over every element (Frobenius), not per row
+    a2 = np.array([[1.0, 2.0], [2.0, 0.0]])                      # ||.|| = 3
+    r2 = np.array([[1.0, 2.0], [2.0, 4.0]])                      # ||.|| = 5, difference 4
+    assert O.relative_l2(a2, r2) == pytest.approx(0.8, rel=1e-15)
+    # zero reference: the absolute norm of a
+    assert O.relative_l2(np.array([1.0, 2.0, 2.0]), np.zeros(3)) == pytest.approx(3.0, rel=1e-15)
+    # a NaN anywhere makes the result NaN, so no `err <= tol` gate can pass it
+    assert np.isnan(O.relative_l2(np.array([3.0, np.nan]), ref))
+    assert not (O.relative_l2(np.array([3.0, np.nan]), ref) <= 1e-2)
