@@ -40,7 +40,10 @@
  *     before anything is enqueued: an invalid call enqueues nothing.
  *     MOE_ERR_HIP reports a launch failure (hipGetLastError after launch).
  *     T = 0 (no tokens) is valid and enqueues nothing.
- *   - The library keeps no state between calls and is thread-safe.
+ *   - The only state the library keeps between calls is a per-device cache of
+ *     how many workgroups of the weight-streaming kernels fit on the device
+ *     at once (filled on first use, read-only afterwards).  Entry points are
+ *     thread-safe; calls that share buffers must be ordered by the caller.
  */
 #ifndef MOE_LAYER_ROUTER_AMD_MOE_H
 #define MOE_LAYER_ROUTER_AMD_MOE_H
@@ -266,7 +269,8 @@ int32_t moe_grouped_gemm_down(const moe_layer_desc* L, const void* act, const fl
  * Qwen 3.5 page): y[t] = bf16( sum_{j<k} w[t,j] * out_perm[inv_perm[t*k+j]]
  * + out_perm[inv_perm[T*k+t]] (shared, when n_shared = 1) ), accumulated in
  * fp32 in that order.  out_dtype 0: out_perm fp32; 1: bf16.  Rows with
- * inv_perm = -1 contribute nothing.  y: [T, D] bf16.
+ * inv_perm = -1 contribute nothing.  y: [T, D] bf16.  Limits: D % 8 == 0 and
+ * k + n_shared <= MOE_MAX_TOPK + 1 (MOE_ERR_UNSUPPORTED otherwise).
  */
 int32_t moe_unpermute_combine(const void* out_perm, int32_t out_dtype, const int32_t* inv_perm,
                               const float* topk_w, int32_t T, int32_t k, int32_t n_shared,
@@ -288,7 +292,11 @@ int32_t moe_workspace_layout(const moe_layer_desc* L, int32_t T, int32_t block_m
  * combine.  x: [T, D] bf16; logits: [T, E] fp32 or NULL (then L->router_w is
  * required); y: [T, D] bf16.  block_m 0 picks moe_default_block_m.  The
  * workspace (>= moe_forward_workspace_size bytes, 256-byte aligned) holds
- * every intermediate at the offsets of moe_workspace_layout.
+ * every intermediate at the offsets of moe_workspace_layout.  Every limit of
+ * every kernel of the call (including the 32-bit byte ranges of the
+ * LDS-tiled GEMMs: T*D, 2*I*D and max_rows*I elements of FP8 codes or bf16
+ * below 4 GiB) is checked before the first launch; moe_forward_workspace_size
+ * returns 0 and moe_workspace_layout MOE_ERR_UNSUPPORTED for such shapes.
  */
 int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* logits_or_null,
                     int32_t T, int32_t block_m, void* y_bf16, void* workspace,

@@ -1,5 +1,6 @@
 // C ABI: argument validation, workspace carving and the fused forward.
-// Every check runs on the host before anything is enqueued.
+// Every check runs on the host before anything is enqueued (moe_forward
+// checks the limits of all of its kernels before the first launch).
 #include "common.h"
 
 namespace moe {
@@ -91,6 +92,18 @@ int32_t check_layer(const moe_layer_desc* L) {
     MOE_CHECK_SUP(L->I % 128 == 0 && L->D % 256 == 0);
     MOE_CHECK_SUP(L->D <= 16384 && L->I <= 16384);
     return MOE_OK;
+}
+
+// The LDS-tiled GEMMs address the activation rows and one expert's weights
+// with 32-bit byte offsets from a 64-bit base (the weight-streaming kernels,
+// block_m 16, use 64-bit addresses throughout).  Checked on the host before
+// any launch of a call.
+bool gemm_ranges_ok(const moe_layer_desc* L, int64_t T, int block_m, int64_t R) {
+    if (block_m == 16) return true;
+    const int64_t elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    const int64_t lim = 1LL << 32;
+    return T * L->D * elem < lim && 2LL * L->I * L->D * elem < lim &&   // gate/up
+           R * L->I * elem < lim;                                        // down (its weights are half of W13)
 }
 
 struct Carver {
@@ -234,6 +247,7 @@ int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a, con
     MOE_CHECK_ARG(a && sorted_ids && block_expert && expert_offsets && act_bf16);
     MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || a_scale);
     const int64_t R = max_rows_of(T, L->top_k, L->E, L->n_shared, block_m);
+    MOE_CHECK_SUP(gemm_ranges_ok(L, T, block_m, R));
     return gemm_gateup_launch(L, a, a_scale, T, block_m, R, sorted_ids, block_expert, expert_offsets, expert_counts,
                               act_bf16,
                               as_stream(stream));
@@ -250,6 +264,7 @@ int32_t moe_grouped_gemm_down(const moe_layer_desc* L, const void* act, const fl
     MOE_CHECK_ARG(act && block_expert && expert_offsets && out_perm);
     MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || act_scale);
     const int64_t R = max_rows_of(T, L->top_k, L->E, L->n_shared, block_m);
+    MOE_CHECK_SUP(gemm_ranges_ok(L, T, block_m, R));
     return gemm_down_launch(L, act, act_scale, T, block_m, R, block_expert, expert_offsets, expert_counts, out_perm,
                             as_stream(stream));
 }
@@ -260,6 +275,7 @@ int32_t moe_unpermute_combine(const void* out_perm, int32_t out_dtype, const int
     MOE_CHECK_ARG(T >= 0 && k > 0 && D > 0 && (n_shared == 0 || n_shared == 1));
     MOE_CHECK_ARG(out_dtype == 0 || out_dtype == 1);
     MOE_CHECK_SUP(D % 8 == 0);
+    MOE_CHECK_SUP(k + n_shared <= MOE_MAX_TOPK + 1);   // rows a token gathers, all loads in flight at once
     if (T == 0) return MOE_OK;
     MOE_CHECK_ARG(out_perm && inv_perm && topk_w && y_bf16);
     return combine_launch(out_perm, out_dtype, inv_perm, topk_w, T, k, n_shared, D, static_cast<uint16_t*>(y_bf16),
@@ -284,6 +300,7 @@ size_t moe_forward_workspace_size(const moe_layer_desc* L, int32_t T, int32_t bl
     if (!block_m_ok(block_m)) return 0;
     moe_ws_layout o;
     layout_of(L, T, block_m, &o);
+    if (!gemm_ranges_ok(L, T, block_m, o.max_rows)) return 0;
     return static_cast<size_t>(o.total);
 }
 
@@ -294,6 +311,7 @@ int32_t moe_workspace_layout(const moe_layer_desc* L, int32_t T, int32_t block_m
     if (block_m == 0) block_m = moe_default_block_m(L, T);
     MOE_CHECK_SUP(block_m_ok(block_m));
     layout_of(L, T, block_m, out);
+    MOE_CHECK_SUP(gemm_ranges_ok(L, T, block_m, out->max_rows));
     return MOE_OK;
 }
 
@@ -315,6 +333,7 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     MOE_CHECK_ARG(reinterpret_cast<uintptr_t>(workspace) % kAlign == 0);
     moe_ws_layout o;
     layout_of(L, T, block_m, &o);
+    MOE_CHECK_SUP(gemm_ranges_ok(L, T, block_m, o.max_rows));
     if (static_cast<int64_t>(workspace_bytes) < o.total) return MOE_ERR_WORKSPACE;
 
     hipStream_t s = as_stream(stream);

@@ -25,26 +25,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // ---------------------------------------------------------------- e4m3fn
 // OCP e4m3fn: bias 7, 3 mantissa bits, subnormals m * 2^-9, max 448 (0x7E),
-// 0x7F/0xFF NaN (never produced).  Round to nearest even, keep the sign of
-// zero, saturate magnitudes above 448.  Written from the format definition
-// with integer rounding so the result does not depend on a hardware mode.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
-    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fminf(fabsf(y), 448.0f);
-    if (a < 0.015625f) {                       // below 2^-6: subnormal codes 0..8
-        const float s = a * 512.0f;            // exact scaling by 2^9
-        return sign | static_cast<uint32_t>(__builtin_rintf(s));   // ties to even
-    }
-    const uint32_t ua = __float_as_uint(a);
-    const uint32_t e = (ua >> 23) - 120u;      // (exp - 127) + 7, in 1..15
-    uint32_t keep = (ua >> 20) & 7u;           // top 3 mantissa bits
-    const uint32_t rest = ua & 0xFFFFFu;       // 20 dropped bits
-    keep += (rest > 0x80000u) | ((rest == 0x80000u) & (keep & 1u));
-    uint32_t code = (e << 3) + keep;           // a carry of keep moves into e
-    code = code > 0x7Eu ? 0x7Eu : code;
-    return sign | code;
-}
-
+// 0x7F/0xFF NaN.  Value of a code (encoding uses the hardware converter
+// after a +-448 clamp; see quant_dev.h).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
     const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
     float v = e == 0 ? static_cast<float>(m) * 0.001953125f

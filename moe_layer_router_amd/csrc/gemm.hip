@@ -673,9 +673,8 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
                            const int* counts, void* act, hipStream_t s) {
     if (block_m == 16) return stream_gateup_launch(L, a, a_scale, T, sorted_ids, offsets, counts, act, s);
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
-    // the copies address activations and one expert's weights with 32-bit offsets
-    if (static_cast<int64_t>(T) * L->D * elem >= (1LL << 32) || 2LL * L->I * L->D * elem >= (1LL << 32))
-        return MOE_ERR_UNSUPPORTED;
+    // the copies address activations and one expert's weights with 32-bit
+    // offsets: the C ABI has checked the byte ranges before any launch
     GemmArgs g{};
     g.offsets = offsets;
     g.counts = counts;
@@ -712,8 +711,6 @@ int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* 
     if (block_m == 16) return stream_down_launch(L, act, act_scale, T, offsets, counts, out_perm, s, act_blocked);
     if (act_blocked) return MOE_ERR_UNSUPPORTED;   // only the streaming kernel reads blocked act codes
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
-    if (max_rows * L->I * elem >= (1LL << 32) || static_cast<int64_t>(L->D) * L->I * elem >= (1LL << 32))
-        return MOE_ERR_UNSUPPORTED;
     GemmArgs g{};
     g.offsets = offsets;
     g.counts = counts;

@@ -17,10 +17,10 @@ __device__ __forceinline__ bf16x8 ld_once(const bf16x8* p) {
 }
 
 // Eight codes with the packed hardware conversion (v_cvt_pk_fp8_f32, round to
-// nearest even) after clamping to +-448.  Over every finite fp32 input this
-// gives the same code as f32_to_e4m3 (common.h), the encoder written from
-// the format definition; an exhaustive sweep of all 2^32 bit patterns on
-// gfx950 found no difference.
+// nearest even, subnormals kept) after clamping to +-448, so that nothing
+// reaches the NaN codes.  The GPU tests compare these codes with an encoder
+// written from the format definition on every bf16 value at scale 1 and at
+// a scale that is not a power of two, and on every rounding midpoint.
 __device__ __forceinline__ float clamp448(float y) { return fminf(fmaxf(y, -448.0f), 448.0f); }
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
     uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);

@@ -76,6 +76,36 @@ def test_validation_happens_before_any_launch():
     assert lib.moe_permute_align(None, 4, 2, 8, 0, 0, None, None, None, None, None, None, None) \
         == L.MOE_ERR_INVALID_ARG
     assert lib.moe_unpermute_combine(None, 2, None, None, 4, 2, 0, 256, None, None) == L.MOE_ERR_INVALID_ARG
+    # a token gathers at most MOE_MAX_TOPK + 1 rows: the check comes before the pointer checks
+    assert lib.moe_unpermute_combine(None, 1, None, None, 4, 17, 1, 256, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine(None, 1, None, None, 4, 18, 0, 256, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine(None, 1, None, None, 4, 16, 1, 256, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_unpermute_combine(None, 1, None, None, 4, 17, 0, 256, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_unpermute_combine(None, 1, None, None, 0, 17, 1, 256, None, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_gemm_byte_ranges_are_checked_before_any_launch():
+    """The LDS-tiled GEMMs address rows with 32-bit byte offsets.  A layer
+    whose shapes exceed them is rejected by moe_forward before it enqueues
+    its first kernel (routing), and has no workspace size."""
+    lib = L.lib()
+    # bf16, D = I = 16384, T = 70000: T*D*2 bytes >= 4 GiB
+    d = _desc(D=16384, I=16384, E=8, top_k=2, quant=0, weight_layout=0, w13_scale=None, w2_scale=None)
+    assert lib.moe_forward_workspace_size(ctypes.byref(d), 70000, 256) == 0
+    lay = L.WsLayout()
+    assert lib.moe_workspace_layout(ctypes.byref(d), 70000, 256, ctypes.byref(lay)) == L.MOE_ERR_UNSUPPORTED
+    # pointers that would fault if anything were launched: nothing is
+    assert lib.moe_forward(ctypes.byref(d), 1 << 24, 1 << 27, 70000, 256, 1 << 25, 1 << 26, 1 << 40, None) \
+        == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_gemm_gateup_silu(ctypes.byref(d), 1, None, 70000, 256, 1, 1, 1, None, 1, None) \
+        == L.MOE_ERR_UNSUPPORTED
+    # FP8 PTPC at D = 4096, I = 16384: max_rows * I bytes of act codes >= 4 GiB
+    d8 = _desc(D=4096, I=16384, E=128, top_k=8)
+    assert lib.moe_forward_workspace_size(ctypes.byref(d8), 40000, 128) == 0
+    assert lib.moe_grouped_gemm_down(ctypes.byref(d8), 1, 1, 40000, 128, 1, 1, None, 1, None) \
+        == L.MOE_ERR_UNSUPPORTED
+    # the weight-streaming kernels (block_m 16) use 64-bit addresses
+    assert lib.moe_forward_workspace_size(ctypes.byref(d8), 64, 16) > 0
 
 
 def test_layer_validation_and_workspace():
