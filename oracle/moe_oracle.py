@@ -67,7 +67,7 @@ __all__ = [
     "LayerSpec", "ExpertBank", "expert_gateup_silu", "expert_down", "combine",
     "moe_forward", "moe_forward_tokens", "relative_l2",
     "E2M1_MAGNITUDES", "e2m1_value", "e2m1_encode", "mxfp4_quant", "mxfp4_payload", "mxfp4_unpack",
-    "fp8_block_payload", "fp8_block_unpack", "ep_payload_bytes",
+    "fp8_block_payload", "fp8_block_unpack", "ep_payload_bytes", "mxfp4_dequant",
 ]
 
 E4M3_MAX = 448.0          # largest finite OCP e4m3fn magnitude (S.1111.110)
@@ -498,7 +498,16 @@ def permute_align(ids, E: int, n_shared: int, block_m: int) -> Dict[str, np.ndar
 # expert computation   [TPU-QWEN35] GMM V2; [QWEN-MI300X] 2.1.1 PTPC
 # --------------------------------------------------------------------------
 
-QUANT_NONE, QUANT_PTPC, QUANT_BLOCK = "bf16", "ptpc_fp8", "block128_fp8"
+QUANT_NONE, QUANT_PTPC, QUANT_BLOCK, QUANT_MXFP4 = "bf16", "ptpc_fp8", "block128_fp8", "mxfp4"
+
+
+def mxfp4_dequant(codes, scale_codes, block: int = 32) -> np.ndarray:
+    """float64 values of MXFP4 data: E2M1 code value * 2^(scale code - 127),
+    one scale per ``block`` consecutive elements of a row ([MI355X-MORI]
+    A4W4: 4-bit weights and activations with E8M0 block scales)."""
+    v = e2m1_value(codes)
+    e = np.asarray(scale_codes, dtype=np.float64) - 127.0
+    return v * np.repeat(np.exp2(e), block, axis=-1)
 
 
 @dataclass
@@ -513,7 +522,7 @@ class LayerSpec:
     topk_groups: int = 1
     renormalize: bool = True
     route_scale: float = 1.0
-    quant: str = QUANT_NONE           # "bf16" | "ptpc_fp8" | "block128_fp8"
+    quant: str = QUANT_NONE           # "bf16" | "ptpc_fp8" | "block128_fp8" | "mxfp4"
 
 
 class ExpertBank:
@@ -522,7 +531,9 @@ class ExpertBank:
     ``master(e)`` returns the bf16-valued master weights (W13 [2I, D] with the
     gate rows first and the up rows after them, W2 [D, I]) as float32 arrays.
     In the FP8 modes the bank quantizes them itself, per output channel (PTPC)
-    or per 128 x 128 block, and keeps the float64 dequantized copies it uses.
+    or per 128 x 128 block, and in the MXFP4 mode to E2M1 codes with one E8M0
+    scale per 32 elements of each row (along the reduction dimension), and
+    keeps the float64 dequantized copies it uses.
     Expert index E is the shared expert when the layer has one.
     """
 
@@ -543,8 +554,11 @@ class ExpertBank:
         elif self.spec.quant == QUANT_BLOCK:
             q13, s13 = quant_weight_blocks(w13, 128)
             q2, s2 = quant_weight_blocks(w2, 128)
+        elif self.spec.quant == QUANT_MXFP4:
+            q13, s13 = mxfp4_quant(w13, 32)
+            q2, s2 = mxfp4_quant(w2, 32)
         else:
-            raise ValueError("not an FP8 layer")
+            raise ValueError("not a quantized layer")
         out = (q13, s13, q2, s2)
         if self.cache:
             self._codes[e] = out
@@ -560,6 +574,8 @@ class ExpertBank:
             q13, s13, q2, s2 = self.quantized(e)
             if self.spec.quant == QUANT_PTPC:
                 out = (dequant_rows(q13, s13), dequant_rows(q2, s2))
+            elif self.spec.quant == QUANT_MXFP4:
+                out = (mxfp4_dequant(q13, s13), mxfp4_dequant(q2, s2))
             else:
                 out = (dequant_weight_blocks(q13, s13), dequant_weight_blocks(q2, s2))
         if self.cache:
@@ -627,21 +643,45 @@ def _act_group(spec: LayerSpec) -> int:
     return 128 if spec.quant == QUANT_BLOCK else 0
 
 
+def _quant_act(spec: LayerSpec, a):
+    """Codes and scales of activation rows: per row / 1x128 group (FP8) or
+    MXFP4 per 32 elements."""
+    if spec.quant == QUANT_MXFP4:
+        return mxfp4_quant(a, 32)
+    return quant_rows(a, _act_group(spec))
+
+
+def _dequant_act(spec: LayerSpec, q, sc):
+    if spec.quant == QUANT_MXFP4:
+        return mxfp4_dequant(q, sc, 32)
+    return dequant_rows(q, sc, _act_group(spec))
+
+
 def _a_rows_of(spec: LayerSpec, xq, sx, x):
     """Dequantized activation rows the GEMMs consume."""
     if spec.quant == QUANT_NONE:
         return np.asarray(x, np.float64)
-    return dequant_rows(xq, sx, _act_group(spec))
+    return _dequant_act(spec, xq, sx)
 
 
 def moe_forward(spec: LayerSpec, bank: ExpertBank, x, logits=None, router_w=None,
-                sel_bias=None, block_m: int = 16) -> Dict[str, np.ndarray]:
+                sel_bias=None, block_m: int = 16, pmap=map,
+                on_expert: Optional[Callable] = None) -> Dict[str, np.ndarray]:
     """Full routed-expert forward over all T tokens, step by step.
 
     x: [T, D] float32 holding bf16 values.  logits: [T, E] fp32, or None with
     router_w [E, D] given (then the router projection runs first).
     Returns every intermediate: logits, ids, w, the permutation dict, xq/sx
     (FP8 modes), act [max_rows, I] (pad rows zero), aq/sa, out_perm and y.
+
+    Experts are independent given the permutation (each writes only its own
+    rows), so the per-expert step may be mapped with ``pmap`` (for example a
+    thread pool's ``map``; the result does not depend on it).  ``on_expert``,
+    when given, is called after each expert as
+    ``on_expert(e, lo, hi, w13, w2, rows)`` with the expert's routed rows
+    [lo, hi), its dequantized weights and ``rows``, a dict of that expert's
+    rows of act, aq/sa (FP8 modes) and out_perm, so a caller can inspect them
+    while the weights are at hand.
     """
     x = np.asarray(x, np.float32)
     T = x.shape[0]
@@ -653,34 +693,46 @@ def moe_forward(spec: LayerSpec, bank: ExpertBank, x, logits=None, router_w=None
     out: Dict[str, np.ndarray] = dict(logits=np.asarray(logits, np.float32), ids=ids, w=w, perm=perm)
     xq = sx = None
     if spec.quant != QUANT_NONE:
-        xq, sx = quant_rows(x, _act_group(spec))
+        xq, sx = _quant_act(spec, x)
         out["xq"], out["sx"] = xq, sx
     a_all = _a_rows_of(spec, xq, sx, x)
     R = perm["max_rows"]
     g = _act_group(spec)
-    fp8 = spec.quant != QUANT_NONE
+    fp8 = spec.quant != QUANT_NONE          # a quantized layer (FP8 or MXFP4)
     act = np.zeros((R, I), np.float32)
     out_perm = np.zeros((R, D), np.float32)
-    if fp8:
+    if spec.quant == QUANT_MXFP4:
+        aq = np.zeros((R, I), np.uint8)
+        sa = np.zeros((R, I // 32), np.uint8)
+    elif fp8:
         aq = np.zeros((R, I), np.uint8)
         sa = np.ones((R,) if g == 0 else (R, I // g), np.float32)
     offs, srt = perm["offsets"], perm["sorted_ids"]
-    for e in range(spec.E + spec.n_shared):
+
+    def one_expert(e):
         lo, hi = int(offs[e]), int(offs[e]) + int(perm["counts"][e])
         if hi == lo:
-            continue
+            return
         f = srt[lo:hi].astype(np.int64)
         rows = np.where(f < T * k, f // max(k, 1), f - T * k)
         w13, w2 = bank.dequantized(e)
         act[lo:hi] = expert_gateup_silu(a_all[rows], w13, I)
         if fp8:
-            # per-row (or per 1x128 group) scales: quantizing one expert's rows
+            # per-row (or per-group) scales: quantizing one expert's rows
             # alone gives the same codes as quantizing the whole buffer
-            aq[lo:hi], sa[lo:hi] = quant_rows(act[lo:hi], g)
-            act_in = dequant_rows(aq[lo:hi], sa[lo:hi], g)
+            aq[lo:hi], sa[lo:hi] = _quant_act(spec, act[lo:hi])
+            act_in = _dequant_act(spec, aq[lo:hi], sa[lo:hi])
         else:
             act_in = act[lo:hi].astype(np.float64)
         out_perm[lo:hi] = expert_down(act_in, w2, fp8)
+        if on_expert is not None:
+            rows_of = dict(act=act[lo:hi], out=out_perm[lo:hi])
+            if fp8:
+                rows_of.update(aq=aq[lo:hi], sa=sa[lo:hi])
+            on_expert(e, lo, hi, w13, w2, rows_of)
+
+    for _ in pmap(one_expert, range(spec.E + spec.n_shared)):
+        pass
     out["act"] = act
     if fp8:
         out["aq"], out["sa"] = aq, sa
@@ -707,11 +759,10 @@ def moe_forward_tokens(spec: LayerSpec, bank: ExpertBank, x_rows, logits_rows,
     res = dict(ids=ids, w=w)
     xq = sx = None
     if spec.quant != QUANT_NONE:
-        xq, sx = quant_rows(x_rows, _act_group(spec))
+        xq, sx = _quant_act(spec, x_rows)
         res["xq"], res["sx"] = xq, sx
     a = _a_rows_of(spec, xq, sx, x_rows)
     out_bf16 = spec.quant != QUANT_NONE
-    g = _act_group(spec)
     y = np.zeros((n, spec.D), np.float32)
     for t in range(n):
         experts = list(ids[t]) + ([spec.E] if spec.n_shared else [])
@@ -720,8 +771,8 @@ def moe_forward_tokens(spec: LayerSpec, bank: ExpertBank, x_rows, logits_rows,
             w13, w2 = bank.dequantized(int(e))
             act = expert_gateup_silu(a[t:t + 1], w13, spec.I)
             if spec.quant != QUANT_NONE:
-                aq, sa = quant_rows(act, g)
-                act = dequant_rows(aq, sa, g)
+                aq, sa = _quant_act(spec, act)
+                act = _dequant_act(spec, aq, sa)
             o.append(expert_down(act, w2, out_bf16)[0])
         o = np.stack(o)
         y[t] = combine(o[None, :spec.top_k], w[t:t + 1],

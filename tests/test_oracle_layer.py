@@ -322,3 +322,124 @@ def test_relative_l2_closed_forms():
     # a NaN anywhere makes the result NaN, so no `err <= tol` gate can pass it
     assert np.isnan(O.relative_l2(np.array([3.0, np.nan]), ref))
     assert not (O.relative_l2(np.array([3.0, np.nan]), ref) <= 1e-2)
+
+
+def test_expert_map_and_hook_do_not_change_the_forward():
+    """moe_forward over a thread pool (pmap) equals the plain loop bitwise, and
+    the per-expert hook sees exactly that expert's rows."""
+    from concurrent.futures import ThreadPoolExecutor
+    spec = O.LayerSpec(D=256, I=128, E=6, top_k=2, n_shared=1, quant="block128_fp8")
+    bank, _, _ = _bank(spec, 41)
+    x = _x(30, 256, 42)
+    logits = np.random.default_rng(43).standard_normal((30, 6)).astype(np.float32)
+    a = O.moe_forward(spec, bank, x, logits, block_m=8)
+    seen = {}
+
+    def hook(e, lo, hi, w13, w2, rows):
+        seen[e] = (lo, hi, rows["act"].copy(), rows["aq"].copy(), rows["out"].copy(), w2.shape)
+
+    with ThreadPoolExecutor(4) as ex:
+        b = O.moe_forward(spec, bank, x, logits, block_m=8, pmap=ex.map, on_expert=hook)
+    for key in ("y", "act", "out_perm"):
+        assert np.array_equal(a[key].view(np.uint32), b[key].view(np.uint32)), key
+    assert np.array_equal(a["aq"], b["aq"])
+    counts, offs = a["perm"]["counts"], a["perm"]["offsets"]
+    assert sorted(seen) == [e for e in range(7) if counts[e] > 0]
+    for e, (lo, hi, act, aq, out, w2s) in seen.items():
+        assert (lo, hi) == (offs[e], offs[e] + counts[e]) and w2s == (256, 128)
+        assert np.array_equal(act, a["act"][lo:hi]) and np.array_equal(aq, a["aq"][lo:hi])
+        assert np.array_equal(out.view(np.uint32), a["out_perm"][lo:hi].view(np.uint32))
+
+
+# ------------------------------------------------------------ MXFP4 layers
+
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _mx_dequant_py(vals):
+    """MXFP4 round trip of a list of values in blocks of 32 (OCP MX v1.0),
+    written out per element: shared scale X = 2^(floor(log2 amax) - 2), each
+    element the nearest E2M1 magnitude of |v| / X (ties to the even mantissa
+    bit, above 6 saturating), sign kept; returns the values code * X."""
+    import math
+    out = []
+    for b0 in range(0, len(vals), 32):
+        blk = [float(v) for v in vals[b0:b0 + 32]]
+        amax = max(abs(v) for v in blk)
+        if amax == 0.0:
+            out += [0.0] * len(blk)
+            continue
+        _, ex = math.frexp(amax)                 # amax = m 2^ex, m in [0.5, 1)
+        X = 2.0 ** max(-127, min(127, ex - 1 - 2))
+        for v in blk:
+            a = abs(v) / X
+            best = min(range(8), key=lambda i: (abs(a - _E2M1_MAG[i]), i % 2))
+            out.append(math.copysign(_E2M1_MAG[best] * X, v))
+    return out
+
+
+def _py_layer_mx(spec, x, logits, w13, w2):
+    """The MXFP4 layer token by token with Python loops: x, the weight rows
+    and each act row in MXFP4 (blocks of 32 along the reduction dimension),
+    fp64 dot products, act = bf16(fp32(silu(g) u)), expert outputs stored
+    bf16, combine j = 0..k-1 then the shared expert, one bf16 rounding."""
+    T = x.shape[0]
+    ids, w = O.route_softmax_topk(logits, spec.top_k)
+    W13 = {e: [_mx_dequant_py(w13[e][n].tolist()) for n in range(2 * spec.I)] for e in range(spec.E + spec.n_shared)}
+    W2 = {e: [_mx_dequant_py(w2[e][d].tolist()) for d in range(spec.D)] for e in range(spec.E + spec.n_shared)}
+    y = np.zeros((T, spec.D), np.float32)
+    for t in range(T):
+        a = _mx_dequant_py(x[t].tolist())
+        experts = [(int(e), float(wt)) for e, wt in zip(ids[t], w[t])]
+        if spec.n_shared:
+            experts.append((spec.E, 1.0))
+        acc = [0.0] * spec.D
+        for e, wt in experts:
+            act = []
+            for i in range(spec.I):
+                g = sum(a[d] * W13[e][i][d] for d in range(spec.D))
+                u = sum(a[d] * W13[e][spec.I + i][d] for d in range(spec.D))
+                act.append(_bf16_t(float(np.float32(g / (1.0 + np.exp(-g)) * u))))
+            aq = _mx_dequant_py(act)
+            for d in range(spec.D):
+                acc[d] += wt * _bf16_t(float(np.float32(sum(aq[i] * W2[e][d][i] for i in range(spec.I)))))
+        y[t] = [_bf16_t(float(np.float32(v))) for v in acc]
+    return y
+
+
+def test_mx_quantizer_matches_the_elementwise_definition():
+    rng = np.random.default_rng(51)
+    x = (rng.standard_normal((6, 96)) * np.exp(rng.standard_normal((6, 1)) * 4)).astype(np.float32)
+    x[1] = 0.0
+    x[2, :32] = 6.0 * 2.0 ** -3                   # an exact block maximum
+    x[3, :32] = np.linspace(-1, 1, 32)
+    codes, sc = O.mxfp4_quant(x, 32)
+    got = O.mxfp4_dequant(codes, sc, 32)
+    ref = np.array([_mx_dequant_py(r.tolist()) for r in x])
+    assert np.array_equal(got, ref)
+
+
+def test_tiny_mxfp4_layer_top2_shared_vs_python_loops():
+    spec = O.LayerSpec(D=64, I=32, E=5, top_k=2, n_shared=1, quant="mxfp4")
+    bank, w13, w2 = _bank(spec, 52)
+    x = _x(6, 64, 53)
+    x[4] = 0.0
+    logits = np.random.default_rng(54).standard_normal((6, 5)).astype(np.float32)
+    out = O.moe_forward(spec, bank, x, logits, block_m=4)
+    ref = _py_layer_mx(spec, x, logits, w13, w2)
+    assert O.relative_l2(out["y"], ref) <= 1e-6
+    assert np.all(out["y"][4] == 0)
+    # the intermediates are codes in 0..15 and E8M0 scale bytes
+    assert out["xq"].max() <= 15 and out["sx"].shape == (6, 2) and out["aq"].max() <= 15
+
+
+def test_mxfp4_identical_experts_give_dense_mlp():
+    spec = O.LayerSpec(D=128, I=64, E=8, top_k=3, quant="mxfp4")
+    bank, w13, w2 = _bank(spec, 55, same=True)
+    x = _x(20, 128, 56)
+    logits = np.random.default_rng(57).standard_normal((20, 8)).astype(np.float32)
+    out = O.moe_forward(spec, bank, x, logits, block_m=4)
+    one = O.LayerSpec(D=128, I=64, E=1, top_k=1, quant="mxfp4")
+    dense = O.moe_forward(one, O.ExpertBank(one, lambda e: (w13[0], w2[0])), x,
+                          np.zeros((20, 1), np.float32), block_m=4)
+    assert O.relative_l2(out["y"], dense["y"]) < 3e-3
