@@ -70,6 +70,7 @@ extern "C" {
 #define MOE_QUANT_NONE_BF16     0  /* bf16 operands, fp32 accumulate            */
 #define MOE_QUANT_PTPC_FP8      1  /* e4m3 per-token x per-output-channel       */
 #define MOE_QUANT_BLOCK128_FP8  2  /* e4m3 1x128 activations, 128x128 weights   */
+#define MOE_QUANT_MXFP4         3  /* E2M1 + E8M0 per 32 along K, both operands  */
 
 /* weight_layout (moe_layer_desc) / layout (moe_quant_weight_fp8) */
 #define MOE_WEIGHTS_ROWS        0  /* row-major                                 */
@@ -91,21 +92,33 @@ extern "C" {
  *   n_shared in {0,1}: the shared expert is expert index E, applied to every
  *   token with weight 1 (not scaled by route_scale).
  *   w13: [E+n_shared, 2I, D] -- rows 0..I-1 the gate projection, rows I..2I-1
- *        the up projection of each expert; bf16 (quant 0) or e4m3 codes.
+ *        the up projection of each expert; bf16 (quant 0) or e4m3 codes;
+ *        quant 3: E2M1 codes, two per byte ([E+n_shared, 2I, D/2] bytes,
+ *        element 2i of a row in the low nibble of byte i).
  *   w13_scale: quant 1: [E+n_shared, 2I] fp32 per output channel;
  *              quant 2: [E+n_shared, 2I/128, D/128] fp32 per 128x128 block;
+ *              quant 3: [E+n_shared, 2I, D/32] E8M0 bytes (a uint8 array
+ *              passed through this pointer), one per 32 elements of a row;
  *              quant 0: NULL.
- *   w2: [E+n_shared, D, I]; w2_scale: [E+n_shared, D] or [.., D/128, I/128].
+ *   w2: [E+n_shared, D, I]; w2_scale: [E+n_shared, D] or [.., D/128, I/128]
+ *        (quant 3: codes [E+n_shared, D, I/2] bytes, scales [.., D, I/32]).
+ *   MXFP4 (quant 3, the A4W4 FusedMoE of the MI355X MoRI page, OCP
+ *   Microscaling v1.0): activations, weights and the re-quantized act are
+ *   all E2M1 with an E8M0 scale 2^e per 32 elements along the reduction
+ *   dimension, e = floor(log2(amax)) - 2 clamped to [-127, 127]; the matrix
+ *   cores apply both scales.  I % 256 == 0; block_m >= 32 (the LDS-tiled
+ *   kernels; moe_default_block_m never picks 16 for it).
  *   weight_layout: order of the bytes of each [N, K] weight matrix (w13:
- *              N = 2I, K = D; w2: N = D, K = I):
+ *              N = 2I, K = D; w2: N = D, K = I; K_bytes = K, or K/2 for MXFP4):
  *              MOE_WEIGHTS_ROWS    row-major, K contiguous;
  *              MOE_WEIGHTS_BLOCKED blocks of 16 rows x 128 bytes (the unit
  *              the expert GEMMs read per step), the byte (n, b) of a row at
  *              ((n/16) * (K_bytes/128) + b/128) * 2048 + o(n%16, b%128)
  *              with o(r, c) = (r/2 + 8 * (c/64)) * 128 +
  *              ((r%2) * 4 + (c%64)/16) * 16 + c%16: each 128-byte line of
- *              a block holds one 64-byte K half of two consecutive rows.  FP8 modes only (N % 16 == 0 and
- *              K a multiple of 128 there); moe_quant_weight_fp8 writes it.
+ *              a block holds one 64-byte K half of two consecutive rows.
+ *              Quantized modes only (N % 16 == 0, K_bytes % 128 == 0);
+ *              moe_quant_weight_fp8 / moe_quant_weight_mxfp4 write it.
  *   router_w: [E, D] fp32 router gate, used by moe_forward when it is given
  *             no logits (may be NULL otherwise).
  *   sel_bias: [E] fp32 selection-only bias of grouped-sigmoid routing or NULL.
@@ -169,6 +182,25 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
                        void* stream);
 
 /*
+ * Router projection fused with top-k routing and the FP8 quantization of x,
+ * in one launch (router gate of the Qwen 3.5 MoE paragraph; the page's
+ * roadmap item puts the top-k selection where the scores are computed).
+ * For the layer L (L->router_w required; E <= 512, D % 64 == 0, else
+ * MOE_ERR_UNSUPPORTED) and x [T, D] bf16:
+ *   logits [T, E] fp32: x . router_w on the matrix cores; each fp32 weight
+ *     is split exactly into three bf16 pieces, so the products are exact and
+ *     only fp32 accumulation rounds (|error| within 1e-6 of sum_d
+ *     |x[t, d] * router_w[e, d]|, far tighter in practice);
+ *   topk_ids, topk_w [T, k]: moe_route_topk of those logits (bit for bit);
+ *   FP8 layers: xq [T, D] codes and xs [T] or [T, D/128] scales, as
+ *     moe_quant_ptpc_fp8 (xq, xs may be NULL for a bf16 layer).
+ * moe_forward uses it when it is given no logits and T is above the
+ * small-batch sizes (those project in fp64 per token, moe_router_logits).
+ */
+int32_t moe_router_front(const moe_layer_desc* L, const void* x_bf16, int32_t T, float* logits,
+                         int32_t* topk_ids, float* topk_w, uint8_t* xq, float* xs, void* stream);
+
+/*
  * Host-only: rows of the padded permuted buffer, an upper bound valid for any
  * routing: block_m * min(floor((A' + E'(block_m-1)) / block_m), A') with
  * A' = T(k + n_shared), E' = E + n_shared.  Returns -1 on invalid input.
@@ -213,6 +245,29 @@ int32_t moe_quant_ptpc_fp8(const void* x_bf16, int64_t M, int32_t K, int32_t gro
                            const int32_t* valid_rows, uint8_t* q, float* scale, void* stream);
 
 /*
+ * MXFP4 quantization of bf16 rows (OCP Microscaling v1.0; the A4W4 expert
+ * arithmetic of the MI355X MoRI page, "FlyDSL FusedMoE").  x: [M, K] bf16,
+ * K % 128 == 0, K <= 65536.  Per block of 32 consecutive elements of a row:
+ * amax = max|x|, e = floor(log2(amax)) - 2 clamped to [-127, 127] (-127 for
+ * an all-zero block), scale byte e + 127, codes = E2M1 of x / 2^e (exact
+ * division) rounded to nearest, ties to the even mantissa, saturating to
+ * +-6, sign of zero kept.  Outputs q [M, K/2] (element 2i in the low nibble
+ * of byte i) and scale [M, K/32] bytes.  valid_rows as in moe_quant_ptpc_fp8.
+ */
+int32_t moe_quant_mxfp4(const void* x_bf16, int64_t M, int32_t K, const int32_t* valid_rows, uint8_t* q,
+                        uint8_t* scale, void* stream);
+
+/*
+ * Offline MXFP4 quantization of bf16 weights [n_mats, N, K] along K (the
+ * reduction dimension), the arithmetic of moe_quant_mxfp4: codes q
+ * [n_mats, N, K/2] bytes (layout MOE_WEIGHTS_ROWS, or MOE_WEIGHTS_BLOCKED on
+ * the byte matrix: N % 16 == 0, K % 256 == 0), scale [n_mats, N, K/32] E8M0
+ * bytes.
+ */
+int32_t moe_quant_weight_mxfp4(const void* w_bf16, int64_t n_mats, int32_t N, int32_t K, int32_t layout,
+                               uint8_t* q, uint8_t* scale, void* stream);
+
+/*
  * Offline FP8 quantization of bf16 weights [n_mats, N, K] (row n of a matrix
  * is output channel n).  quant 1 (PTPC): one scale per row, scale
  * [n_mats, N]; quant 2: one scale per 128x128 block, scale
@@ -230,7 +285,8 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
  *   [g | u] = A[t] . W13[e]^T (fp32 accumulate, dequantized by the row's
  *   activation scale and the weight scales), act[r] = bf16(silu(g) * u).
  * a: quant 0: x bf16 [T, D]; quant 1/2: codes [T, D] with a_scale [T] or
- * [T, D/128].  act: [R, I] bf16 where R = moe_permute_max_rows(...).
+ * [T, D/128]; quant 3: codes [T, D/2] with E8M0 bytes [T, D/32] passed as
+ * a_scale.  act: [R, I] bf16 where R = moe_permute_max_rows(...).
  * expert_counts (device, [E+n_shared], as moe_permute_align writes it; may
  * be NULL) lets the LDS-tiled kernels skip the 32-row tiles at the end of an
  * expert's segment that hold only pads; it must match expert_offsets.
@@ -239,8 +295,8 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
  * kernels; their contents are then unspecified); rows at or past
  * expert_offsets[E'] are not written.  block_m must equal the block_m of moe_permute_align and be one
  * of: 16 (weight-streaming kernels for small batches: each weight byte is
- * read once per 64 rows of its expert), 32, 64, 128 or 256 (LDS-tiled
- * kernels).  Shapes: I % 128 == 0 and D % 256 == 0.
+ * read once per 64 rows of its expert; not for MXFP4), 32, 64, 128 or 256
+ * (LDS-tiled kernels).  Shapes: I % 128 == 0 (MXFP4: 256) and D % 256 == 0.
  */
 int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
                                      const float* a_scale, int32_t T, int32_t block_m,
@@ -256,8 +312,9 @@ int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
  * out_perm are 0, or unspecified in pad-only 32-row tiles (as for act); with
  * expert_counts NULL every row of a segment is computed, so pad rows of
  * out_perm are 0 only where the pad rows of act hold zeros.  act: quant 0:
- * bf16 [R, I]; quant 1/2: codes [R, I] with act_scale [R] or [R, I/128].
- * out_perm [R, D]: fp32 for quant 0, bf16 for quant 1/2.
+ * bf16 [R, I]; quant 1/2: codes [R, I] with act_scale [R] or [R, I/128];
+ * quant 3: codes [R, I/2] with E8M0 bytes [R, I/32] passed as act_scale.
+ * out_perm [R, D]: fp32 for quant 0, bf16 for quant 1/2/3.
  */
 int32_t moe_grouped_gemm_down(const moe_layer_desc* L, const void* act, const float* act_scale,
                               int32_t T, int32_t block_m, const int32_t* block_expert,

@@ -15,8 +15,9 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 SCORING_SOFTMAX, SCORING_SIGMOID_GROUPED = 0, 1
-QUANT_NONE_BF16, QUANT_PTPC_FP8, QUANT_BLOCK128_FP8 = 0, 1, 2
-QUANT_CODES = {"bf16": QUANT_NONE_BF16, "ptpc_fp8": QUANT_PTPC_FP8, "block128_fp8": QUANT_BLOCK128_FP8}
+QUANT_NONE_BF16, QUANT_PTPC_FP8, QUANT_BLOCK128_FP8, QUANT_MXFP4 = 0, 1, 2, 3
+QUANT_CODES = {"bf16": QUANT_NONE_BF16, "ptpc_fp8": QUANT_PTPC_FP8, "block128_fp8": QUANT_BLOCK128_FP8,
+               "mxfp4": QUANT_MXFP4}
 WEIGHTS_ROWS, WEIGHTS_BLOCKED = 0, 1
 LAYOUT_CODES = {"rows": WEIGHTS_ROWS, "blocked": WEIGHTS_BLOCKED}
 PAYLOAD_MXFP4, PAYLOAD_FP8_BLOCK = 0, 1
@@ -41,6 +42,8 @@ class WsLayout(ctypes.Structure):
 SIGNATURES = {
     "moe_status_str": (c_char_p, [c_int32]),
     "moe_router_logits": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "moe_router_front": (c_int32, [POINTER(LayerDesc), c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p]),
     "moe_route_topk": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                  c_int32, c_float, c_void_p, c_void_p, c_void_p]),
     "moe_permute_max_rows": (c_int64, [c_int32, c_int32, c_int32, c_int32, c_int32]),
@@ -49,6 +52,9 @@ SIGNATURES = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_quant_ptpc_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                      c_void_p]),
+    "moe_quant_mxfp4": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_quant_weight_mxfp4": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                         c_void_p]),
     "moe_quant_weight_fp8": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                        c_void_p, c_void_p]),
     "moe_grouped_gemm_gateup_silu": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_int32,

@@ -18,6 +18,8 @@ int32_t quant_wrows_launch(const uint16_t* w, int64_t M, int K, bool blocked, ui
 int32_t quant_rows_launch(const uint16_t* x, int64_t M, int K, int group, const int* valid_rows, uint8_t* q,
                           float* scale, hipStream_t s, bool blocked = false, const int* skip_ids = nullptr,
                           int skip_id = 0);
+int32_t quant_mx_rows_launch(const uint16_t* x, int64_t M, int K, const int* valid_rows, bool blocked,
+                             const int* skip_ids, int skip_id, uint8_t* q, uint8_t* scale, hipStream_t s);
 int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, bool blocked, uint8_t* q, float* scale,
                             hipStream_t s);
 bool front_small_ok(int T, int k, int n_shared);
@@ -34,6 +36,9 @@ int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* 
                          void* out_perm, hipStream_t s, bool act_blocked = false);
 int32_t combine_launch(const void* out_perm, int out_dtype, const int* inv_perm, const float* topk_w, int T,
                        int k, int n_shared, int D, uint16_t* y, hipStream_t s);
+bool router_front_ok(int E, int D);
+int32_t router_front_launch(const moe_layer_desc* L, const void* x, int T, int group, float* logits, int* ids,
+                            float* w, uint8_t* xq, float* xs, hipStream_t s);
 int64_t ep_payload_row_bytes(int D, int format);
 int32_t ep_pack_launch(const uint16_t* x, int T, int D, int format, uint8_t* payload, hipStream_t s);
 int32_t ep_unpack_launch(const uint8_t* payload, int T, int D, int format, uint16_t* x, hipStream_t s);
@@ -83,7 +88,7 @@ int32_t check_layer(const moe_layer_desc* L) {
     if (st != MOE_OK) return st;
     MOE_CHECK_SUP(L->E + L->n_shared <= MOE_MAX_EXPERTS);
     MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || L->quant == MOE_QUANT_PTPC_FP8 ||
-                  L->quant == MOE_QUANT_BLOCK128_FP8);
+                  L->quant == MOE_QUANT_BLOCK128_FP8 || L->quant == MOE_QUANT_MXFP4);
     MOE_CHECK_ARG(L->w13 != nullptr && L->w2 != nullptr);
     if (L->quant != MOE_QUANT_NONE_BF16) MOE_CHECK_ARG(L->w13_scale != nullptr && L->w2_scale != nullptr);
     MOE_CHECK_ARG(L->weight_layout == MOE_WEIGHTS_ROWS || L->weight_layout == MOE_WEIGHTS_BLOCKED);
@@ -91,7 +96,28 @@ int32_t check_layer(const moe_layer_desc* L) {
     // column tiles of the grouped GEMMs: 128 act columns, 256 output columns
     MOE_CHECK_SUP(L->I % 128 == 0 && L->D % 256 == 0);
     MOE_CHECK_SUP(L->D <= 16384 && L->I <= 16384);
+    // MXFP4: each 128-byte step of the tiled GEMMs is 256 elements
+    if (L->quant == MOE_QUANT_MXFP4) MOE_CHECK_SUP(L->I % 256 == 0);
     return MOE_OK;
+}
+
+// The activation format of the layer's quantizers: -1 none (bf16), 0 PTPC
+// (fp32 scale per row), 128 (fp32 scale per 1x128 group), 32 (MXFP4).
+int act_group(const moe_layer_desc* L) {
+    switch (L->quant) {
+        case MOE_QUANT_PTPC_FP8: return 0;
+        case MOE_QUANT_BLOCK128_FP8: return 128;
+        case MOE_QUANT_MXFP4: return 32;
+        default: return -1;
+    }
+}
+
+// the weight-streaming kernels (block_m 16) cover bf16 and the FP8 modes;
+// MXFP4 runs the LDS-tiled kernels up to 128-row tiles (the 256-row tile's
+// scale words do not fit its registers)
+bool block_m_ok_for(const moe_layer_desc* L, int block_m) {
+    if (L->quant == MOE_QUANT_MXFP4) return block_m == 32 || block_m == 64 || block_m == 128;
+    return block_m_ok(block_m);
 }
 
 // The LDS-tiled GEMMs address the activation rows and one expert's weights
@@ -100,7 +126,7 @@ int32_t check_layer(const moe_layer_desc* L) {
 // any launch of a call.
 bool gemm_ranges_ok(const moe_layer_desc* L, int64_t T, int block_m, int64_t R) {
     if (block_m == 16) return true;
-    const int64_t elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    const int64_t elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;   // (MXFP4: half a byte, within this)
     const int64_t lim = 1LL << 32;
     return T * L->D * elem < lim && 2LL * L->I * L->D * elem < lim &&   // gate/up
            R * L->I * elem < lim;                                        // down (its weights are half of W13)
@@ -119,8 +145,9 @@ void layout_of(const moe_layer_desc* L, int T, int B, moe_ws_layout* o) {
     const int64_t k = L->top_k, E = L->E, Ep = E + L->n_shared, D = L->D, I = L->I;
     const int64_t A = static_cast<int64_t>(T) * (k + L->n_shared);
     const int64_t R = max_rows_of(T, k, E, L->n_shared, B);
-    const bool fp8 = L->quant != MOE_QUANT_NONE_BF16;
+    const bool fp8 = L->quant != MOE_QUANT_NONE_BF16;     // any quantized mode
     const bool blk = L->quant == MOE_QUANT_BLOCK128_FP8;
+    const bool mx = L->quant == MOE_QUANT_MXFP4;
     Carver c;
     o->logits = c.take(static_cast<int64_t>(T) * E * 4);
     o->topk_ids = c.take(T * k * 4);
@@ -130,11 +157,21 @@ void layout_of(const moe_layer_desc* L, int T, int B, moe_ws_layout* o) {
     o->sorted_ids = c.take(R * 4);
     o->block_expert = c.take(R / B * 4);
     o->inv_perm = c.take(A * 4);
-    o->xq = fp8 ? c.take(static_cast<int64_t>(T) * D) : -1;
-    o->xs = fp8 ? c.take(static_cast<int64_t>(T) * (blk ? D / 128 : 1) * 4) : -1;
+    if (mx) {
+        o->xq = c.take(static_cast<int64_t>(T) * D / 2);
+        o->xs = c.take(static_cast<int64_t>(T) * D / 32);
+    } else {
+        o->xq = fp8 ? c.take(static_cast<int64_t>(T) * D) : -1;
+        o->xs = fp8 ? c.take(static_cast<int64_t>(T) * (blk ? D / 128 : 1) * 4) : -1;
+    }
     o->act = c.take(R * I * 2);
-    o->aq = fp8 ? c.take(R * I) : -1;
-    o->as = fp8 ? c.take(R * (blk ? I / 128 : 1) * 4) : -1;
+    if (mx) {
+        o->aq = c.take(R * I / 2);
+        o->as = c.take(R * I / 32);
+    } else {
+        o->aq = fp8 ? c.take(R * I) : -1;
+        o->as = fp8 ? c.take(R * (blk ? I / 128 : 1) * 4) : -1;
+    }
     o->out_perm = c.take(R * D * (fp8 ? 2 : 4));
     o->scratch = c.take(static_cast<int64_t>(permute_scratch_bytes(T, static_cast<int>(k), L->n_shared,
                                                                     static_cast<int>(E))));
@@ -180,6 +217,20 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
                              topk_ids, topk_w, as_stream(stream));
 }
 
+int32_t moe_router_front(const moe_layer_desc* L, const void* x_bf16, int32_t T, float* logits,
+                         int32_t* topk_ids, float* topk_w, uint8_t* xq, float* xs, void* stream) {
+    int32_t st = check_layer(L);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(T >= 0 && L->router_w != nullptr);
+    MOE_CHECK_SUP(router_front_ok(L->E, L->D));
+    if (T == 0) return MOE_OK;
+    const bool fp8 = L->quant != MOE_QUANT_NONE_BF16;
+    MOE_CHECK_ARG(x_bf16 && logits && topk_ids && topk_w);
+    if (fp8) MOE_CHECK_ARG(xq && xs);
+    return router_front_launch(L, x_bf16, T, act_group(L), logits, topk_ids, topk_w, fp8 ? xq : nullptr,
+                               fp8 ? xs : nullptr, as_stream(stream));
+}
+
 int64_t moe_permute_max_rows(int32_t T, int32_t k, int32_t E, int32_t n_shared, int32_t block_m) {
     if (T < 0 || k <= 0 || E <= 0 || n_shared < 0 || n_shared > 1 || block_m <= 0) return -1;
     return max_rows_of(T, k, E, n_shared, block_m);
@@ -215,6 +266,30 @@ int32_t moe_quant_ptpc_fp8(const void* x_bf16, int64_t M, int32_t K, int32_t gro
                              as_stream(stream));
 }
 
+int32_t moe_quant_mxfp4(const void* x_bf16, int64_t M, int32_t K, const int32_t* valid_rows, uint8_t* q,
+                        uint8_t* scale, void* stream) {
+    MOE_CHECK_ARG(M >= 0 && K > 0);
+    MOE_CHECK_SUP(K % 128 == 0 && K <= 65536);
+    MOE_CHECK_SUP(M < (1LL << 31) * 4);
+    if (M == 0) return MOE_OK;
+    MOE_CHECK_ARG(x_bf16 && q && scale);
+    return quant_mx_rows_launch(static_cast<const uint16_t*>(x_bf16), M, K, valid_rows, false, nullptr, 0, q, scale,
+                                as_stream(stream));
+}
+
+int32_t moe_quant_weight_mxfp4(const void* w_bf16, int64_t n_mats, int32_t N, int32_t K, int32_t layout, uint8_t* q,
+                               uint8_t* scale, void* stream) {
+    MOE_CHECK_ARG(n_mats >= 0 && N > 0 && K > 0);
+    MOE_CHECK_ARG(layout == MOE_WEIGHTS_ROWS || layout == MOE_WEIGHTS_BLOCKED);
+    MOE_CHECK_SUP(K % 128 == 0 && K <= 65536);
+    const bool blocked = layout == MOE_WEIGHTS_BLOCKED;
+    if (blocked) MOE_CHECK_SUP(N % 16 == 0 && K % 256 == 0);
+    if (n_mats == 0) return MOE_OK;
+    MOE_CHECK_ARG(w_bf16 && q && scale);
+    return quant_mx_rows_launch(static_cast<const uint16_t*>(w_bf16), n_mats * N, K, nullptr, blocked, nullptr, 0, q,
+                                scale, as_stream(stream));
+}
+
 int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int32_t K, int32_t quant,
                              int32_t layout, uint8_t* q, float* scale, void* stream) {
     MOE_CHECK_ARG(n_mats >= 0 && N > 0 && K > 0);
@@ -242,7 +317,7 @@ int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a, con
     int32_t st = check_layer(L);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(T >= 0);
-    MOE_CHECK_SUP(block_m_ok(block_m));
+    MOE_CHECK_SUP(block_m_ok_for(L, block_m));
     if (T == 0) return MOE_OK;
     MOE_CHECK_ARG(a && sorted_ids && block_expert && expert_offsets && act_bf16);
     MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || a_scale);
@@ -259,7 +334,7 @@ int32_t moe_grouped_gemm_down(const moe_layer_desc* L, const void* act, const fl
     int32_t st = check_layer(L);
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(T >= 0);
-    MOE_CHECK_SUP(block_m_ok(block_m));
+    MOE_CHECK_SUP(block_m_ok_for(L, block_m));
     if (T == 0) return MOE_OK;
     MOE_CHECK_ARG(act && block_expert && expert_offsets && out_perm);
     MOE_CHECK_ARG(L->quant == MOE_QUANT_NONE_BF16 || act_scale);
@@ -286,10 +361,10 @@ int32_t moe_default_block_m(const moe_layer_desc* L, int32_t T) {
     if (!L || L->E <= 0 || T < 0) return 64;
     const int64_t rows = static_cast<int64_t>(T) * (L->top_k + L->n_shared);
     const int64_t per_expert = rows / (L->E + L->n_shared);
-    if (T <= kStreamMaxT) return 16;
+    if (T <= kStreamMaxT) return L->quant == MOE_QUANT_MXFP4 ? 32 : 16;
     // 32-row tiles of pads are skipped, so a tall tile costs little beyond
     // the expert's rows and reads each weight tile once per 256 rows
-    if (per_expert >= 96) return 256;
+    if (per_expert >= 96) return L->quant == MOE_QUANT_MXFP4 ? 128 : 256;
     if (per_expert >= 48) return 128;
     return 32;
 }
@@ -297,7 +372,7 @@ int32_t moe_default_block_m(const moe_layer_desc* L, int32_t T) {
 size_t moe_forward_workspace_size(const moe_layer_desc* L, int32_t T, int32_t block_m) {
     if (check_layer(L) != MOE_OK || T < 0) return 0;
     if (block_m == 0) block_m = moe_default_block_m(L, T);
-    if (!block_m_ok(block_m)) return 0;
+    if (!block_m_ok_for(L, block_m)) return 0;
     moe_ws_layout o;
     layout_of(L, T, block_m, &o);
     if (!gemm_ranges_ok(L, T, block_m, o.max_rows)) return 0;
@@ -309,7 +384,7 @@ int32_t moe_workspace_layout(const moe_layer_desc* L, int32_t T, int32_t block_m
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(T >= 0 && out);
     if (block_m == 0) block_m = moe_default_block_m(L, T);
-    MOE_CHECK_SUP(block_m_ok(block_m));
+    MOE_CHECK_SUP(block_m_ok_for(L, block_m));
     layout_of(L, T, block_m, out);
     MOE_CHECK_SUP(gemm_ranges_ok(L, T, block_m, out->max_rows));
     return MOE_OK;
@@ -321,7 +396,7 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     if (st != MOE_OK) return st;
     MOE_CHECK_ARG(T >= 0);
     if (block_m == 0) block_m = moe_default_block_m(L, T);
-    MOE_CHECK_SUP(block_m_ok(block_m));
+    MOE_CHECK_SUP(block_m_ok_for(L, block_m));
     const int64_t A = static_cast<int64_t>(T) * (L->top_k + L->n_shared);
     MOE_CHECK_SUP(A < (1LL << 30));
     if (T == 0) return MOE_OK;
@@ -340,12 +415,18 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     auto at = [&](int64_t off) { return static_cast<void*>(ws + off); };
     const int k = L->top_k, E = L->E, Ep = E + L->n_shared;
-    const bool fp8 = L->quant != MOE_QUANT_NONE_BF16;
-    const int group = L->quant == MOE_QUANT_BLOCK128_FP8 ? 128 : 0;
+    const bool fp8 = L->quant != MOE_QUANT_NONE_BF16;     // any quantized mode (FP8 or MXFP4)
+    const int group = act_group(L);
 
+    // Without logits: batches that take the small-batch front end run the
+    // per-token fp64 router projection first; larger ones route in the fused
+    // router kernel (projection on the matrix cores, top-k and x
+    // quantization in the same launch).
+    const bool small_front = block_m == 16 && front_small_ok(T, k, L->n_shared);
+    const bool fused_router = !logits_or_null && !small_front && router_front_ok(E, L->D);
+    float* lg = static_cast<float*>(at(o.logits));
     const float* logits = logits_or_null;
-    if (!logits) {
-        float* lg = static_cast<float*>(at(o.logits));
+    if (!logits && !fused_router) {
         if ((st = router_logits_launch(static_cast<const uint16_t*>(x_bf16), L->router_w, T, L->D, E, lg, s)) != MOE_OK)
             return st;
         logits = lg;
@@ -358,7 +439,7 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     int* inv = static_cast<int*>(at(o.inv_perm));
     const void* a = fp8 ? at(o.xq) : x_bf16;
     const float* a_scale = fp8 ? static_cast<float*>(at(o.xs)) : nullptr;
-    if (block_m == 16 && front_small_ok(T, k, L->n_shared)) {
+    if (small_front) {
         // small batch: routing, permutation and x quantization in one launch
         if ((st = front_small_launch(L, x_bf16, logits, T, block_m, static_cast<int>(o.max_rows), ids, w,
                                      static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv,
@@ -366,12 +447,17 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
                                      fp8 ? static_cast<float*>(at(o.xs)) : nullptr, s)) != MOE_OK)
             return st;
     } else {
-        // routing and x quantization in one launch (one workgroup per token),
-        // then the multi-kernel permutation
-        if ((st = front_route_quant_launch(L, x_bf16, logits, T, ids, w,
-                                           fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr,
-                                           fp8 ? static_cast<float*>(at(o.xs)) : nullptr, s)) != MOE_OK)
+        // routing and x quantization in one launch (with the router
+        // projection when there are no logits), then the multi-kernel
+        // permutation
+        uint8_t* xq = fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr;
+        float* xs = fp8 ? static_cast<float*>(at(o.xs)) : nullptr;
+        if (fused_router) {
+            if ((st = router_front_launch(L, x_bf16, T, group, lg, ids, w, xq, xs, s)) != MOE_OK)
+                return st;
+        } else if ((st = front_route_quant_launch(L, x_bf16, logits, T, ids, w, xq, xs, s)) != MOE_OK) {
             return st;
+        }
         if ((st = permute_align_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
                                        static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, at(o.scratch),
                                        s)) != MOE_OK)
@@ -391,10 +477,16 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     // quantized for it.
     const bool aq_blocked = fp8 && block_m == 16;
     if (fp8) {
-        if ((st = quant_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, group, offsets + Ep,
-                                    static_cast<uint8_t*>(at(o.aq)), static_cast<float*>(at(o.as)), s, aq_blocked,
-                                    block_m == 16 ? nullptr : sorted, T * (k + L->n_shared))) != MOE_OK)
-            return st;
+        if (group == 32) {
+            st = quant_mx_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, offsets + Ep, false, sorted,
+                                      T * (k + L->n_shared), static_cast<uint8_t*>(at(o.aq)),
+                                      static_cast<uint8_t*>(at(o.as)), s);
+        } else {
+            st = quant_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, group, offsets + Ep,
+                                   static_cast<uint8_t*>(at(o.aq)), static_cast<float*>(at(o.as)), s, aq_blocked,
+                                   block_m == 16 ? nullptr : sorted, T * (k + L->n_shared));
+        }
+        if (st != MOE_OK) return st;
         act_in = at(o.aq);
         act_scale = static_cast<float*>(at(o.as));
     }

@@ -19,8 +19,6 @@
 // aligned).
 #include "quant_dev.h"
 
-#include <type_traits>
-
 namespace moe {
 
 // 16-byte vectors per lane loaded before any is used: the unpack kernels
@@ -29,36 +27,6 @@ namespace moe {
 // loads; holding 8 vectors measured 18.8 -> 24.9 us for the FP8 pack of
 // 8192 x 4096)
 constexpr int kPackUnroll = 1, kUnpackUnroll = 8;
-
-// value of an E2M1 code: exponent field 0 is 0 or 0.5, else (1 + m/2) * 2^(e-1)
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-    const uint32_t e = (c >> 1) & 3, m = c & 1;
-    const float mag = e == 0 ? 0.5f * static_cast<float>(m) : __uint_as_float(((e + 126) << 23) | (m << 22));
-    return (c & 8) ? -mag : mag;
-}
-
-// 2^k as fp32 for k in [-127, 127] (2^-127 is a subnormal)
-__device__ __forceinline__ float exp2i(int k) {
-    return k >= -126 ? __uint_as_float(static_cast<uint32_t>(k + 127) << 23) : __uint_as_float(0x00400000u);
-}
-
-// floor(log2(a)) for finite a > 0, from the exponent field (subnormals by
-// the position of their leading mantissa bit)
-__device__ __forceinline__ int floor_log2(float a) {
-    const uint32_t b = __float_as_uint(a);
-    const int ef = static_cast<int>((b >> 23) & 0xFF);
-    return ef > 0 ? ef - 127 : (31 - __clz(b & 0x7FFFFF)) - 149;
-}
-
-// f(0) .. f(3) with compile-time indices (the conversion's byte selector
-// must be a constant)
-template <typename F>
-__device__ __forceinline__ void static_for_pk(F&& f) {
-    f(std::integral_constant<int, 0>{});
-    f(std::integral_constant<int, 1>{});
-    f(std::integral_constant<int, 2>{});
-    f(std::integral_constant<int, 3>{});
-}
 
 __global__ void __launch_bounds__(256) ep_pack_mxfp4_kernel(const uint16_t* __restrict__ x, int T, int D,
                                                             uint8_t* __restrict__ payload) {
@@ -83,20 +51,8 @@ __global__ void __launch_bounds__(256) ep_pack_mxfp4_kernel(const uint16_t* __re
             float m = amax8(v[i]);
             m = fmaxf(m, __shfl_xor(m, 1, 64));
             m = fmaxf(m, __shfl_xor(m, 2, 64));
-            const int e = m > 0.0f ? max(floor_log2(m) - 2, -127) : -127;
-            const float inv = exp2i(-e);      // x / 2^e, exact (a power of two)
-            // E2M1 codes of the scaled elements, two per byte (element 2j in
-            // the low nibble of byte j) by the hardware conversion
-            // (v_cvt_scalef32_pk_fp4_f32 with scale 1: round to nearest, ties
-            // to the even mantissa, saturating to +-6, sign of zero kept),
-            // which matches the E2M1 encoder written from the format
-            // definition on every bf16-representable value (tested)
-            uint32_t w = 0;
-            static_for_pk([&](auto J) {
-                constexpr int j = decltype(J)::value;
-                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16_to_f32(v[i].v[2 * j]) * inv,
-                                                             bf16_to_f32(v[i].v[2 * j + 1]) * inv, 1.0f, j);
-            });
+            const int e = mx_exponent(m);
+            const uint32_t w = mx_codes8(v[i], exp2i(-e));   // x / 2^e, exact (a power of two)
             // the scale bytes of 4 consecutive blocks (lanes l, l+4, l+8, l+12)
             // go out as one word from lane l, l % 16 == 0
             const uint32_t sb = static_cast<uint32_t>(e + 127);

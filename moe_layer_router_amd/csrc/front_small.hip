@@ -47,67 +47,7 @@ struct FrontArgs {
     float* xs;                 // scales [T] or [T, D/128]
 };
 
-// One row of x into codes with the wave, in chunks of 4096 elements (8
-// vectors of 8 per lane, all loads of a chunk in flight together).  GROUP 0
-// (one scale per row): amax over the chunks, then codes (a single-chunk row
-// stays in registers, longer rows are read again); GROUP 128: one pass,
-// 16-lane groups.
-template <int GROUP>
-__device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, int K, uint8_t* __restrict__ qr,
-                                               float* __restrict__ sr, int lane) {
-    constexpr int CV = 8;
-    const int nvec = K >> 3;
-    const int nch = (nvec + 64 * CV - 1) / (64 * CV);
-    const bf16x8* xv = reinterpret_cast<const bf16x8*>(xr);
-    uint2* qv = reinterpret_cast<uint2*>(qr);
-    bf16x8 v[CV];
-    auto load = [&](int ch) {
-#pragma unroll
-        for (int i = 0; i < CV; ++i) {
-            const int c = ch * 64 * CV + lane + 64 * i;
-            v[i] = c < nvec ? xv[c] : bf16x8{};
-        }
-    };
-    if constexpr (GROUP == 0) {
-        float m = 0.0f;
-        for (int ch = 0; ch < nch; ++ch) {
-            load(ch);
-#pragma unroll
-            for (int i = 0; i < CV; ++i) m = fmaxf(m, amax8(v[i]));
-        }
-        m = wave_max(m);
-        float sc, inv;
-        scale_pair(m, sc, inv);
-        for (int ch = 0; ch < nch; ++ch) {
-            if (nch > 1) load(ch);
-#pragma unroll
-            for (int i = 0; i < CV; ++i) {
-                const int c = ch * 64 * CV + lane + 64 * i;
-                if (c < nvec) qv[c] = quant8(v[i], inv);
-            }
-        }
-        if (lane == 0) sr[0] = sc;
-    } else {
-        for (int ch = 0; ch < nch; ++ch) {
-            load(ch);
-#pragma unroll
-            for (int i = 0; i < CV; ++i) {
-                const int c = ch * 64 * CV + lane + 64 * i;
-                float m = amax8(v[i]);
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-                float sc, inv;
-                scale_pair(m, sc, inv);
-                if (c < nvec) {
-                    qv[c] = quant8(v[i], inv);
-                    if ((lane & 15) == 0) sr[c >> 4] = sc;
-                }
-            }
-        }
-    }
-}
-
-// GROUP: -1 (bf16 layer, no quantization), 0 (per row), 128 (1x128).
+// GROUP: -1 (bf16 layer, no quantization), 0 (per row), 128 (1x128), 32 (MXFP4).
 template <int EPL, int SCORING, int GROUP>
 __global__ void __launch_bounds__(128) token_front_kernel(const FrontArgs p) {
     const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -121,9 +61,7 @@ __global__ void __launch_bounds__(128) token_front_kernel(const FrontArgs p) {
             p.w[t * p.k + lane] = wt;
         }
     } else if constexpr (GROUP >= 0) {
-        const int ng = GROUP == 0 ? 1 : p.D / 128;
-        quant_row_wave<GROUP>(p.x + static_cast<int64_t>(t) * p.D, p.D, p.xq + static_cast<int64_t>(t) * p.D,
-                              p.xs + static_cast<int64_t>(t) * ng, lane);
+        quant_x_row<GROUP>(p.x, p.D, t, p.xq, p.xs, lane);
     }
 }
 
@@ -213,6 +151,7 @@ static void front_group(int group, const FrontArgs& a, hipStream_t s) {
     const dim3 g(static_cast<unsigned>(a.T)), b(128);
     if (group < 0) hipLaunchKernelGGL((token_front_kernel<EPL, SCORING, -1>), g, b, 0, s, a);
     else if (group == 0) hipLaunchKernelGGL((token_front_kernel<EPL, SCORING, 0>), g, b, 0, s, a);
+    else if (group == 32) hipLaunchKernelGGL((token_front_kernel<EPL, SCORING, 32>), g, b, 0, s, a);
     else hipLaunchKernelGGL((token_front_kernel<EPL, SCORING, 128>), g, b, 0, s, a);
 }
 
@@ -227,7 +166,8 @@ bool front_small_ok(int T, int k, int n_shared) {
 }
 
 static void front_tokens(const moe_layer_desc* L, const FrontArgs& a, hipStream_t s) {
-    const int group = L->quant == MOE_QUANT_NONE_BF16 ? -1 : (L->quant == MOE_QUANT_BLOCK128_FP8 ? 128 : 0);
+    const int group = L->quant == MOE_QUANT_NONE_BF16 ? -1
+                      : L->quant == MOE_QUANT_BLOCK128_FP8 ? 128 : L->quant == MOE_QUANT_MXFP4 ? 32 : 0;
     const int epl = static_cast<int>(ceil_div(L->E, 64));
     if (epl <= 1) front_scoring<1>(L->scoring, group, a, s);
     else if (epl <= 2) front_scoring<2>(L->scoring, group, a, s);

@@ -5,7 +5,10 @@
 // row count in bounded slices.  PTPC-FP8 (Qwen3 MI300X page, 2.1.1) applies a
 // per-token activation scale and a per-output-channel weight scale; the
 // DeepSeek-R1 layer's blockwise FP8 (MI355X MoRI page) uses 1x128 activation
-// and 128x128 weight scales.
+// and 128x128 weight scales; MXFP4 (the MoRI page's A4W4 FusedMoE) has E2M1
+// activations and weights with one E8M0 scale per 32 elements along K, which
+// the matrix cores apply themselves (v_mfma_scale_f32_32x32x64_f8f6f4 with
+// FP4 operands and per-lane scale bytes).
 //
 // One workgroup per CU (256 threads, 4 waves in a WM x WN grid) computes a
 // tile of BM permuted rows of one expert (the permutation pads every expert
@@ -78,7 +81,8 @@ constexpr int wm_of(int bm) { return bm >= 128 ? 2 : 1; }
 // 8-wave tile holds 128 x 64 per wave)
 static int tn_of(int mode, int weight_rows, int bm) {
     if (nw_of(mode, bm) == 8) return 2;
-    return mode == MOE_QUANT_PTPC_FP8 && weight_rows % ((4 / wm_of(bm)) * 128) == 0 ? 4 : 2;
+    return (mode == MOE_QUANT_PTPC_FP8 || mode == MOE_QUANT_MXFP4) && weight_rows % ((4 / wm_of(bm)) * 128) == 0
+               ? 4 : 2;
 }
 
 struct GemmArgs {
@@ -97,6 +101,9 @@ struct GemmArgs {
     const float* w_scale;      // PTPC: [E', Nw]; block: [E', Nw/128, K/128]
     int64_t ws_expert;         // floats per expert
     int ws_ld;                 // block mode: K/128
+    const uint8_t* a_mx;       // MXFP4: E8M0 scales of the activation rows [rows, K/32]
+    const uint8_t* w_mx;       // MXFP4: E8M0 weight scales [E', Nw, K/32]
+    int64_t w_mx_expert;       // MXFP4: scale bytes per expert
     int K;                     // reduction length (elements)
     int I;                     // gate_up: act columns; weight rows 2I
     void* out;
@@ -155,6 +162,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(void* base) {
 template <int MODE, bool GATEUP, int BM, int TN>
 __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(const GemmArgs p) {
     constexpr int ELEM = MODE == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    constexpr bool MX = MODE == MOE_QUANT_MXFP4;
     constexpr int NW = nw_of(MODE, BM), NT = NW * 64;
     constexpr int WM = wm_of(BM), WN = NW / WM;
     constexpr int TM = BM / (32 * WM);
@@ -170,7 +178,12 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     constexpr int NS = 2 * STAGE + 4096 <= 80 * 1024 ? 2 : (3 * STAGE <= kLdsBudget ? 3 : 2);
     constexpr int A_IN = BM / (8 * NW);         // copies (8 rows x 128 B) of A per wave per step
     constexpr int B_IN = NROWS / (8 * NW);      // copies of B per wave per step
-    constexpr int N_BIG = A_IN + B_IN + (BLOCKQ ? 1 : 0);   // copies per wave per step
+    // MXFP4: each row has 8 scale bytes (two dwords) per 128-byte step; a
+    // copy moves 64 dwords, and every wave issues the same number (dwords
+    // past the tile's rows land in padding slots)
+    constexpr int AS_IN = MX ? (2 * BM + 64 * NW - 1) / (64 * NW) : 0;
+    constexpr int WS_IN = MX ? (2 * NROWS + 64 * NW - 1) / (64 * NW) : 0;
+    constexpr int N_BIG = A_IN + B_IN + (BLOCKQ ? 1 : 0) + AS_IN + WS_IN;   // copies per wave per step
     static_assert(TM >= 1 && A_IN >= 1 && B_IN >= 1 && BM % (8 * NW) == 0 && NROWS % (8 * NW) == 0 && BM <= 256 &&
                       2 * STAGE <= kLdsBudget && (!BLOCKQ || BM <= 64 * NW),
                   "tile shape");
@@ -183,6 +196,10 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     // PTPC: channel scales of the tile's output columns (gate_up: gate, then up)
     __shared__ __attribute__((aligned(16))) float s_chs[MODE == MOE_QUANT_PTPC_FP8 ? (GATEUP ? 2 : 1) * TILE_N : 1];
     __shared__ float s_wscale[BLOCKQ ? WN * TN : 1][BLOCKQ ? 128 : 1];   // blockwise: weight scales of the tile
+    // MXFP4: the step's scale dwords, slot 2 row + half (activation rows) and
+    // 2 t + half (weight row t of the tile)
+    __shared__ __attribute__((aligned(16))) uint32_t s_asc[MX ? NS : 1][MX ? 64 * NW * AS_IN : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t s_wsc[MX ? NS : 1][MX ? 64 * NW * WS_IN : 1];
 
     // tile order: expert-major, weight tile, then row block; each XCD takes
     // a contiguous eighth of the tiles that hold rows (the grid covers the
@@ -263,7 +280,7 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     // weight tile row t (LDS row BM + t) is row t % WCOLS of wave column t / WCOLS
     // (gate rows first, then up rows)
     const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
-    const int64_t wrow_bytes = static_cast<int64_t>(p.K) * ELEM;
+    const int64_t wrow_bytes = MX ? static_cast<int64_t>(p.K) / 2 : static_cast<int64_t>(p.K) * ELEM;
     uint32_t b_src[B_IN];                                   // byte offsets within the expert
 #pragma unroll
     for (int j = 0; j < B_IN; ++j) {
@@ -296,9 +313,31 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         const int r = wave * 64 + lane;
         sc_src = p.a_scale + static_cast<int64_t>(s_tok[r < BM ? r : 0]) * p.a_scale_ld;
     }
+    // MXFP4 scale copies: lane source addresses (the step adds 8 bytes)
+    const uint8_t* as_src[AS_IN > 0 ? AS_IN : 1];
+    const uint8_t* ws_src[WS_IN > 0 ? WS_IN : 1];
+    if constexpr (MX) {
+        const int kb = p.K >> 5;                            // scale bytes per row
+#pragma unroll
+        for (int j = 0; j < AS_IN; ++j) {
+            int d = 64 * (wave + NW * j) + lane;
+            d = d < 2 * BM ? d : d % (2 * BM);
+            as_src[j] = p.a_mx + static_cast<int64_t>(s_tok[d >> 1]) * kb + 4 * (d & 1);
+        }
+#pragma unroll
+        for (int j = 0; j < WS_IN; ++j) {
+            int d = 64 * (wave + NW * j) + lane;
+            d = d < 2 * NROWS ? d : d % (2 * NROWS);
+            const int t = d >> 1, w = t / WCOLS, jj = t % WCOLS;
+            const int wr = GATEUP ? (jj < HALF ? n0 + w * HALF + jj : p.I + n0 + w * HALF + jj - HALF) : n0 + t;
+            ws_src[j] = p.w_mx + e * p.w_mx_expert + static_cast<int64_t>(wr) * kb + 4 * (d & 1);
+        }
+    }
     const int nbig = static_cast<int>(wrow_bytes / kRow);   // steps; K bytes are a multiple of 128
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     const uint32_t sc0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_ascale[0][0]));
+    const uint32_t asc0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_asc[0][0]));
+    const uint32_t wsc0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_wsc[0][0]));
 
     // copy D (0 .. N_BIG-1) of step S into LDS stage BUF (uniform M0 per copy)
     auto issue_one = [&](auto D, int S, int buf) {
@@ -312,8 +351,16 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         } else if constexpr (d < A_IN + B_IN) {
             constexpr int j = d - A_IN;
             dma16(b_src[j], wexp + kw, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
-        } else {
+        } else if constexpr (BLOCKQ && d == A_IN + B_IN) {
             dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 64 * NW + wave * 64) * 4));
+        } else if constexpr (MX && d < A_IN + B_IN + AS_IN) {
+            constexpr int j = d - A_IN - B_IN;
+            dma4(as_src[j] + 8 * S,
+                 __builtin_amdgcn_readfirstlane(asc0 + (buf * 64 * NW * AS_IN + 64 * (wave + NW * j)) * 4));
+        } else if constexpr (MX) {
+            constexpr int j = d - A_IN - B_IN - AS_IN;
+            dma4(ws_src[j] + 8 * S,
+                 __builtin_amdgcn_readfirstlane(wsc0 + (buf * 64 * NW * WS_IN + 64 * (wave + NW * j)) * 4));
         }
     };
     auto issue = [&](int S) { static_for<N_BIG>([&](auto D) { issue_one(D, S, S % NS); }); };
@@ -341,6 +388,7 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     // Operand fragments, double-buffered in registers: set X holds the two
     // 16-byte chunks of this lane's rows for one half-step.
     u32x4 fa[2][TM][2], fb[2][TN][2];
+    uint32_t asw[2][MX ? TM : 1], wsw[2][MX ? TN : 1];      // MXFP4 scale words, double-buffered like the fragments
 
     // Row tiles of this wave that hold at least one routed row: 32-row tiles
     // made only of pads get no operand reads and no MFMAs (their
@@ -354,8 +402,10 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     auto run = [&](auto TAc) __attribute__((always_inline)) {
         constexpr int TA = decltype(TAc)::value;
         // LDS reads per half-step (none without live rows) and MFMAs
-        constexpr int NL = TA > 0 ? 2 * (TA + TN) : 0;
-        constexpr int NM = (MODE == MOE_QUANT_NONE_BF16 ? 2 : 1) * TA * TN;
+        // (MXFP4: plus one scale word per row tile and weight tile)
+        constexpr int NLF = TA > 0 ? 2 * (TA + TN) : 0;
+        constexpr int NL = NLF + (MX && TA > 0 ? TA + TN : 0);
+        constexpr int NM = (MODE == MOE_QUANT_NONE_BF16 || MX ? 2 : 1) * TA * TN;
 
         // LDS read L (0 .. NL-1) of half-step H of the step in stage BUF into
         // set X, in the order the MFMAs consume them: weight tile 0, the row
@@ -364,7 +414,17 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         auto load_one = [&](auto X, auto Lc, int buf, int h) {
             constexpr int l = decltype(Lc)::value, x = decltype(X)::value;
             const uint8_t* L = lds + buf * STAGE;
-            if constexpr (l >= 2 && l < 2 + 2 * TA) {
+            if constexpr (l >= NLF) {
+                // MXFP4 scale words of half-step h: the row's dword h holds
+                // the scales of K blocks 4h .. 4h+3; shifted by 16 q, bytes 0
+                // and 1 are this lane's blocks 4h + 2q and 4h + 2q + 1
+                constexpr int i = l - NLF;
+                if constexpr (i < TA) {
+                    asw[x][i] = s_asc[buf][2 * (arow + i * 32 + r32) + h] >> (16 * q);
+                } else {
+                    wsw[x][i - TA] = s_wsc[buf][2 * (wn * WCOLS + (i - TA) * 32 + r32) + h] >> (16 * q);
+                }
+            } else if constexpr (l >= 2 && l < 2 + 2 * TA) {
                 constexpr int tm = (l - 2) / 2, c = (l - 2) % 2;
                 fa[x][tm][c] = lds16(L, lds_off(arow + tm * 32 + r32, 4 * h + 2 * q + c));
             } else {
@@ -410,6 +470,15 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
                 acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fb[x][tn][c]),
                                                                       __builtin_bit_cast(v8bf, fa[x][tm][c]),
                                                                       acc[tm][tn], 0, 0, 0);
+            } else if constexpr (MX) {
+                // chunk c (16 bytes = 32 E2M1 elements = one scale block) of
+                // both operands; format selectors 4 (FP4) for both, scale
+                // byte c of each lane's shifted scale word
+                constexpr int c = j / (TA * TN), tn = (j % (TA * TN)) / TA, tm = j % TA;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    cat8(fb[x][tn][c], z), cat8(fa[x][tm][c], z), acc[tm][tn], 4, 4, c,
+                    static_cast<int>(wsw[x][tn]), c, static_cast<int>(asw[x][tm]));
             } else {
                 constexpr int tn = j / TA, tm = j % TA;
                 if constexpr (BLOCKQ && decltype(H0)::value) {
@@ -418,7 +487,10 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
                     for (int i = 0; i < 16; ++i) acc[tm][tn][i] *= r;
                 }
                 const v8i av = cat8(fa[x][tm][0], fa[x][tm][1]), bv = cat8(fb[x][tn][0], fb[x][tn][1]);
-                // e4m3 x e4m3 (format selectors 0, 0), no hardware block scaling
+                // e4m3 x e4m3 (format selectors 0, 0), no hardware block
+                // scaling: zero immediates select the unscaled
+                // v_mfma_f32_32x32x64_f8f6f4 (a scale byte of 0 passed at run
+                // time would mean 2^-127)
                 acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[tm][tn], 0, 0, 0, 0, 0, 0);
             }
         };
@@ -638,7 +710,7 @@ static int32_t launch_bm(int block_m, const GemmArgs& a, hipStream_t s) {
                                a);
             return moe_launch_status();
         }
-        if constexpr (TN == 2) {   // tn_of gives the 256-row tile 2 weight tiles per wave
+        if constexpr (TN == 2 && MODE != MOE_QUANT_MXFP4) {   // tn_of gives the 256-row tile 2 weight tiles per wave
             if (block_m == 256) {
                 hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 256, TN>), grid, dim3(nw_of(MODE, 256) * 64), 0,
                                    s, a);
@@ -658,6 +730,9 @@ static int32_t launch_mode(int quant, int tn, int block_m, const GemmArgs& a, hi
             return tn == 4 ? launch_bm<MOE_QUANT_PTPC_FP8, GATEUP, 4>(block_m, a, s)
                            : launch_bm<MOE_QUANT_PTPC_FP8, GATEUP, 2>(block_m, a, s);
         case MOE_QUANT_BLOCK128_FP8: return launch_bm<MOE_QUANT_BLOCK128_FP8, GATEUP, 2>(block_m, a, s);
+        case MOE_QUANT_MXFP4:
+            return tn == 4 ? launch_bm<MOE_QUANT_MXFP4, GATEUP, 4>(block_m, a, s)
+                           : launch_bm<MOE_QUANT_MXFP4, GATEUP, 2>(block_m, a, s);
     }
     return MOE_ERR_UNSUPPORTED;
 }
@@ -675,11 +750,17 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     // the copies address activations and one expert's weights with 32-bit
     // offsets: the C ABI has checked the byte ranges before any launch
+    const bool mx = L->quant == MOE_QUANT_MXFP4;
     GemmArgs g{};
     g.offsets = offsets;
     g.counts = counts;
     g.a = static_cast<const uint8_t*>(a);
-    g.a_ld = static_cast<int64_t>(L->D) * elem;
+    g.a_ld = mx ? L->D / 2 : static_cast<int64_t>(L->D) * elem;
+    if (mx) {
+        g.a_mx = reinterpret_cast<const uint8_t*>(a_scale);
+        g.w_mx = reinterpret_cast<const uint8_t*>(L->w13_scale);
+        g.w_mx_expert = 2LL * L->I * (L->D / 32);
+    }
     g.a_scale = a_scale;
     g.a_scale_ld = L->D / 128;
     g.sorted_ids = sorted_ids;
@@ -689,7 +770,7 @@ int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* 
     g.block_expert = block_expert;
     g.w = static_cast<const uint8_t*>(L->w13);
     g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
-    g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
+    g.w_expert_bytes = mx ? static_cast<int64_t>(L->I) * L->D : static_cast<int64_t>(2) * L->I * L->D * elem;
     g.w_scale = L->w13_scale;
     g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? 2LL * L->I
                                                   : static_cast<int64_t>(2 * L->I / 128) * (L->D / 128);
@@ -711,18 +792,24 @@ int32_t gemm_down_launch(const moe_layer_desc* L, const void* act, const float* 
     if (block_m == 16) return stream_down_launch(L, act, act_scale, T, offsets, counts, out_perm, s, act_blocked);
     if (act_blocked) return MOE_ERR_UNSUPPORTED;   // only the streaming kernel reads blocked act codes
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    const bool mx = L->quant == MOE_QUANT_MXFP4;
     GemmArgs g{};
     g.offsets = offsets;
     g.counts = counts;
     g.a = static_cast<const uint8_t*>(act);
-    g.a_ld = static_cast<int64_t>(L->I) * elem;
+    g.a_ld = mx ? L->I / 2 : static_cast<int64_t>(L->I) * elem;
+    if (mx) {
+        g.a_mx = reinterpret_cast<const uint8_t*>(act_scale);
+        g.w_mx = reinterpret_cast<const uint8_t*>(L->w2_scale);
+        g.w_mx_expert = static_cast<int64_t>(L->D) * (L->I / 32);
+    }
     g.a_scale = act_scale;
     g.a_scale_ld = L->I / 128;
     g.sorted_ids = nullptr;
     g.block_expert = block_expert;
     g.w = static_cast<const uint8_t*>(L->w2);
     g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
-    g.w_expert_bytes = static_cast<int64_t>(L->D) * L->I * elem;
+    g.w_expert_bytes = mx ? static_cast<int64_t>(L->D) * L->I / 2 : static_cast<int64_t>(L->D) * L->I * elem;
     g.w_scale = L->w2_scale;
     g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? static_cast<int64_t>(L->D)
                                                   : static_cast<int64_t>(L->D / 128) * (L->I / 128);

@@ -1,10 +1,13 @@
-// PTPC / blockwise FP8 quantization.
+// PTPC / blockwise FP8 and MXFP4 quantization.
 //
 // PTPC-FP8 (Qwen3 MI300X page, 2.1.1 and Figure 3) gives every activation row
 // (token) its own dynamic scale and every weight output channel its own
 // static scale; the MI355X MoRI page's blockwise FP8 uses one fp32 scale per
 // 128 elements.  Per group: amax = max|x|, scale = amax/448,
 // q = e4m3(x * (448/amax)), IEEE fp32 divisions and one fp32 multiply.
+// MXFP4 (the MoRI page's A4W4 FusedMoE and its MXFP4 dispatch): blocks of
+// 32 elements with a power-of-two E8M0 scale and E2M1 elements
+// (mx_row_wave in quant_dev.h).
 //
 // HBM-bound: one wave per row reads 16 B per lane per step (1 KB coalesced
 // per wave instruction), keeps the row in registers, reduces amax with
@@ -139,6 +142,32 @@ __global__ void __launch_bounds__(256) quant_wblock_kernel(const uint16_t* __res
         *reinterpret_cast<uint2*>(q + code_off(row, bk * 128 + 8 * c, K, blocked)) = quant8(v[i], inv);
     }
     if (tid == 0) scale[blk] = sc;
+}
+
+// MXFP4 rows [M, K] (activations, or weight rows with K the reduction
+// dimension): E2M1 codes [M, K/2] bytes, row-major or (BLOCKED) in the
+// blocked order of the byte matrix, and E8M0 scales [M, K/32]; one wave per
+// row, one 16-byte vector of bf16 per lane at a time.
+__global__ void __launch_bounds__(256) mx_rows_kernel(const uint16_t* __restrict__ x, int64_t M, int K,
+                                                      const int* __restrict__ valid_rows, bool blocked,
+                                                      const int* __restrict__ skip_ids, int skip_id,
+                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    if (valid_rows && row >= *valid_rows) return;
+    if (skip_ids && skip_ids[row] == skip_id) return;
+    const int Kb = K >> 1;
+    mx_row_wave(x + row * K, K, [&](int b) { return q + code_off(row, b, Kb, blocked); },
+                scale + row * (K >> 5), lane);
+}
+
+int32_t quant_mx_rows_launch(const uint16_t* x, int64_t M, int K, const int* valid_rows, bool blocked,
+                             const int* skip_ids, int skip_id, uint8_t* q, uint8_t* scale, hipStream_t s) {
+    if (M == 0) return MOE_OK;
+    hipLaunchKernelGGL(mx_rows_kernel, dim3(static_cast<unsigned>(ceil_div(M, 4))), dim3(256), 0, s, x, M, K,
+                       valid_rows, blocked, skip_ids, skip_id, q, scale);
+    return moe_launch_status();
 }
 
 template <int GROUP>

@@ -4,6 +4,8 @@
 #pragma once
 #include "common.h"
 
+#include <type_traits>
+
 namespace moe {
 
 struct alignas(16) bf16x8 { uint16_t v[8]; };
@@ -43,6 +45,162 @@ __device__ __forceinline__ float amax8(const bf16x8& x) {
 __device__ __forceinline__ void scale_pair(float amax, float& scale, float& inv) {
     if (amax == 0.0f) { scale = 1.0f; inv = 1.0f; }
     else { scale = amax / 448.0f; inv = 448.0f / amax; }
+}
+
+// One row of x into codes with the wave, in chunks of 4096 elements (8
+// vectors of 8 per lane, all loads of a chunk in flight together).  GROUP 0
+// (one scale per row): amax over the chunks, then codes (a single-chunk row
+// stays in registers, longer rows are read again); GROUP 128: one pass,
+// 16-lane groups.
+template <int GROUP>
+__device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, int K, uint8_t* __restrict__ qr,
+                                               float* __restrict__ sr, int lane) {
+    constexpr int CV = 8;
+    const int nvec = K >> 3;
+    const int nch = (nvec + 64 * CV - 1) / (64 * CV);
+    const bf16x8* xv = reinterpret_cast<const bf16x8*>(xr);
+    uint2* qv = reinterpret_cast<uint2*>(qr);
+    bf16x8 v[CV];
+    auto load = [&](int ch) {
+#pragma unroll
+        for (int i = 0; i < CV; ++i) {
+            const int c = ch * 64 * CV + lane + 64 * i;
+            v[i] = c < nvec ? xv[c] : bf16x8{};
+        }
+    };
+    if constexpr (GROUP == 0) {
+        float m = 0.0f;
+        for (int ch = 0; ch < nch; ++ch) {
+            load(ch);
+#pragma unroll
+            for (int i = 0; i < CV; ++i) m = fmaxf(m, amax8(v[i]));
+        }
+        m = wave_max(m);
+        float sc, inv;
+        scale_pair(m, sc, inv);
+        for (int ch = 0; ch < nch; ++ch) {
+            if (nch > 1) load(ch);
+#pragma unroll
+            for (int i = 0; i < CV; ++i) {
+                const int c = ch * 64 * CV + lane + 64 * i;
+                if (c < nvec) qv[c] = quant8(v[i], inv);
+            }
+        }
+        if (lane == 0) sr[0] = sc;
+    } else {
+        for (int ch = 0; ch < nch; ++ch) {
+            load(ch);
+#pragma unroll
+            for (int i = 0; i < CV; ++i) {
+                const int c = ch * 64 * CV + lane + 64 * i;
+                float m = amax8(v[i]);
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                float sc, inv;
+                scale_pair(m, sc, inv);
+                if (c < nvec) {
+                    qv[c] = quant8(v[i], inv);
+                    if ((lane & 15) == 0) sr[c >> 4] = sc;
+                }
+            }
+        }
+    }
+}
+
+// value of an E2M1 code: exponent field 0 is 0 or 0.5, else (1 + m/2) * 2^(e-1)
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3, m = c & 1;
+    const float mag = e == 0 ? 0.5f * static_cast<float>(m) : __uint_as_float(((e + 126) << 23) | (m << 22));
+    return (c & 8) ? -mag : mag;
+}
+
+// 2^k as fp32 for k in [-127, 127] (2^-127 is a subnormal)
+__device__ __forceinline__ float exp2i(int k) {
+    return k >= -126 ? __uint_as_float(static_cast<uint32_t>(k + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// floor(log2(a)) for finite a > 0, from the exponent field (subnormals by
+// the position of their leading mantissa bit)
+__device__ __forceinline__ int floor_log2(float a) {
+    const uint32_t b = __float_as_uint(a);
+    const int ef = static_cast<int>((b >> 23) & 0xFF);
+    return ef > 0 ? ef - 127 : (31 - __clz(b & 0x7FFFFF)) - 149;
+}
+
+// f(0) .. f(3) with compile-time indices (the conversion's byte selector
+// must be a constant)
+template <typename F>
+__device__ __forceinline__ void static_for_pk(F&& f) {
+    f(std::integral_constant<int, 0>{});
+    f(std::integral_constant<int, 1>{});
+    f(std::integral_constant<int, 2>{});
+    f(std::integral_constant<int, 3>{});
+}
+
+// MXFP4 (OCP Microscaling v1.0) block exponent of a 32-element block with
+// largest magnitude amax: floor(log2(amax)) - 2 (E2M1's largest value is
+// 1.5 * 2^2), clamped to E8M0's [-127, 127]; an all-zero block gets -127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    return amax > 0.0f ? max(floor_log2(amax) - 2, -127) : -127;
+}
+
+// E2M1 codes of 8 elements scaled by inv (a power of two, so the scaling is
+// exact), two per byte with element 2j in the low nibble of byte j, by the
+// hardware conversion (v_cvt_scalef32_pk_fp4_f32 with scale 1: round to
+// nearest, ties to the even mantissa, saturating to +-6, sign of zero
+// kept), which matches the E2M1 encoder written from the format definition
+// on every bf16 value (tested).
+__device__ __forceinline__ uint32_t mx_codes8(const bf16x8& v, float inv) {
+    uint32_t w = 0;
+    static_for_pk([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16_to_f32(v.v[2 * j]) * inv,
+                                                     bf16_to_f32(v.v[2 * j + 1]) * inv, 1.0f, j);
+    });
+    return w;
+}
+
+// One row of K bf16 values (K % 128 == 0) to MXFP4 with the wave: codes
+// [K/2] bytes (4 bytes per lane per vector of 8, at code_byte(4c)), E8M0
+// scale bytes [K/32] (four blocks per word, from every 16th lane).  Vector
+// c covers elements 8c .. 8c+7; a 32-element block is 4 consecutive lanes.
+template <typename CodeByte>
+__device__ __forceinline__ void mx_row_wave(const uint16_t* __restrict__ xr, int K, CodeByte code_byte,
+                                            uint8_t* __restrict__ sr, int lane) {
+    const int nvec = K >> 3;
+    const bf16x8* xv = reinterpret_cast<const bf16x8*>(xr);
+    for (int c0 = 0; c0 < nvec; c0 += 64) {
+        const int c = c0 + lane;
+        const bool valid = c < nvec;          // uniform over each 16-lane group (nvec % 16 == 0)
+        const bf16x8 v = valid ? ld_once(xv + c) : bf16x8{};
+        float m = amax8(v);
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        const int e = mx_exponent(m);
+        const uint32_t w = mx_codes8(v, exp2i(-e));
+        const uint32_t sb = static_cast<uint32_t>(e + 127);
+        const uint32_t s4 = __shfl_down(sb, 0, 64) | (__shfl_down(sb, 4, 64) << 8) |
+                            (__shfl_down(sb, 8, 64) << 16) | (__shfl_down(sb, 12, 64) << 24);
+        if (valid) {
+            *reinterpret_cast<uint32_t*>(code_byte(4 * c)) = w;
+            if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(sr + (c >> 2)) = s4;
+        }
+    }
+}
+
+// Token t's row of x [T, D] to the layer's activation format with the wave:
+// GROUP 0 (PTPC: fp32 scale per row), 128 (fp32 scale per 1x128 group) or
+// 32 (MXFP4: codes [T, D/2], E8M0 scale bytes [T, D/32] at xs).
+template <int GROUP>
+__device__ __forceinline__ void quant_x_row(const uint16_t* __restrict__ x, int D, int64_t t, uint8_t* xq, void* xs,
+                                            int lane) {
+    if constexpr (GROUP == 32) {
+        uint8_t* qr = xq + t * (D / 2);
+        mx_row_wave(x + t * D, D, [&](int b) { return qr + b; }, static_cast<uint8_t*>(xs) + t * (D / 32), lane);
+    } else {
+        quant_row_wave<GROUP>(x + t * D, D, xq + t * D, static_cast<float*>(xs) + t * (GROUP == 128 ? D / 128 : 1),
+                              lane);
+    }
 }
 
 }  // namespace moe

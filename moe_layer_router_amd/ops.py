@@ -114,6 +114,28 @@ def quant_weight_fp8(w: torch.Tensor, quant: str, layout: str = "blocked"):
     return q, s
 
 
+def quant_mxfp4(x: torch.Tensor, valid_rows: Optional[torch.Tensor] = None):
+    """MXFP4 rows: codes [M, K/2] uint8 (two E2M1 per byte), E8M0 scales [M, K/32] uint8."""
+    M, K = x.shape
+    _need(x, _BF16, "x")
+    q = _empty((M, K // 2), _U8, x)
+    s = _empty((M, K // 32), _U8, x)
+    L.check("moe_quant_mxfp4", L.lib().moe_quant_mxfp4(_ptr(x), M, K, _ptr(valid_rows), _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
+def quant_weight_mxfp4(w: torch.Tensor, layout: str = "blocked"):
+    """w: [n_mats, N, K] bf16 -> E2M1 codes [n_mats, N, K/2] (row-major or in
+    16-row x 128-byte blocks) and E8M0 scales [n_mats, N, K/32]."""
+    n, N, K = w.shape
+    _need(w, _BF16, "w")
+    q = _empty((n, N, K // 2), _U8, w)
+    s = _empty((n, N, K // 32), _U8, w)
+    L.check("moe_quant_weight_mxfp4", L.lib().moe_quant_weight_mxfp4(_ptr(w), n, N, K, L.LAYOUT_CODES[layout], _ptr(q),
+                                                                      _ptr(s), _stream()))
+    return q, s
+
+
 def unblock_weights(q: torch.Tensor) -> torch.Tensor:
     """Row-major copy of codes [..., N, K] stored in 16-row x 128-byte blocks
     (inside a block: K half h, line l, row parity p, 16-byte piece c, byte
@@ -151,14 +173,18 @@ class MoELayer:
         self.weight_layout = weight_layout or ("rows" if quant == "bf16" else "blocked")
         Ep = E + n_shared
         wdt = _BF16 if quant == "bf16" else _U8
-        _need(weights.w13, wdt, "w13", (Ep, 2 * I, D))
-        _need(weights.w2, wdt, "w2", (Ep, D, I))
+        kdiv = 2 if quant == "mxfp4" else 1            # MXFP4: two codes per byte
+        _need(weights.w13, wdt, "w13", (Ep, 2 * I, D // kdiv))
+        _need(weights.w2, wdt, "w2", (Ep, D, I // kdiv))
         if quant == "ptpc_fp8":
             _need(weights.w13_scale, _F32, "w13_scale", (Ep, 2 * I))
             _need(weights.w2_scale, _F32, "w2_scale", (Ep, D))
         elif quant == "block128_fp8":
             _need(weights.w13_scale, _F32, "w13_scale", (Ep, 2 * I // 128, D // 128))
             _need(weights.w2_scale, _F32, "w2_scale", (Ep, D // 128, I // 128))
+        elif quant == "mxfp4":
+            _need(weights.w13_scale, _U8, "w13_scale", (Ep, 2 * I, D // 32))
+            _need(weights.w2_scale, _U8, "w2_scale", (Ep, D, I // 32))
         if weights.router_w is not None:
             _need(weights.router_w, _F32, "router_w", (E, D))
         if weights.sel_bias is not None:
@@ -182,6 +208,11 @@ class MoELayer:
         if quant == "bf16":
             w = LayerWeights(w13_bf16.contiguous(), w2_bf16.contiguous(), router_w=router_w, sel_bias=sel_bias)
             weight_layout = "rows"
+        elif quant == "mxfp4":
+            weight_layout = weight_layout or "blocked"
+            q13, s13 = quant_weight_mxfp4(w13_bf16.contiguous(), weight_layout)
+            q2, s2 = quant_weight_mxfp4(w2_bf16.contiguous(), weight_layout)
+            w = LayerWeights(q13, q2, s13, s2, router_w=router_w, sel_bias=sel_bias)
         else:
             weight_layout = weight_layout or "blocked"
             q13, s13 = quant_weight_fp8(w13_bf16.contiguous(), quant, weight_layout)
@@ -271,7 +302,12 @@ class MoELayer:
             block_expert=view("block_expert", R // B, _I32, (R // B,)),
             inv_perm=view("inv_perm", A, _I32, (A,)), act=view("act", R * I, _BF16, (R, I)),
             out_perm=view("out_perm", R * D, _F32 if self.quant == "bf16" else _BF16, (R, D)))
-        if self.quant != "bf16":
+        if self.quant == "mxfp4":
+            out["xq"] = view("xq", T * D // 2, _U8, (T, D // 2))
+            out["xs"] = view("xs", T * D // 32, _U8, (T, D // 32))
+            out["aq"] = view("aq", R * I // 2, _U8, (R, I // 2))
+            out["as"] = view("as_", R * I // 32, _U8, (R, I // 32))
+        elif self.quant != "bf16":
             out["xq"] = view("xq", T * D, _U8, (T, D))
             out["xs"] = view("xs", T * (D // 128 if blk else 1), _F32, (T, D // 128) if blk else (T,))
             aq = view("aq", R * I, _U8, (R, I))

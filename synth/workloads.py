@@ -44,7 +44,7 @@ class Workload:
     E: int
     k: int
     I: int
-    quant: str                     # "bf16" | "ptpc_fp8" | "block128_fp8"
+    quant: str                     # "bf16" | "ptpc_fp8" | "block128_fp8" | "mxfp4"
     scoring: str = "softmax"       # or "sigmoid_grouped"
     n_groups: int = 1
     topk_groups: int = 1
@@ -96,6 +96,18 @@ WORKLOADS = {
         # page, at an 8192-token prefill (81,920 routed rows)
         Workload("e512_top10_shared_ptpc", 6, T=8192, D=4096, E=512, k=10, I=1024,
                  quant="ptpc_fp8", n_shared=1, logit_recipe="normal"),
+        # the Qwen3-235B-shaped prefill layer routed by its own router gate
+        # (router weight ~ N(0, 0.02), logits = x . Wr^T) instead of given logits
+        Workload("qwen3_235b_prefill_router", 7, T=8192, D=4096, E=128, k=8, I=1536,
+                 quant="ptpc_fp8", router="gemm"),
+        # MXFP4 (A4W4) expert arithmetic on the Qwen3-235B-shaped prefill and
+        # the DeepSeek-R1-shaped layer: 4-bit activations and weights with
+        # E8M0 scales per 32 elements
+        Workload("qwen3_235b_prefill_mxfp4", 8, T=8192, D=4096, E=128, k=8, I=1536,
+                 quant="mxfp4", logit_recipe="normal_bias"),
+        Workload("deepseek_r1_mxfp4", 9, T=4096, D=7168, E=256, k=8, I=2048,
+                 quant="mxfp4", scoring="sigmoid_grouped", n_groups=8,
+                 topk_groups=4, route_scale=2.5, n_shared=1),
     ]
 }
 

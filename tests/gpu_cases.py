@@ -32,6 +32,11 @@ REDUCED = {
     "qwen3_30b_a3b_ptpc_i384": synth.get("qwen3_30b_a3b_ptpc").replace(T=200, D=1280, I=384, E=16),
     # 512-expert top-10 layer with a shared expert, reduced: top-10 of 64
     "e512_top10_shared_r": synth.get("e512_top10_shared_ptpc").replace(T=500, D=1024, I=256, E=64),
+    # MXFP4 (A4W4) layers: several tiles and ragged tails, softmax and
+    # grouped routing with a shared expert, a small batch (32-row tiles)
+    "qwen3_235b_prefill_mxfp4_r": synth.get("qwen3_235b_prefill_mxfp4").replace(T=1000, D=1024, I=512, E=32),
+    "deepseek_r1_mxfp4_r": synth.get("deepseek_r1_mxfp4").replace(T=300, D=1024, I=256, E=32),
+    "deepseek_r1_mxfp4_small": synth.get("deepseek_r1_mxfp4").replace(T=40, D=1024, I=256, E=32),
 }
 
 
@@ -93,12 +98,67 @@ def build_case(w: synth.Workload, device="cuda", cache_experts: bool = True, kee
     return Case(w, layer, x, logits, router_w, w13, w2, spec, bank)
 
 
+def check_router_logits(lg_gpu: np.ndarray, x_np: np.ndarray, wr_np: np.ndarray) -> np.ndarray:
+    """The GPU's router logits against the oracle's float64 projection.  The
+    per-token fp64 kernel (small batches) rounds once, so it is within one
+    fp32 ulp; the fused matrix-core kernel has exact products and fp32
+    accumulation, so |error| <= n u sum_d |x[d] w[d]| for n additions; both
+    are inside 1e-6 sum_d |x[d] w[d]| plus half an ulp of the stored value.
+    Returns the oracle's logits."""
+    ref = O.router_logits(x_np, wr_np)
+    cond = np.abs(x_np.astype(np.float64)) @ np.abs(wr_np.astype(np.float64)).T
+    err = np.abs(lg_gpu.astype(np.float64) - ref.astype(np.float64))
+    assert np.all(err <= 1e-6 * cond + np.abs(ref.astype(np.float64)) * 2.0 ** -24), float(np.max(err / cond))
+    return ref
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """E2M1 codes [rows, K] (0..15) as the GPU stores them: [rows, K/2] bytes,
+    element 2i in the low nibble of byte i."""
+    c = np.asarray(codes, np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b, np.uint8)
+    out = np.empty((b.shape[0], 2 * b.shape[1]), np.uint8)
+    out[:, 0::2] = b & 15
+    out[:, 1::2] = b >> 4
+    return out
+
+
+def quant_act_ref(quant: str, a: np.ndarray):
+    """The oracle's quantization of activation rows in the GPU's storage
+    layout: (codes, scales) with codes [rows, K] e4m3 or [rows, K/2] packed
+    E2M1, scales fp32 [rows] / [rows, K/128] or E8M0 bytes [rows, K/32]."""
+    if quant == "mxfp4":
+        q, sc = O.mxfp4_quant(a, 32)
+        return pack_nibbles(q), sc
+    return O.quant_rows(a, 128 if quant == "block128_fp8" else 0)
+
+
+def dequant_act(quant: str, q: np.ndarray, sc: np.ndarray) -> np.ndarray:
+    """float64 values of GPU-layout activation codes (see quant_act_ref)."""
+    if quant == "mxfp4":
+        return O.mxfp4_dequant(unpack_nibbles(q), sc, 32)
+    return O.dequant_rows(q, sc, 128 if quant == "block128_fp8" else 0)
+
+
+def same_scales(a: np.ndarray, b: np.ndarray) -> bool:
+    """Bitwise equality of fp32 or E8M0 scale arrays."""
+    a, b = np.asarray(a), np.asarray(b)
+    if a.dtype == np.float32:
+        return a.shape == b.shape and np.array_equal(a.view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+    return np.array_equal(a, b)
+
+
 def rel_l2(a, b) -> float:
     return O.relative_l2(np.asarray(a, np.float64), np.asarray(b, np.float64))
 
 
 def tol_of(quant: str) -> float:
-    """Relative L2 bound on y: 2e-3 for the bf16 path, 1e-2 for the FP8 paths."""
+    """Relative L2 bound on y: 2e-3 for the bf16 path, 1e-2 for the quantized
+    (FP8 and MXFP4) paths."""
     return 2e-3 if quant == "bf16" else 1e-2
 
 

@@ -1,8 +1,8 @@
 """End-to-end GPU parity of moe_forward against the oracle: routing,
 permutation and x codes bit-exact; y within relative L2 2e-3 (bf16 path) or
-1e-2 (FP8 paths); determinism and token-order invariance; full-size
-workloads checked on sampled tokens in the launch configuration the bench
-times."""
+1e-2 (FP8 paths); determinism and token-order invariance, on reduced shapes
+with several tiles and ragged tails in every mode and tile size (the full
+sizes are in test_gpu_fullsize.py)."""
 
 import numpy as np
 import pytest
@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 import synth
-from tests.gpu_cases import REDUCED, build_case, rel_l2, say, tol_of
+from tests.gpu_cases import REDUCED, build_case, check_router_logits, rel_l2, say, tol_of
 
 pytestmark = pytest.mark.gpu
 
@@ -59,12 +59,13 @@ def test_forward_matches_oracle(name, block_m):
     c = build_case(w)
     y, inter = _run(c, block_m)
     B = inter["block_m"]
-    rw = None if c.router_w is None else c.router_w.cpu().numpy()
-    ref = O.moe_forward(c.spec, c.bank, c.x_np(), c.logits_np(), router_w=rw, block_m=B)
+    lg = c.logits_np()
     if w.router == "gemm":
-        d = np.abs(inter["logits"].cpu().numpy().view(np.int32).astype(np.int64) -
-                   ref["logits"].view(np.int32).astype(np.int64))
-        assert d.max() <= 1
+        # routing is bit-exact given the same fp32 logits: the oracle routes
+        # the GPU's logits once they are within the projection's bound
+        lg = inter["logits"].cpu().numpy()
+        check_router_logits(lg, c.x_np(), c.router_w.cpu().numpy())
+    ref = O.moe_forward(c.spec, c.bank, c.x_np(), lg, block_m=B)
     _check_exact(inter, ref, w.quant)
     err = rel_l2(y.float().cpu().numpy(), ref["y"])
     say("rel_l2", err)
@@ -153,48 +154,3 @@ def test_forward_zero_tokens_rows_and_one_hot_routing():
     _check_exact(inter, ref, w.quant)
     assert rel_l2(y.float().cpu().numpy(), ref["y"]) <= tol_of(w.quant)
     assert np.all(y[::7].float().cpu().numpy() == 0)
-
-
-# --------------------------------------------------------------- full sizes
-
-@pytest.mark.parametrize("name", ["tiny_bf16", "qwen3_30b_a3b_ptpc", "qwen3_235b_prefill_ptpc",
-                                  "qwen3_235b_decode_ptpc", "deepseek_r1_block_fp8", "e512_top10_shared_ptpc"])
-def test_full_size_sampled_tokens(name):
-    """The full workload in the launch configuration the bench times: routing,
-    permutation and x codes compared whole; y on sampled tokens, which the
-    oracle evaluates one by one."""
-    w = synth.get(name)
-    say("full size", name)
-    c = build_case(w, cache_experts=False, keep_masters=w.E_total * w.I * w.D < 3e9)
-    y, inter = _run(c)
-    x_np = c.x_np()
-    lg = c.logits_np()
-    if lg is None:
-        lg = O.router_logits(x_np, c.router_w.cpu().numpy())
-    ids_ref, _ = (O.route_softmax_topk(lg, w.k) if w.scoring == "softmax" else
-                  O.route_sigmoid_grouped(lg, w.k, w.n_groups, w.topk_groups, None, w.route_scale))
-    assert np.array_equal(inter["topk_ids"].cpu().numpy(), ids_ref)
-    p = O.permute_align(ids_ref, w.E, w.n_shared, inter["block_m"])
-    for key in ("counts", "offsets", "sorted_ids", "block_expert", "inv_perm"):
-        assert np.array_equal(inter[key].cpu().numpy(), p[key]), key
-    if w.quant != "bf16":
-        xq, xs = O.quant_rows(x_np, 128 if w.quant == "block128_fp8" else 0)
-        assert np.array_equal(inter["xq"].cpu().numpy(), xq)
-        assert np.array_equal(inter["xs"].cpu().numpy().view(np.uint32), xs.view(np.uint32))
-    # sampled tokens: first, last, and a seeded spread
-    n = min(w.T, 6 if w.D * w.I < 8e6 else 2)
-    rng = np.random.default_rng(w.cid)
-    toks = np.unique(np.concatenate([[0, w.T - 1], rng.integers(0, w.T, n)]))
-    c.bank.cache = True
-    ref = O.moe_forward_tokens(c.spec, c.bank, x_np[toks], lg[toks])
-    got = y[torch.from_numpy(toks).cuda()].float().cpu().numpy()
-    err = rel_l2(got, ref["y"])
-    say("sampled rel_l2", err, "tokens", len(toks))
-    assert err <= tol_of(w.quant)
-    # the layer's quantized weights for those experts are the oracle's codes
-    if w.quant != "bf16":
-        for e in sorted(set(int(v) for v in ids_ref[toks].reshape(-1)))[:4]:
-            q13, s13, q2, s2 = c.bank.quantized(e)
-            assert c.layer.weight_layout == "blocked"
-            assert np.array_equal(mlr.unblock_weights(c.layer.weights.w13[e]).cpu().numpy(), q13)
-            assert np.array_equal(c.layer.weights.w2_scale[e].cpu().numpy().view(np.uint32), s2.view(np.uint32))

@@ -177,6 +177,34 @@ def test_quant_rows(M, K, group):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
 
 
+@pytest.mark.parametrize("amax", [448.0, 300.0])
+def test_quant_every_bf16_value(amax):
+    """Every finite bf16 value of magnitude at most amax goes through the
+    encoder in rows whose first element is amax, so the scale is amax/448 and
+    each value is multiplied by fp32(448/amax): 1 (the bf16 values themselves)
+    or a factor that is not a power of two (fp32 inputs with all mantissa bits
+    in use).  Codes and scales bit-exact against the oracle's encoder."""
+    say("quant every bf16", amax)
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= amax)]
+    K = 4096
+    n = -(-vals.size // (K - 1))
+    rows = np.zeros((n, K), np.float32)
+    rows[:, 0] = amax
+    flat = rows[:, 1:].reshape(-1)
+    flat[:vals.size] = vals
+    rows[:, 1:] = flat.reshape(n, K - 1)
+    x = torch.from_numpy(rows).to(torch.bfloat16)
+    assert np.array_equal(x.to(torch.float32).numpy(), rows)       # exact: every value is bf16
+    q, sc = mlr.quant_ptpc_fp8(x.cuda(), 0)
+    torch.cuda.synchronize()
+    rq, rs = O.quant_rows(rows, 0)
+    assert np.all(rs == np.float32(amax) / np.float32(448.0))
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
 def test_quant_valid_rows_leaves_the_rest():
     say("quant valid_rows")
     x = _quant_inputs(100, 512, 1).cuda()
