@@ -42,8 +42,9 @@
  *     T = 0 (no tokens) is valid and enqueues nothing.
  *   - The only state the library keeps between calls is a per-device cache of
  *     how many workgroups of the weight-streaming kernels fit on the device
- *     at once (filled on first use, read-only afterwards).  Entry points are
- *     thread-safe; calls that share buffers must be ordered by the caller.
+ *     at once (filled on first use, read-only afterwards) and the per-device
+ *     scratch array of moe_forward_noalloc.  Entry points are thread-safe;
+ *     calls that share buffers must be ordered by the caller.
  */
 #ifndef MOE_LAYER_ROUTER_AMD_MOE_H
 #define MOE_LAYER_ROUTER_AMD_MOE_H
@@ -358,6 +359,25 @@ int32_t moe_workspace_layout(const moe_layer_desc* L, int32_t T, int32_t block_m
 int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* logits_or_null,
                     int32_t T, int32_t block_m, void* y_bf16, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as moe_forward; the
+ * intermediates live in a device array of MOE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU until the process ends.  The call allocates
+ * nothing (its first call on a device looks up that device's copy of the
+ * array).  Returns MOE_ERR_WORKSPACE, enqueueing nothing, when
+ * moe_forward_workspace_size(L, T, block_m) exceeds the array (96 MiB: the
+ * decode batches of the Qwen3-235B-shaped layer, D 4096, I 1536, 128 experts
+ * top-8, up to T = 128, and of the DeepSeek-R1-shaped layer, D 7168, I 2048,
+ * 256 + 1 experts top-8, up to T = 64).  Every call on a GPU uses that GPU's one array and
+ * leaves its intermediates there: calls that overlap on one GPU (two streams,
+ * two threads) race and must be ordered by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (96LL << 20)
+int32_t moe_forward_noalloc(const moe_layer_desc* L, const void* x_bf16, const float* logits_or_null,
+                            int32_t T, int32_t block_m, void* y_bf16, void* stream);
 
 /*
  * Expert-parallel payloads ("Win on TCO ... MoRI", "Hybrid FP4/FP8 quantized

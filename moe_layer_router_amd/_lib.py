@@ -22,6 +22,7 @@ WEIGHTS_ROWS, WEIGHTS_BLOCKED = 0, 1
 LAYOUT_CODES = {"rows": WEIGHTS_ROWS, "blocked": WEIGHTS_BLOCKED}
 PAYLOAD_MXFP4, PAYLOAD_FP8_BLOCK = 0, 1
 PAYLOAD_CODES = {"mxfp4": PAYLOAD_MXFP4, "fp8_block": PAYLOAD_FP8_BLOCK}
+NOALLOC_SCRATCH_BYTES = 96 << 20      # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class LayerDesc(ctypes.Structure):
@@ -68,6 +69,8 @@ SIGNATURES = {
     "moe_workspace_layout": (c_int32, [POINTER(LayerDesc), c_int32, c_int32, POINTER(WsLayout)]),
     "moe_forward": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                               c_size_t, c_void_p]),
+    "moe_forward_noalloc": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                      c_void_p]),
     "moe_ep_payload_bytes": (c_int64, [c_int32, c_int32]),
     "moe_ep_pack_payload": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "moe_ep_unpack_payload": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),

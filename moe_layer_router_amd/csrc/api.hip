@@ -3,6 +3,9 @@
 // checks the limits of all of its kernels before the first launch).
 #include "common.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace moe {
 int32_t route_topk_launch(const float* logits, int T, int E, int k, int scoring, int n_groups, int topk_groups,
                           const float* sel_bias, int renormalize, float route_scale, int* ids, float* w,
@@ -495,6 +498,59 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
                                aq_blocked)) != MOE_OK)
         return st;
     return combine_launch(outp, fp8 ? 1 : 0, inv, w, T, k, L->n_shared, L->D, static_cast<uint16_t*>(y_bf16), s);
+}
+
+}  // extern "C"
+
+// Workspace of moe_forward_noalloc: device memory the library owns for the
+// life of the process, one copy per GPU (the loader places the array on every
+// device the code object is loaded on).  In host code `scratch` names only
+// the host-side stand-in of the array; its device address comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array (the current device: the
+// one the caller's stream belongs to).
+int32_t scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+                (void)hipGetLastError();
+                return MOE_ERR_HIP;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t moe_forward_noalloc(const moe_layer_desc* L, const void* x_bf16, const float* logits_or_null, int32_t T,
+                            int32_t block_m, void* y_bf16, void* stream) {
+    int32_t st = check_layer(L);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_ARG(T >= 0);
+    if (T == 0) return MOE_OK;
+    const size_t need = moe_forward_workspace_size(L, T, block_m);
+    if (need > static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES)) return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+    // need == 0 (a block_m or shape the kernels do not cover): moe_forward
+    // reports it before launching anything
+    return moe_forward(L, x_bf16, logits_or_null, T, block_m, y_bf16, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int64_t moe_ep_payload_bytes(int32_t D, int32_t format) {
