@@ -34,7 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer TFLOP/s (prefill) and expert-weight GB/s (decode), % of roofline"
-PEAK_TFLOPS = {"ptpc_fp8": 5000.0, "block128_fp8": 5000.0, "bf16": 2500.0}
+PEAK_TFLOPS = {"ptpc_fp8": 5000.0, "block128_fp8": 5000.0, "bf16": 2500.0, "mxfp4": 10100.0}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -114,8 +114,12 @@ class Steps:
         L.check("permute", lib.moe_permute_align(p["topk_ids"], self.T, w.k, w.E, w.n_shared, self.B, p["counts"],
                                                  p["offsets"], p["sorted_ids"], p["block_expert"], p["inv_perm"],
                                                  p["scratch"], s))
+        mx = w.quant == "mxfp4"
         a, a_s = self.x.data_ptr(), None
-        if fp8:
+        if mx:
+            L.check("quant x", lib.moe_quant_mxfp4(self.x.data_ptr(), self.T, w.D, None, p["xq"], p["xs"], s))
+            a, a_s = p["xq"], p["xs"]
+        elif fp8:
             L.check("quant x", lib.moe_quant_ptpc_fp8(self.x.data_ptr(), self.T, w.D, group, None, p["xq"], p["xs"], s))
             a, a_s = p["xq"], p["xs"]
         if ev is not None:
@@ -125,7 +129,11 @@ class Steps:
         if ev is not None:
             ev[1].record()
         act, act_s = p["act"], None
-        if fp8:
+        if mx:
+            L.check("quant act", lib.moe_quant_mxfp4(p["act"], self.lay["max_rows"], w.I, p["offsets"] + 4 * Ep,
+                                                     p["aq"], p["as_"], s))
+            act, act_s = p["aq"], p["as_"]
+        elif fp8:
             L.check("quant act", lib.moe_quant_ptpc_fp8(p["act"], self.lay["max_rows"], w.I, group,
                                                         p["offsets"] + 4 * Ep, p["aq"], p["as_"], s))
             act, act_s = p["aq"], p["as_"]
@@ -144,6 +152,10 @@ def gateup_bytes(w, ids_np):
     the experts the batch uses, the activation rows read once, act written once."""
     import numpy as np
     used = len(np.unique(ids_np)) + w.n_shared
+    if w.quant == "mxfp4":           # E2M1 codes (half a byte) + one E8M0 byte per 32
+        wb = 2 * w.I * w.D // 2 + 2 * w.I * w.D // 32
+        ab = w.T * w.D // 2 + w.T * w.D // 32
+        return used * wb + ab + w.T * (w.k + w.n_shared) * w.I * 2
     elem = 2 if w.quant == "bf16" else 1
     wb = 2 * w.I * w.D * elem
     if w.quant == "ptpc_fp8":
@@ -158,6 +170,8 @@ def active_expert_bytes(w, ids_np):
     """Weight bytes of the experts the batch routes to (codes + scales)."""
     import numpy as np
     used = len(np.unique(ids_np)) + w.n_shared
+    if w.quant == "mxfp4":
+        return used * (3 * w.I * w.D // 2 + 3 * w.I * w.D // 32), used
     elem = 2 if w.quant == "bf16" else 1
     per = 3 * w.I * w.D * elem
     if w.quant == "ptpc_fp8":
@@ -284,6 +298,25 @@ def time_layer(torch, mlr, synth, name, steps, warmup):
                gemms_frac_of_peak=round((gu_f + dn_f) / ((gu_ms + dn_ms) * 1e-3) / 1e12 / peak, 4),
                tokens_per_s=round(w.T / (ms * 1e-3), 1))
     out["frac_of_floor"] = round(out["floor_ms"] / ms, 4)
+    if c.logits is None and w.T > 64:
+        # the fused router front alone (projection, top-k, x quantization),
+        # into the workspace's slots
+        from moe_layer_router_amd import _lib as L
+        lay = c.layer.layout(w.T, 0)
+        base = ws.data_ptr()
+        sp = torch.cuda.current_stream().cuda_stream
+
+        def front(i):
+            L.check("router_front", L.lib().moe_router_front(
+                ctypes.byref(c.layer.desc), c.x.data_ptr(), w.T, base + lay["logits"], base + lay["topk_ids"],
+                base + lay["topk_w"], base + lay["xq"], base + lay["xs"], base + lay["router"],
+                ws.numel() - lay["router"], sp))
+        rmed, _, _ = timed_calls(torch, front, steps, warmup)
+        rflops = 3 * 2.0 * w.T * w.E * w.D          # three exact bf16 pieces of the router weight
+        out["router_front"] = dict(us=round(rmed, 2), tflops=round(rflops / (rmed * 1e-6) / 1e12, 1),
+                                   frac_bf16_peak=round(rflops / (rmed * 1e-6) / 1e12 / 2500.0, 4),
+                                   note="router projection (3 exact bf16 pieces), top-k and x quantization "
+                                        "in one launch")
     del st, layers, c, inter
     torch.cuda.empty_cache()
     return out
@@ -370,7 +403,8 @@ def time_payloads(torch, mlr, x, steps, warmup):
     return res
 
 
-OTHER_LAYERS = ("tiny_bf16", "qwen3_30b_a3b_ptpc", "deepseek_r1_block_fp8", "e512_top10_shared_ptpc")
+OTHER_LAYERS = ("tiny_bf16", "qwen3_30b_a3b_ptpc", "deepseek_r1_block_fp8", "e512_top10_shared_ptpc",
+                "qwen3_235b_prefill_mxfp4", "deepseek_r1_mxfp4", "qwen3_235b_prefill_router")
 
 
 def main():
@@ -492,7 +526,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8_e4m3" if w.quant != "bf16" else "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": {"bf16": "bf16", "mxfp4": "fp4_e2m1"}.get(w.quant, "fp8_e4m3"), "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "E": w.E, "top_k": w.k, "I": w.I,
                    "n_shared": w.n_shared, "quant": w.quant, "scoring": w.scoring, "block_m": st.B},
         "roofline": roof,

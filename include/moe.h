@@ -107,8 +107,8 @@ extern "C" {
  *   Microscaling v1.0): activations, weights and the re-quantized act are
  *   all E2M1 with an E8M0 scale 2^e per 32 elements along the reduction
  *   dimension, e = floor(log2(amax)) - 2 clamped to [-127, 127]; the matrix
- *   cores apply both scales.  I % 256 == 0; block_m >= 32 (the LDS-tiled
- *   kernels; moe_default_block_m never picks 16 for it).
+ *   cores apply both scales.  I % 256 == 0; block_m 32, 64, 128 or 192 (the
+ *   LDS-tiled kernels; moe_default_block_m never picks 16 for it).
  *   weight_layout: order of the bytes of each [N, K] weight matrix (w13:
  *              N = 2I, K = D; w2: N = D, K = I; K_bytes = K, or K/2 for MXFP4):
  *              MOE_WEIGHTS_ROWS    row-major, K contiguous;
@@ -142,7 +142,7 @@ typedef struct moe_layer_desc {
  * (host struct; -1 when a buffer is not used by the layer's mode). */
 typedef struct moe_ws_layout {
     int64_t logits, topk_ids, topk_w, counts, offsets, sorted_ids, block_expert,
-            inv_perm, xq, xs, act, aq, as, out_perm, scratch, total;
+            inv_perm, xq, xs, act, aq, as, out_perm, scratch, router, total;
     int64_t max_rows;   /* moe_permute_max_rows of the layer                 */
     int32_t block_m;    /* the block_m the layout was computed for            */
 } moe_ws_layout;
@@ -186,7 +186,7 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
  * Router projection fused with top-k routing and the FP8 quantization of x,
  * in one launch (router gate of the Qwen 3.5 MoE paragraph; the page's
  * roadmap item puts the top-k selection where the scores are computed).
- * For the layer L (L->router_w required; E <= 512, D % 64 == 0, else
+ * For the layer L (L->router_w required; E <= 512, D % 256 == 0, else
  * MOE_ERR_UNSUPPORTED) and x [T, D] bf16:
  *   logits [T, E] fp32: x . router_w on the matrix cores; each fp32 weight
  *     is split exactly into three bf16 pieces, so the products are exact and
@@ -197,9 +197,15 @@ int32_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int
  *     moe_quant_ptpc_fp8 (xq, xs may be NULL for a bf16 layer).
  * moe_forward uses it when it is given no logits and T is above the
  * small-batch sizes (those project in fp64 per token, moe_router_logits).
+ * workspace: device memory of moe_router_front_workspace_size(L) bytes,
+ * 16-byte aligned, for the router weight split into its three pieces in the
+ * kernel's load order (rewritten by every call; MOE_ERR_WORKSPACE if
+ * smaller).
  */
+size_t moe_router_front_workspace_size(const moe_layer_desc* L);
 int32_t moe_router_front(const moe_layer_desc* L, const void* x_bf16, int32_t T, float* logits,
-                         int32_t* topk_ids, float* topk_w, uint8_t* xq, float* xs, void* stream);
+                         int32_t* topk_ids, float* topk_w, uint8_t* xq, float* xs, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * Host-only: rows of the padded permuted buffer, an upper bound valid for any
@@ -296,8 +302,8 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
  * kernels; their contents are then unspecified); rows at or past
  * expert_offsets[E'] are not written.  block_m must equal the block_m of moe_permute_align and be one
  * of: 16 (weight-streaming kernels for small batches: each weight byte is
- * read once per 64 rows of its expert; not for MXFP4), 32, 64, 128 or 256
- * (LDS-tiled kernels).  Shapes: I % 128 == 0 (MXFP4: 256) and D % 256 == 0.
+ * read once per 64 rows of its expert; not for MXFP4), 32, 64, 128, 192
+ * (FP8 and MXFP4 only) or 256 (not MXFP4) (LDS-tiled kernels).  Shapes: I % 128 == 0 (MXFP4: 256) and D % 256 == 0.
  */
 int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,
                                      const float* a_scale, int32_t T, int32_t block_m,

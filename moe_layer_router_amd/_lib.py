@@ -36,15 +36,16 @@ class LayerDesc(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in ("logits", "topk_ids", "topk_w", "counts", "offsets", "sorted_ids",
                                        "block_expert", "inv_perm", "xq", "xs", "act", "aq", "as_",
-                                       "out_perm", "scratch", "total", "max_rows")] + [("block_m", c_int32)]
+                                       "out_perm", "scratch", "router", "total", "max_rows")] + [("block_m", c_int32)]
 
 
 # name -> (restype, argtypes)
 SIGNATURES = {
     "moe_status_str": (c_char_p, [c_int32]),
     "moe_router_logits": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "moe_router_front_workspace_size": (c_size_t, [POINTER(LayerDesc)]),
     "moe_router_front": (c_int32, [POINTER(LayerDesc), c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
-                                   c_void_p, c_void_p]),
+                                   c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_route_topk": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                  c_int32, c_float, c_void_p, c_void_p, c_void_p]),
     "moe_permute_max_rows": (c_int64, [c_int32, c_int32, c_int32, c_int32, c_int32]),

@@ -72,7 +72,13 @@ constexpr int kLdsBudget = 150 * 1024;
 // one or two row blocks and stream from HBM) the 128-row tile also runs 8
 // waves (2 x 4, each 64 x 64): a 128 x 256 tile whose 48 KB stages fit 3
 // deep in LDS, so the weight copies get two steps to land instead of one.
-constexpr int nw_of(int mode, int bm) { return bm == 256 || (bm == 128 && mode == MOE_QUANT_BLOCK128_FP8) ? 8 : 4; }
+// MXFP4 takes the same 8-wave 128-row tile (its 256-row tile's scale words
+// do not fit the register budget of two waves per SIMD).  The quantized
+// modes also have a 192-row tile (8 waves 2 x 4, each 96 x 64): more MFMA
+// work per copied byte than 128 rows, and within MXFP4's register budget.
+constexpr int nw_of(int mode, int bm) {
+    return bm >= 192 || (bm == 128 && (mode == MOE_QUANT_BLOCK128_FP8 || mode == MOE_QUANT_MXFP4)) ? 8 : 4;
+}
 constexpr int wm_of(int bm) { return bm >= 128 ? 2 : 1; }
 
 // 32-row weight tiles per wave: 4 for PTPC where the weight rows divide into
@@ -705,10 +711,19 @@ static int32_t launch_bm(int block_m, const GemmArgs& a, hipStream_t s) {
                                a);
             return moe_launch_status();
         }
-        if (block_m == 128 && (TN == 2 || nw_of(MODE, 128) == 4)) {
-            hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 128, TN>), grid, dim3(nw_of(MODE, 128) * 64), 0, s,
-                               a);
-            return moe_launch_status();
+        if constexpr (TN == 2 || nw_of(MODE, 128) == 4) {   // tn_of gives the 8-wave 128-row tile 2
+            if (block_m == 128) {
+                hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 128, TN>), grid, dim3(nw_of(MODE, 128) * 64), 0,
+                                   s, a);
+                return moe_launch_status();
+            }
+        }
+        if constexpr (TN == 2 && MODE != MOE_QUANT_NONE_BF16) {
+            if (block_m == 192) {
+                hipLaunchKernelGGL((grouped_gemm_kernel<MODE, GATEUP, 192, TN>), grid, dim3(nw_of(MODE, 192) * 64), 0,
+                                   s, a);
+                return moe_launch_status();
+            }
         }
         if constexpr (TN == 2 && MODE != MOE_QUANT_MXFP4) {   // tn_of gives the 256-row tile 2 weight tiles per wave
             if (block_m == 256) {

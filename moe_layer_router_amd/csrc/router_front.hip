@@ -3,15 +3,17 @@
 // The router gate scores every token against the routed experts (Qwen 3.5
 // TPU page, MoE paragraph of the model description), and the page's roadmap
 // item asks for the top-k selection to happen where the scores are computed
-// instead of moving the logits between units.  Here one workgroup takes 32
-// tokens against all E experts:
-//   1. logits[t, e] = x[t] . Wr[e] on the matrix cores.  x is bf16; each
-//      fp32 router weight is split exactly into three bf16 pieces
-//      (hi = bf16(w), mid = bf16(w - hi), lo = w - hi - mid, which has at most
-//      8 significant bits), so every product x * piece is exact in fp32 and
-//      v_mfma_f32_32x32x16_bf16 only adds: the logits carry nothing but fp32
-//      accumulation rounding.  The weight rows are the first operand, so lane
-//      (token l % 32) ends with 16 experts of its token per 32-expert tile.
+// instead of moving the logits between units.  Here one workgroup (8 waves)
+// takes 32 tokens against all E experts:
+//   0. (a separate small launch) each fp32 router weight is split exactly
+//      into three bf16 pieces, hi = bf16(w), mid = bf16(w - hi),
+//      lo = w - hi - mid (at most 8 significant bits), stored in the MFMA's
+//      lane order so that every operand load below is one contiguous 1 KB;
+//   1. logits[t, e] = x[t] . Wr[e] on the matrix cores: every product
+//      x * piece is exact in fp32 and v_mfma_f32_32x32x16_bf16 only adds, so
+//      the logits carry nothing but fp32 accumulation rounding.  The weight
+//      rows are the first operand, so lane (token l % 32) ends with 16
+//      experts of its token per 32-expert tile.
 //   2. The tile's logits go to LDS (and to the logits buffer); each wave then
 //      routes 8 of the tokens with the wave-per-token top-k (route_token).
 //   3. The same tokens' x rows are quantized to FP8 (one scale per row or
@@ -22,18 +24,29 @@
 #include "quant_dev.h"
 #include "route_dev.h"
 
+#include <utility>
+
 namespace moe {
 
 typedef __bf16 v8bf_r __attribute__((ext_vector_type(8)));
 typedef float v16f_r __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_r __attribute__((ext_vector_type(4)));
 
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_r(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_r(f, std::make_integer_sequence<int, N>{});
+}
+
 constexpr int kRouterTokens = 32;
 constexpr int kRouterMaxE = 512;
 
 struct RouterArgs {
     const uint16_t* x;
-    const float* wr;
+    const u32x4_r* prep;       // the prepared router weight (router_prep_kernel)
     int T, D, E, k;
     int n_groups, topk_groups;
     const float* sel_bias;
@@ -47,91 +60,194 @@ struct RouterArgs {
 };
 
 // w == hi + mid + lo exactly, each piece a bf16 (see the file comment).
-__device__ __forceinline__ void split3(const float (&w)[8], v8bf_r& hi, v8bf_r& mid, v8bf_r& lo) {
-    uint16_t h[8], m[8], l[8];
+__device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+    hi = f32_to_bf16(w);
+    const float r1 = w - bf16_to_f32(hi);        // exact
+    mid = f32_to_bf16(r1);
+    lo = f32_to_bf16(r1 - bf16_to_f32(mid));     // exact, and exactly a bf16
+}
+
+// Prepared router weight: for 32-expert tile et, K step s (64 elements),
+// 16-wide chunk c and piece p (0 hi, 1 mid, 2 lo) one 1 KB block in MFMA
+// lane order -- lane l = (r, kh) holds the 8 bf16 pieces of expert
+// 32 et + r, elements [64 s + 32 kh + 8 c, +8) -- so that every operand load
+// of the router kernel is one contiguous 1 KB (8 whole lines) per wave.
+// Block ((et * nsteps + s) * 4 + c) * 3 + p; experts past E are zero.
+__host__ __device__ inline int64_t router_prep_bytes(int E, int D) {
+    return static_cast<int64_t>((E + 31) / 32) * (D / 64) * 12 * 1024;
+}
+
+__global__ void __launch_bounds__(256) router_prep_kernel(const float* __restrict__ wr, int E, int D,
+                                                          uint16_t* __restrict__ prep) {
+    const int nsteps = D >> 6;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (et, s, c, lane)
+    const int64_t n = static_cast<int64_t>((E + 31) / 32) * nsteps * 4 * 64;
+    if (i >= n) return;
+    const int l = static_cast<int>(i & 63), c = static_cast<int>((i >> 6) & 3);
+    const int64_t es = i >> 8;                        // et * nsteps + s
+    const int s = static_cast<int>(es % nsteps), et = static_cast<int>(es / nsteps);
+    const int e = et * 32 + (l & 31);
+    const int k0 = 64 * s + 32 * (l >> 5) + 8 * c;
+    uint16_t h[8], m[8], lo[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        h[i] = f32_to_bf16(w[i]);
-        const float r1 = w[i] - bf16_to_f32(h[i]);       // exact
-        m[i] = f32_to_bf16(r1);
-        l[i] = f32_to_bf16(r1 - bf16_to_f32(m[i]));     // exact, and exactly a bf16
+    for (int q = 0; q < 8; ++q) {
+        const float w = e < E ? wr[static_cast<int64_t>(e) * D + k0 + q] : 0.0f;
+        split3(w, h[q], m[q], lo[q]);
     }
-    hi = __builtin_bit_cast(v8bf_r, h);
-    mid = __builtin_bit_cast(v8bf_r, m);
-    lo = __builtin_bit_cast(v8bf_r, l);
+    u32x4_r* out = reinterpret_cast<u32x4_r*>(prep) + ((es * 4 + c) * 3) * 64 + l;
+    out[0] = __builtin_bit_cast(u32x4_r, h);
+    out[64] = __builtin_bit_cast(u32x4_r, m);
+    out[128] = __builtin_bit_cast(u32x4_r, lo);
 }
 
 // EPT: 32-expert tiles per wave (E <= 128 * EPT); EPL: experts per lane in
 // the top-k (E <= 64 * EPL); GROUP: -1 (bf16 layer, x not quantized), 0 (per
-// row), 128 (1x128 groups).
+// row), 128 (1x128 groups), 32 (MXFP4).
+//
+// 8 waves: wave w takes the expert tiles w % 4, w % 4 + 4, ... over one half
+// of K (w / 4), so two waves per SIMD keep loads in flight; the second half's
+// partial sums are added to the first's through LDS in a fixed order (the
+// result does not depend on timing).  Each half's x rows move through LDS
+// two K steps (128 elements) at a time: the four waves of the half load the
+// 32 rows x 256 bytes with 16 lanes per row (whole lines), the next chunk's
+// loads in flight while the current chunk multiplies.  The prepared weight
+// pieces go straight to registers, the next (step, tile) unit loading while
+// the current one multiplies (a two-deep ring at constant indices).
 template <int EPT, int EPL, int SCORING, int GROUP>
-__global__ void __launch_bounds__(256) router_front_kernel(const RouterArgs p) {
-    constexpr int LD = EPT * 128 + 1;                 // LDS row stride (floats)
-    __shared__ float s_lg[kRouterTokens][LD];
+__global__ void __launch_bounds__(512) router_front_kernel(const RouterArgs p) {
+    constexpr int LD = EPT * 128 + 1;                       // logits row stride (floats)
+    constexpr int XROW = 2 * 128 + 16;                      // staged x row: 2 steps of 128 bytes + pad
+    constexpr int XBUF = kRouterTokens * XROW;              // one half's chunk buffer
+    constexpr int X_BYTES = 2 * 2 * XBUF;                   // [half][buffer]
+    constexpr int LG_BYTES = kRouterTokens * LD * 4;
+    constexpr int PART_BYTES = 4 * EPT * 16 * 64 * 4;
+    constexpr int RAW = X_BYTES > LG_BYTES + PART_BYTES ? X_BYTES : LG_BYTES + PART_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t s_raw[RAW];
+    // the x staging area is reused after the K loop for the logits and the
+    // second half's partial sums
+    float (*s_lg)[LD] = reinterpret_cast<float (*)[LD]>(s_raw);
+    float (*s_part)[EPT][16][64] = reinterpret_cast<float (*)[EPT][16][64]>(s_raw + LG_BYTES);
+
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tg = wave & 3, half = wave >> 2;
     const int t0 = blockIdx.x * kRouterTokens;
     const int r = lane & 31, kh = lane >> 5;
+    const int nsteps = p.D >> 6;
+    const int s_beg = half * (nsteps >> 1);
+    const int nchunks = nsteps >> 2;                        // 2-step chunks per half (D % 256 == 0)
 
-    // Lane (r, kh) supplies, for K step s and 16-wide chunk c, the elements
-    // [64 s + 32 kh + 8 c, +8) of its token row and of its expert rows: both
-    // operands use the same K positions, so the products pair up.
-    const int tok = min(t0 + r, p.T - 1);               // rows past T read the last token (not stored)
-    const uint16_t* xr = p.x + static_cast<int64_t>(tok) * p.D + kh * 32;
-    const float* wrow[EPT];
+    // x staging: thread tg * 64 + lane of this half copies 16-byte segment
+    // (idx % 16) of row idx / 16, idx = that thread + 256 rho (rho = 0, 1)
+    const int cthr = tg * 64 + lane;
+    const uint8_t* xsrc[2];
+    int xdst[2];
+#pragma unroll
+    for (int rho = 0; rho < 2; ++rho) {
+        const int idx = cthr + 256 * rho, row = idx >> 4, seg = idx & 15;
+        const int tok = min(t0 + row, p.T - 1);             // rows past T read the last token (not used)
+        xsrc[rho] = reinterpret_cast<const uint8_t*>(p.x) + (static_cast<int64_t>(tok) * p.D + 64 * s_beg) * 2 +
+                    seg * 16;
+        xdst[rho] = half * 2 * XBUF + row * XROW + seg * 16;
+    }
+    u32x4_r xg[2];
+    auto xload = [&](int ch) {
+#pragma unroll
+        for (int rho = 0; rho < 2; ++rho) xg[rho] = *reinterpret_cast<const u32x4_r*>(xsrc[rho] + ch * 256);
+    };
+    auto xstore = [&](int buf) {
+#pragma unroll
+        for (int rho = 0; rho < 2; ++rho) *reinterpret_cast<u32x4_r*>(s_raw + xdst[rho] + buf * XBUF) = xg[rho];
+    };
+
+    // Lane (r, kh) supplies, for K step s and chunk c, the elements
+    // [64 s + 32 kh + 8 c, +8) of its token row (from LDS) and of its expert
+    // rows (prepared): both operands use the same K positions.
+    const u32x4_r* wp[EPT];
     bool tile_on[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const int et = wave + 4 * j;
+        const int et = tg + 4 * j;
         tile_on[j] = et * 32 < p.E;
-        const int e = et * 32 + r;
-        wrow[j] = p.wr + static_cast<int64_t>(e < p.E ? e : 0) * p.D + kh * 32;
+        wp[j] = p.prep + static_cast<int64_t>(tile_on[j] ? et : 0) * nsteps * 12 * 64 + lane;
     }
     v16f_r acc[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[j] = v16f_r{};
 
-    const int nsteps = p.D >> 6;
-    for (int s = 0; s < nsteps; ++s) {
-        const int ko = s * 64;
-        u32x4_r xa[4];
+    u32x4_r xa[2][4], wa[2][12];
+    auto wload = [&](auto B, int s, int j) {
+        constexpr int b = decltype(B)::value;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xa[c] = *reinterpret_cast<const u32x4_r*>(xr + ko + 8 * c);
+        for (int q = 0; q < 12; ++q) wa[b][q] = wp[j][(static_cast<int64_t>(s) * 12 + q) * 64];
+    };
+    auto compute = [&](auto B, auto DS, int j) {
+        constexpr int b = decltype(B)::value, ds = decltype(DS)::value;
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            if (!tile_on[j]) continue;                    // wave-uniform
-            float4 wf[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) wf[q] = *reinterpret_cast<const float4*>(wrow[j] + ko + 4 * q);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float w8[8] = {wf[2 * c].x, wf[2 * c].y, wf[2 * c].z, wf[2 * c].w,
-                                     wf[2 * c + 1].x, wf[2 * c + 1].y, wf[2 * c + 1].z, wf[2 * c + 1].w};
-                v8bf_r hi, mid, lo;
-                split3(w8, hi, mid, lo);
-                const v8bf_r xb = __builtin_bit_cast(v8bf_r, xa[c]);
-                // smallest pieces first
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, xb, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, xb, acc[j], 0, 0, 0);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, xb, acc[j], 0, 0, 0);
-            }
+        for (int c = 0; c < 4; ++c) {
+            const v8bf_r xb = __builtin_bit_cast(v8bf_r, xa[ds][c]);
+            // smallest pieces first
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf_r, wa[b][3 * c + 2]), xb, acc[j],
+                                                             0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf_r, wa[b][3 * c + 1]), xb, acc[j],
+                                                             0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf_r, wa[b][3 * c]), xb, acc[j],
+                                                             0, 0, 0);
         }
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    xload(0);
+    xstore(0);
+    wload(B0{}, s_beg, 0);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int buf = ch & 1, s = s_beg + 2 * ch;
+        if (ch + 1 < nchunks) xload(ch + 1);                 // in flight during this chunk
+        // this chunk's x fragments of both steps
+        const uint8_t* xs = s_raw + half * 2 * XBUF + buf * XBUF + r * XROW + kh * 64;
+#pragma unroll
+        for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xa[ds][c] = *reinterpret_cast<const u32x4_r*>(xs + ds * 128 + c * 16);
+        static_for<2 * EPT>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            constexpr int j = u % EPT, nj = (u + 1) % EPT, nds = (u + 1) / EPT;
+            using Cur = std::integral_constant<int, u & 1>;
+            using Nxt = std::integral_constant<int, (u + 1) & 1>;
+            using DS = std::integral_constant<int, u / EPT>;
+            if (s + nds < s_beg + 2 * nchunks) wload(Nxt{}, s + nds, nj);
+            if (tile_on[j]) compute(Cur{}, DS{}, j);
+        });
+        if (ch + 1 < nchunks) xstore(buf ^ 1);
+        __syncthreads();
     }
 
+    // second half -> LDS; first half adds it (fixed order) and owns the tile
+    if (half) {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            if (tile_on[j])
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s_part[tg][j][v][lane] = acc[j][v];
+    }
+    __syncthreads();
     // lane (r, kh): token r, register v holds expert 8 (v / 4) + 4 kh + v % 4 of the tile
-    const bool tok_ok = t0 + r < p.T;
+    if (!half) {
+        const bool tok_ok = t0 + r < p.T;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        if (!tile_on[j]) continue;
-        const int ebase = (wave + 4 * j) * 32;
+        for (int j = 0; j < EPT; ++j) {
+            if (!tile_on[j]) continue;
+            const int ebase = (tg + 4 * j) * 32;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int e0 = ebase + 8 * g + 4 * kh;
+            for (int g = 0; g < 4; ++g) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = e0 + i;
-                if (e < p.E) {
-                    s_lg[r][e] = acc[j][4 * g + i];
-                    if (tok_ok) p.logits[static_cast<int64_t>(t0 + r) * p.E + e] = acc[j][4 * g + i];
+                for (int i = 0; i < 4; ++i) {
+                    const int e = ebase + 8 * g + 4 * kh + i;
+                    const float l = acc[j][4 * g + i] + s_part[tg][j][4 * g + i][lane];
+                    if (e < p.E) {
+                        s_lg[r][e] = l;
+                        if (tok_ok) p.logits[static_cast<int64_t>(t0 + r) * p.E + e] = l;
+                    }
                 }
             }
         }
@@ -139,7 +255,7 @@ __global__ void __launch_bounds__(256) router_front_kernel(const RouterArgs p) {
     __syncthreads();
 
     // top-k of each token, one wave per token, from the logits in LDS
-    for (int tt = wave; tt < kRouterTokens; tt += 4) {
+    for (int tt = wave; tt < kRouterTokens; tt += 8) {
         const int t = t0 + tt;
         if (t >= p.T) break;
         int id;
@@ -152,9 +268,9 @@ __global__ void __launch_bounds__(256) router_front_kernel(const RouterArgs p) {
         }
     }
 
-    // FP8 codes of the same tokens' x rows
+    // the same tokens' x rows in the layer's activation format
     if constexpr (GROUP >= 0) {
-        for (int tt = wave; tt < kRouterTokens; tt += 4) {
+        for (int tt = wave; tt < kRouterTokens; tt += 8) {
             const int t = t0 + tt;
             if (t >= p.T) break;
             quant_x_row<GROUP>(p.x, p.D, t, p.xq, p.xs, lane);
@@ -164,10 +280,10 @@ __global__ void __launch_bounds__(256) router_front_kernel(const RouterArgs p) {
 
 template <int EPT, int EPL, int SCORING>
 static void router_launch_group(int group, dim3 g, hipStream_t s, const RouterArgs& a) {
-    if (group < 0) hipLaunchKernelGGL((router_front_kernel<EPT, EPL, SCORING, -1>), g, dim3(256), 0, s, a);
-    else if (group == 0) hipLaunchKernelGGL((router_front_kernel<EPT, EPL, SCORING, 0>), g, dim3(256), 0, s, a);
-    else if (group == 32) hipLaunchKernelGGL((router_front_kernel<EPT, EPL, SCORING, 32>), g, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((router_front_kernel<EPT, EPL, SCORING, 128>), g, dim3(256), 0, s, a);
+    if (group < 0) hipLaunchKernelGGL((router_front_kernel<EPT, EPL, SCORING, -1>), g, dim3(512), 0, s, a);
+    else if (group == 0) hipLaunchKernelGGL((router_front_kernel<EPT, EPL, SCORING, 0>), g, dim3(512), 0, s, a);
+    else if (group == 32) hipLaunchKernelGGL((router_front_kernel<EPT, EPL, SCORING, 32>), g, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((router_front_kernel<EPT, EPL, SCORING, 128>), g, dim3(512), 0, s, a);
 }
 
 template <int EPT, int EPL>
@@ -176,19 +292,26 @@ static void router_launch_scoring(int scoring, int group, dim3 g, hipStream_t s,
     else router_launch_group<EPT, EPL, 1>(group, g, s, a);
 }
 
-bool router_front_ok(int E, int D) { return E <= kRouterMaxE && D % 64 == 0; }
+bool router_front_ok(int E, int D) { return E <= kRouterMaxE && D % 256 == 0; }
 
-// group: -1 (no x quantization), 0, 128 or 32 (MXFP4).  The caller has validated the
-// layer (router_front_ok, routing limits).
+int64_t router_front_scratch_bytes(int E, int D) { return router_prep_bytes(E, D); }
+
+// group: -1 (no x quantization), 0, 128 or 32 (MXFP4).  scratch: at least
+// router_front_scratch_bytes(E, D) bytes, 16-byte aligned.  The caller has
+// validated the layer (router_front_ok, routing limits).
 int32_t router_front_launch(const moe_layer_desc* L, const void* x, int T, int group, float* logits, int* ids,
-                            float* w, uint8_t* xq, float* xs, hipStream_t s) {
+                            float* w, uint8_t* xq, float* xs, void* scratch, hipStream_t s) {
     if (T == 0) return MOE_OK;
+    const int E = L->E, D = L->D;
+    const int64_t nthreads = static_cast<int64_t>((E + 31) / 32) * (D / 64) * 4 * 64;
+    hipLaunchKernelGGL(router_prep_kernel, dim3(static_cast<unsigned>(ceil_div(nthreads, 256))), dim3(256), 0, s,
+                       L->router_w, E, D, static_cast<uint16_t*>(scratch));
     RouterArgs a{};
     a.x = static_cast<const uint16_t*>(x);
-    a.wr = L->router_w;
+    a.prep = static_cast<const u32x4_r*>(scratch);
     a.T = T;
-    a.D = L->D;
-    a.E = L->E;
+    a.D = D;
+    a.E = E;
     a.k = L->top_k;
     a.n_groups = L->n_groups;
     a.topk_groups = L->topk_groups;
@@ -201,7 +324,6 @@ int32_t router_front_launch(const moe_layer_desc* L, const void* x, int T, int g
     a.xq = xq;
     a.xs = xs;
     const dim3 g(static_cast<unsigned>(ceil_div(T, kRouterTokens)));
-    const int E = L->E;
     if (E <= 64) router_launch_scoring<1, 1>(L->scoring, group, g, s, a);
     else if (E <= 128) router_launch_scoring<1, 2>(L->scoring, group, g, s, a);
     else if (E <= 256) router_launch_scoring<2, 4>(L->scoring, group, g, s, a);

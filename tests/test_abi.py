@@ -124,6 +124,12 @@ def test_layer_validation_and_workspace():
     assert lib.moe_default_block_m(ctypes.byref(d), 64) == 16
     assert lib.moe_default_block_m(ctypes.byref(_desc(E=128, top_k=8)), 256) == 32
     assert lib.moe_default_block_m(ctypes.byref(_desc(E=128, top_k=8)), 8192) == 256
+    # about 143 rows per expert (the DeepSeek-R1-shaped batch): one 192-row tile; MXFP4 stays at 128
+    r1 = dict(E=256, top_k=8, n_shared=1, scoring=1, n_groups=8, topk_groups=4)
+    assert lib.moe_default_block_m(ctypes.byref(_desc(quant=2, **r1)), 4096) == 192
+    assert lib.moe_default_block_m(ctypes.byref(_desc(quant=3, I=512, **r1)), 4096) == 128
+    assert lib.moe_default_block_m(ctypes.byref(_desc(quant=0, weight_layout=0, w13_scale=None, w2_scale=None,
+                                                       **r1)), 4096) == 256
     assert lib.moe_forward(ctypes.byref(_desc(I=200)), None, None, 4, 0, None, None, 0, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_forward(ctypes.byref(_desc(w13=None)), None, None, 4, 0, None, None, 0, None) \
         == L.MOE_ERR_INVALID_ARG
@@ -158,7 +164,7 @@ def test_workspace_layout_is_disjoint_and_aligned():
                  (_desc(quant=2, n_shared=1, scoring=1, n_groups=4, topk_groups=2, route_scale=2.5), 77)]:
         lay = L.WsLayout()
         assert lib.moe_workspace_layout(ctypes.byref(d), T, 0, ctypes.byref(lay)) == L.MOE_OK
-        offs = sorted(getattr(lay, n) for n, _ in L.WsLayout._fields_[:15] if getattr(lay, n) >= 0)
+        offs = sorted(getattr(lay, n) for n, _ in L.WsLayout._fields_[:16] if getattr(lay, n) >= 0)
         assert all(o % 256 == 0 for o in offs)
         assert len(set(offs)) == len(offs)
         assert lay.total == lib.moe_forward_workspace_size(ctypes.byref(d), T, 0)

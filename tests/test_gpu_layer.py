@@ -52,7 +52,8 @@ def _check_exact(inter, ref, quant):
                                           ("qwen3_235b_decode_ptpc_t64", 0), ("qwen3_235b_decode_ptpc", 32),
                                           ("bf16_small_t20", 0), ("qwen3_235b_prefill_ptpc_r", 16),
                                           ("deepseek_r1_block_fp8_r", 16), ("e512_top10_shared_r", 0),
-                                          ("e512_top10_shared_r", 128), ("e512_top10_shared_r", 16)])
+                                          ("e512_top10_shared_r", 128), ("e512_top10_shared_r", 16),
+                                          ("qwen3_235b_prefill_ptpc_r", 192), ("deepseek_r1_block_fp8_r", 192)])
 def test_forward_matches_oracle(name, block_m):
     w = REDUCED[name]
     say("forward", name, block_m)

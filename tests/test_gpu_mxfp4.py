@@ -77,6 +77,7 @@ def test_mx_weights(layout):
 @pytest.mark.parametrize("name,block_m", [("qwen3_235b_prefill_mxfp4_r", 0), ("qwen3_235b_prefill_mxfp4_r", 32),
                                           ("qwen3_235b_prefill_mxfp4_r", 64), ("deepseek_r1_mxfp4_r", 0),
                                           ("deepseek_r1_mxfp4_r", 32), ("deepseek_r1_mxfp4_r", 128),
+                                          ("qwen3_235b_prefill_mxfp4_r", 192), ("deepseek_r1_mxfp4_r", 192),
                                           ("deepseek_r1_mxfp4_small", 0)])
 def test_forward_mxfp4(name, block_m):
     w = REDUCED[name]
@@ -86,7 +87,7 @@ def test_forward_mxfp4(name, block_m):
     torch.cuda.synchronize()
     inter = c.layer.intermediates(w.T, block_m)
     B = inter["block_m"]
-    assert B in (32, 64, 128)
+    assert B in (32, 64, 128, 192)
     ref = O.moe_forward(c.spec, c.bank, c.x_np(), c.logits_np(), block_m=B)
     assert np.array_equal(inter["topk_ids"].cpu().numpy(), ref["ids"])
     for key in ("counts", "offsets", "sorted_ids", "block_expert", "inv_perm"):

@@ -58,9 +58,13 @@ def _front(c, T):
     wt = torch.empty((T, w.k), dtype=torch.float32, device=dev)
     xq = torch.empty((T, w.D), dtype=torch.uint8, device=dev) if fp8 else None
     xs = torch.empty((T, w.D // 128) if blk else (T,), dtype=torch.float32, device=dev) if fp8 else None
+    nws = int(L.lib().moe_router_front_workspace_size(ctypes.byref(c.layer.desc)))
+    assert nws > 0
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
     st = L.lib().moe_router_front(ctypes.byref(c.layer.desc), c.x.data_ptr(), T, lg.data_ptr(), ids.data_ptr(),
                                   wt.data_ptr(), None if xq is None else xq.data_ptr(),
-                                  None if xs is None else xs.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                                  None if xs is None else xs.data_ptr(), ws.data_ptr(), nws,
+                                  torch.cuda.current_stream().cuda_stream)
     L.check("moe_router_front", st)
     torch.cuda.synchronize()
     return lg, ids, wt, xq, xs
@@ -146,7 +150,11 @@ def test_router_front_validation():
     c = build_case(w.replace(T=4))
     d = L.LayerDesc.from_buffer_copy(c.layer.desc)
     d.router_w = None
-    assert L.lib().moe_router_front(ctypes.byref(d), 1, 4, 1, 1, 1, 1, 1, None) == L.MOE_ERR_INVALID_ARG
+    assert L.lib().moe_router_front(ctypes.byref(d), 1, 4, 1, 1, 1, 1, 1, 256, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
     d = L.LayerDesc.from_buffer_copy(c.layer.desc)
-    assert L.lib().moe_router_front(ctypes.byref(d), 1, 4, 1, 1, 1, None, None, None) == L.MOE_ERR_INVALID_ARG
-    assert L.lib().moe_router_front(ctypes.byref(d), None, 0, None, None, None, None, None, None) == L.MOE_OK
+    assert L.lib().moe_router_front(ctypes.byref(d), 1, 4, 1, 1, 1, None, None, 256, 1 << 30, None) \
+        == L.MOE_ERR_INVALID_ARG
+    need = int(L.lib().moe_router_front_workspace_size(ctypes.byref(d)))
+    assert need == (w.E + 31) // 32 * (w.D // 64) * 12 * 1024
+    assert L.lib().moe_router_front(ctypes.byref(d), 1, 4, 1, 1, 1, 1, 1, 256, need - 1, None) == L.MOE_ERR_WORKSPACE
+    assert L.lib().moe_router_front(ctypes.byref(d), None, 0, None, None, None, None, None, None, 0, None) == L.MOE_OK
