@@ -23,6 +23,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// two fp32 -> bf16, round to nearest even, packed (a in the low half): one
+// v_cvt_pk_bf16_f32; the same values as f32_to_bf16 for finite inputs
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
+// SwiGLU: silu(g) * u = g / (1 + e^-g) * u, with the hardware base-2
+// exponential and reciprocal (each within about 1 ulp in fp32, far below the
+// bf16 rounding that follows)
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f)) * u;
+}
+
 // ---------------------------------------------------------------- e4m3fn
 // OCP e4m3fn: bias 7, 3 mantissa bits, subnormals m * 2^-9, max 448 (0x7E),
 // 0x7F/0xFF NaN.  Value of a code (encoding uses the hardware converter

@@ -127,7 +127,6 @@ __device__ __forceinline__ v8i cat8(u32x4 lo, u32x4 hi) {
     return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // Global -> LDS copies.  Each lane's bytes land at M0 + size * lane; M0 must
 // be wave-uniform.  Issued as inline asm so that the only waits on them are
@@ -668,9 +667,7 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
                     }
                     uint8_t* dst = reg + r32 * RBP + (t * 32 + 8 * g + 4 * q) * OBYTES;
                     if constexpr (OBYTES == 2) {
-                        const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-                        const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-                        *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+                        *reinterpret_cast<uint2*>(dst) = uint2{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])};
                     } else {
                         *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
                     }

@@ -79,7 +79,6 @@ __device__ __forceinline__ u32x8 ld32(const uint8_t* p, int hi_off) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ float silu_mul_s(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 __device__ __forceinline__ int src_row(const StreamArgs& p, bool gateup, int row, bool& valid) {
     if (!gateup) { valid = true; return row; }
@@ -250,7 +249,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
                         g *= wsx[col];
                         u *= wsx[p.I + col];
                     }
-                    static_cast<uint16_t*>(p.out)[orow + col] = f32_to_bf16(silu_mul_s(g, u));
+                    static_cast<uint16_t*>(p.out)[orow + col] = f32_to_bf16(silu_mul(g, u));
                 }
             } else {
 #pragma unroll
