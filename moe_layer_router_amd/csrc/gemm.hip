@@ -227,10 +227,60 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     // rows of the block that hold routed rows (the expert's pads follow them)
     const int live = p.counts ? min(BM, max(0, p.offsets[e] + p.counts[e] - m0)) : BM;
 
-    // Row tokens go to LDS before the copies can start.  The PTPC row and
-    // channel scales are only needed by the epilogue: their loads go out
-    // here but land in LDS after the main loop, so the copies do not wait
-    // for them.
+    // Copy j of a wave fills 8 LDS rows of block wave + NW*j: lane i writes
+    // row 8*blk + i/8, physical chunk i%8, which holds logical chunk
+    // (i%8) ^ swizzle(row) of that row.
+    const int crow = lane >> 3, cphys = lane & 7;
+    // weight tile row t (LDS row BM + t) is row t % WCOLS of wave column t / WCOLS
+    // (gate rows first, then up rows)
+    const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
+    const int64_t wrow_bytes = MX ? static_cast<int64_t>(p.K) / 2 : static_cast<int64_t>(p.K) * ELEM;
+    const int nbig = static_cast<int>(wrow_bytes / kRow);   // steps; K bytes are a multiple of 128
+    uint32_t b_src[B_IN];                                   // byte offsets within the expert
+#pragma unroll
+    for (int j = 0; j < B_IN; ++j) {
+        const int t = (wave + NW * j) * 8 + crow;
+        const int c = cphys ^ (((BM + t) >> 1) & 7);
+        const int w = t / WCOLS, jj = t % WCOLS;
+        const int wr = GATEUP ? (jj < HALF ? n0 + w * HALF + jj : p.I + n0 + w * HALF + jj - HALF) : n0 + t;
+        // blocked weights: the 8 rows of a copy are half of one 2 KB block
+        // (16 rows x one 128-byte step), 8 whole lines of it
+        b_src[j] = static_cast<uint32_t>(p.w_blocked ? (wr >> 4) * (wrow_bytes / kRow) * 2048 + blocked_byte(wr & 15, c * 16)
+                                                     : wr * wrow_bytes + c * 16);
+    }
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+    // weight copy j of step S into LDS stage BUF
+    auto issue_b = [&](int j, int S, int buf) {
+        const int64_t kw = static_cast<int64_t>(S) * (p.w_blocked ? 2048 : kRow);   // step offset in the weights
+        dma16(b_src[j], wexp + kw,
+              __builtin_amdgcn_readfirstlane(lds0 + buf * STAGE + (BM + (wave + NW * j) * 8) * kRow));
+    };
+    // Two stages without scale copies (PTPC and bf16): the weight copies of
+    // steps 0 and 1 and a copy of the tile's row ids into LDS go out before
+    // any other vector-memory access, so the weights' HBM latency overlaps
+    // the row ids' round trip instead of following it.  A wave reads back
+    // only the ids its own copy brought, once at most its weight copies are
+    // still in flight.
+    constexpr bool EARLY_B = NS == 2 && !BLOCKQ && !MX;
+    if constexpr (EARLY_B) {
+        if (p.sorted_ids && tid < BM)
+            dma4(p.sorted_ids + m0 + tid, __builtin_amdgcn_readfirstlane(
+                                              static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_tok)) + (tid & ~63) * 4));
+        for (int S = 0; S < NS; ++S)
+            if (S < nbig) {
+#pragma unroll
+                for (int j = 0; j < B_IN; ++j) issue_b(j, S, S);
+            }
+        if (p.sorted_ids) {
+            if (nbig >= 2) vmcnt_wait<2 * B_IN>();
+            else vmcnt_wait<B_IN>();
+        }
+    }
+
+    // Row tokens go to LDS before the activation copies can start.  The PTPC
+    // row and channel scales are only needed by the epilogue: their loads go
+    // out here but land in LDS after the main loop, so the copies do not
+    // wait for them.
     constexpr bool PTPC = MODE == MOE_QUANT_PTPC_FP8;
     constexpr int CHN = PTPC ? (GATEUP ? 2 : 1) * TILE_N : 0;    // channel scales of the tile
     constexpr int CH_PER = (CHN + NT - 1) / NT;
@@ -241,7 +291,9 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
         int tok = tid < live ? m0 + tid : m0;
         rs = tid < live ? 1.0f : 0.0f;
         if (p.sorted_ids) {
-            const int f = p.sorted_ids[m0 + tid];
+            int f;
+            if constexpr (EARLY_B) f = s_tok[tid];
+            else f = p.sorted_ids[m0 + tid];
             const bool pad = f == p.sentinel;
             tok = pad ? 0 : (f < p.TK ? f / p.topk : f - p.TK);
             rs = pad ? 0.0f : 1.0f;
@@ -271,32 +323,12 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     };
     __syncthreads();
 
-    // Copy j of a wave fills 8 LDS rows of block wave + NW*j: lane i writes
-    // row 8*blk + i/8, physical chunk i%8, which holds logical chunk
-    // (i%8) ^ swizzle(row) of that row.
-    const int crow = lane >> 3, cphys = lane & 7;
     uint32_t a_src[A_IN];                                   // byte offsets within the activations
 #pragma unroll
     for (int j = 0; j < A_IN; ++j) {
         const int r = (wave + NW * j) * 8 + crow;
         const int c = cphys ^ ((r >> 1) & 7);
         a_src[j] = static_cast<uint32_t>(static_cast<int64_t>(s_tok[r]) * p.a_ld + c * 16);
-    }
-    // weight tile row t (LDS row BM + t) is row t % WCOLS of wave column t / WCOLS
-    // (gate rows first, then up rows)
-    const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
-    const int64_t wrow_bytes = MX ? static_cast<int64_t>(p.K) / 2 : static_cast<int64_t>(p.K) * ELEM;
-    uint32_t b_src[B_IN];                                   // byte offsets within the expert
-#pragma unroll
-    for (int j = 0; j < B_IN; ++j) {
-        const int t = (wave + NW * j) * 8 + crow;
-        const int c = cphys ^ (((BM + t) >> 1) & 7);
-        const int w = t / WCOLS, jj = t % WCOLS;
-        const int wr = GATEUP ? (jj < HALF ? n0 + w * HALF + jj : p.I + n0 + w * HALF + jj - HALF) : n0 + t;
-        // blocked weights: the 8 rows of a copy are half of one 2 KB block
-        // (16 rows x one 128-byte step), 8 whole lines of it
-        b_src[j] = static_cast<uint32_t>(p.w_blocked ? (wr >> 4) * (wrow_bytes / kRow) * 2048 + blocked_byte(wr & 15, c * 16)
-                                                     : wr * wrow_bytes + c * 16);
     }
     // With two stages every in-loop wait is for all outstanding copies, so a
     // wave may leave out the copies of its 8-row groups that lie in 32-row
@@ -338,8 +370,6 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
             ws_src[j] = p.w_mx + e * p.w_mx_expert + static_cast<int64_t>(wr) * kb + 4 * (d & 1);
         }
     }
-    const int nbig = static_cast<int>(wrow_bytes / kRow);   // steps; K bytes are a multiple of 128
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     const uint32_t sc0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_ascale[0][0]));
     const uint32_t asc0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_asc[0][0]));
     const uint32_t wsc0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_wsc[0][0]));
@@ -348,14 +378,12 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
     auto issue_one = [&](auto D, int S, int buf) {
         constexpr int d = decltype(D)::value;
         const int64_t ko = static_cast<int64_t>(S) * kRow;
-        const int64_t kw = static_cast<int64_t>(S) * (p.w_blocked ? 2048 : kRow);   // step offset in the weights
         const uint32_t st = lds0 + buf * STAGE;
         if constexpr (d < A_IN) {
             if (!SKIP_DEAD || a_need[d])
                 dma16(a_src[d], p.a + ko, __builtin_amdgcn_readfirstlane(st + (wave + NW * d) * 8 * kRow));
         } else if constexpr (d < A_IN + B_IN) {
-            constexpr int j = d - A_IN;
-            dma16(b_src[j], wexp + kw, __builtin_amdgcn_readfirstlane(st + (BM + (wave + NW * j) * 8) * kRow));
+            issue_b(d - A_IN, S, buf);
         } else if constexpr (BLOCKQ && d == A_IN + B_IN) {
             dma4(sc_src + S, __builtin_amdgcn_readfirstlane(sc0 + (buf * 64 * NW + wave * 64) * 4));
         } else if constexpr (MX && d < A_IN + B_IN + AS_IN) {
@@ -533,11 +561,20 @@ __global__ void __launch_bounds__(nw_of(MODE, BM) * 64, 1) grouped_gemm_kernel(c
             }
         };
 
-        // Prologue: steps 0 .. NS-1 go out (every stage is free); wait for
+        // Prologue: steps 0 .. NS-1 go out (every stage is free; with early
+        // weight copies only their activation copies are left); wait for
         // step 0, then read the fragments of its first half.
         for (int S = 0; S < NS; ++S)
-            if (S < nbig) issue(S);
-        if (NS <= nbig) {
+            if (S < nbig) {
+                if constexpr (EARLY_B) static_for<A_IN>([&](auto D) { issue_one(D, S, S); });
+                else issue(S);
+            }
+        if (EARLY_B && NS <= nbig) {
+            // in flight after step 0's activation copies: those of step 1
+            static_for<A_IN + 1>([&](auto Dc) {
+                if (n_dead == decltype(Dc)::value) vmcnt_wait<A_IN - decltype(Dc)::value>();
+            });
+        } else if (NS <= nbig) {
             // wait for step 0; the copies of steps 1 .. NS-1 may stay in flight
             if constexpr (SKIP_DEAD) {
                 static_for<A_IN + 1>([&](auto Dc) {
