@@ -462,6 +462,9 @@ def permute_align(ids, E: int, n_shared: int, block_m: int) -> Dict[str, np.ndar
     Returns counts [E'], offsets [E'+1] (padded exclusive prefix sums),
     sorted_ids [max_rows], block_expert [max_rows/B] (-1 past the end) and
     inv_perm [T*(k+n_shared)] (flat index -> permuted row).
+
+    A routed pick outside [0, E) (the pages define no such id) gets no row:
+    it is not counted, appears nowhere in sorted_ids and has inv_perm -1.
     """
     ids = np.asarray(ids, dtype=np.int64)
     T, k = ids.shape if ids.ndim == 2 else (0, 0)
@@ -470,7 +473,9 @@ def permute_align(ids, E: int, n_shared: int, block_m: int) -> Dict[str, np.ndar
     flat_e = ids.reshape(-1)
     if n_shared:
         flat_e = np.concatenate([flat_e, np.full(T, E, dtype=np.int64)])
-    counts = np.bincount(flat_e, minlength=Ep).astype(np.int64)[:Ep]
+    valid = np.ones(A, dtype=bool)
+    valid[:T * k] = (flat_e[:T * k] >= 0) & (flat_e[:T * k] < E)
+    counts = np.bincount(flat_e[valid], minlength=Ep).astype(np.int64)[:Ep]
     padded = (counts + block_m - 1) // block_m * block_m
     offsets = np.zeros(Ep + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(padded)
@@ -480,6 +485,8 @@ def permute_align(ids, E: int, n_shared: int, block_m: int) -> Dict[str, np.ndar
     inv_perm = np.full(A, -1, dtype=np.int64)
     fill = offsets[:-1].copy()
     for f in range(A):                       # ascending flat index => stable
+        if not valid[f]:
+            continue
         e = flat_e[f]
         sorted_ids[fill[e]] = f
         inv_perm[f] = fill[e]

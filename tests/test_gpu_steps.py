@@ -137,14 +137,19 @@ def test_permute_degenerate_routing():
     r = O.permute_align(ids.numpy(), E, 0, 64)
     for key in ("counts", "offsets", "sorted_ids", "block_expert", "inv_perm"):
         assert np.array_equal(p[key].cpu().numpy(), r[key]), key
-    # ids outside [0, E) get no row and inv_perm -1
-    ids = _rand_ids(50, 4, 16, 3)
-    ids[5, 1] = 16
-    ids[7, 0] = -3
-    p = mlr.permute_align(ids.cuda(), 16, 0, 32)
-    inv = p["inv_perm"].cpu().numpy()
-    assert inv[5 * 4 + 1] == -1 and inv[7 * 4] == -1
-    assert int(p["counts"].sum()) == 50 * 4 - 2
+    # ids outside [0, E) get no row and inv_perm -1, as in the oracle
+    for ns in (0, 1):
+        ids = _rand_ids(50, 4, 16, 3)
+        ids[5, 1] = 16
+        ids[7, 0] = -3
+        ids[49, 3] = 1000
+        p = mlr.permute_align(ids.cuda(), 16, ns, 32)
+        r = O.permute_align(ids.numpy(), 16, ns, 32)
+        for key in ("counts", "offsets", "sorted_ids", "block_expert", "inv_perm"):
+            assert np.array_equal(p[key].cpu().numpy(), r[key]), (ns, key)
+        inv = p["inv_perm"].cpu().numpy()
+        assert inv[5 * 4 + 1] == -1 and inv[7 * 4] == -1 and inv[49 * 4 + 3] == -1
+        assert int(p["counts"].sum()) == 50 * (4 + ns) - 3
 
 
 # ------------------------------------------------------------------ quantization

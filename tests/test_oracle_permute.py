@@ -69,3 +69,36 @@ def test_max_rows_bound_is_tight():
     assert p["offsets"][-1] == E * B == p["max_rows"]
     # block count can never exceed the row count
     assert O.permute_max_rows(2, 1, 64, 0, 16) == 2 * 16
+
+
+@pytest.mark.parametrize("n_sh", [0, 1])
+def test_permute_picks_outside_the_experts_get_no_row(n_sh):
+    """Reading: a routed pick outside [0, E) gets no row.  Pinned against the
+    sorted-pairs construction over the valid picks only, by brute force."""
+    rng = np.random.default_rng(9)
+    T, E, k, B = 30, 12, 3, 4
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = [(2, 0, -1), (5, 2, E), (11, 1, E + 7), (29, 0, -40)]
+    for t, j, v in bad:
+        ids[t, j] = v
+    p = O.permute_align(ids, E, n_sh, B)
+    A = T * (k + n_sh)
+    Ep = E + n_sh
+    pairs = [(int(ids[t, j]), t * k + j) for t in range(T) for j in range(k) if 0 <= ids[t, j] < E]
+    pairs += [(E, T * k + t) for t in range(T)] if n_sh else []
+    pairs.sort()
+    assert list(p["counts"]) == [sum(1 for e, _ in pairs if e == x) for x in range(Ep)]
+    offs = p["offsets"]
+    for e in range(Ep):
+        c = int(p["counts"][e])
+        seg = p["sorted_ids"][offs[e]:offs[e + 1]]
+        assert offs[e + 1] - offs[e] == -(-c // B) * B
+        assert list(seg[:c]) == [f for x, f in pairs if x == e]
+        assert np.all(seg[c:] == A)
+    inv = p["inv_perm"]
+    for t, j, _ in bad:
+        assert inv[t * k + j] == -1
+    valid = [f for _, f in pairs]
+    assert sorted(int(v) for v in p["sorted_ids"] if v < A) == sorted(valid)
+    assert np.array_equal(p["sorted_ids"][inv[valid]], np.array(valid))
+    assert int(np.sum(inv == -1)) == len(bad)
