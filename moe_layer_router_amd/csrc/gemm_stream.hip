@@ -306,20 +306,24 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
     }
 }
 
-// 16-row weight tiles per wave (gate/up: a gate and an up tile) and K steps
-// in flight per wave.  One tile per wave for down spreads its items more
+// 16-row weight tiles per wave (gate/up: half gate, half up tiles) and K
+// steps in flight per wave.  Gate/up streams 4 tiles per wave (32 act
+// columns; one wave per SIMD; the blockwise mode keeps 2, its per-step
+// scales would not fit the registers): Qwen3-235B decode step 165.9 ->
+// 163.8 us against 2 tiles.  One tile per wave for down spreads its items more
 // evenly over the waves but halves the bytes each wave keeps in flight, and
-// measured slower (Qwen3-235B decode 178 -> 196 us); so did splitting only
-// the items of the last, partial round (177 -> 181 us): the waves share HBM
-// bandwidth, and the few that run a last round get more of it.
-template <bool GATEUP>
-constexpr int stream_tn() { return 2; }
+// measured slower (178 -> 196 us); so did splitting only the items of the
+// last, partial round (177 -> 181 us): the waves share HBM bandwidth, and
+// the few that run a last round get more of it.  3 or 6 steps in flight
+// instead of 4 were slower (167.4, 167.3 us).
+template <int MODE, bool GATEUP>
+constexpr int stream_tn() { return GATEUP && MODE != MOE_QUANT_BLOCK128_FP8 ? 4 : 2; }
 constexpr int kStreamPF = 4;
 
-// Workgroups of a kernel that fit on the device at once, per device.
+// Workgroups of a kernel that fit on the device at once, per device (CACHE:
+// one per kernel instantiation).
 template <typename Kern>
-static int resident_blocks(Kern kernel) {
-    static int cache[64];
+static int resident_blocks(Kern kernel, int (&cache)[64]) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
@@ -335,16 +339,18 @@ static int resident_blocks(Kern kernel) {
 
 template <int MODE, bool GATEUP, int MT>
 static int32_t stream_launch_mt(const StreamArgs& a, hipStream_t s) {
-    auto kern = stream_gemm_kernel<MODE, GATEUP, stream_tn<GATEUP>(), MT, kStreamPF>;
+    auto kern = stream_gemm_kernel<MODE, GATEUP, stream_tn<MODE, GATEUP>(), MT, kStreamPF>;
+    static int cache[64];
     // no more workgroups than items could need (E' experts x slices / 4 waves)
-    const int wgs = min(resident_blocks(kern), static_cast<int>(ceil_div(static_cast<int64_t>(a.n_exp) * a.nslice, 4)));
+    const int wgs = min(resident_blocks(kern, cache),
+                        static_cast<int>(ceil_div(static_cast<int64_t>(a.n_exp) * a.nslice, 4)));
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(max(wgs, 1))), dim3(256), 0, s, a);
     return moe_launch_status();
 }
 
 template <int MODE, bool GATEUP>
 static int32_t stream_launch_mode(StreamArgs a, int Ep, int ncols, int T, hipStream_t s) {
-    constexpr int COLS_W = GATEUP ? stream_tn<GATEUP>() / 2 * 16 : stream_tn<GATEUP>() * 16;
+    constexpr int COLS_W = GATEUP ? stream_tn<MODE, GATEUP>() / 2 * 16 : stream_tn<MODE, GATEUP>() * 16;
     a.n_exp = Ep;
     a.nslice = ncols / COLS_W;
     if (T <= 16) return stream_launch_mt<MODE, GATEUP, 1>(a, s);
