@@ -307,10 +307,12 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
 }
 
 // 16-row weight tiles per wave (gate/up: half gate, half up tiles) and K
-// steps in flight per wave.  Both GEMMs stream 4 tiles per wave (one wave
-// per SIMD; the blockwise mode keeps 2, its per-step scales would not fit
-// the registers): Qwen3-235B decode step 165.9 -> 163.8 us with 4 gate/up
-// tiles instead of 2, then 162.9 -> 161.8 us with 4 down tiles.  One tile
+// steps in flight per wave.  In the PTPC mode both GEMMs stream 4 tiles per
+// wave (one wave per SIMD): Qwen3-235B decode step 165.9 -> 163.8 us with 4
+// gate/up tiles instead of 2, then 162.9 -> 161.8 us with 4 down tiles.  The
+// blockwise mode keeps 2 (its per-step scales would not fit the registers),
+// and so does bf16 (4 tiles halve its waves; the 64-token bf16 layer went
+// from 0.028 to 0.032 ms).  One tile
 // per wave for down spread its items more evenly over the waves but halved
 // the bytes each wave keeps in flight, and measured slower (178 -> 196 us);
 // so did splitting only the items of the last, partial round (177 ->
@@ -318,7 +320,7 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
 // get more of it.  3 or 6 steps in flight instead of 4 were slower (167.4,
 // 167.3 against 165.9 us).
 template <int MODE, bool GATEUP>
-constexpr int stream_tn() { return MODE != MOE_QUANT_BLOCK128_FP8 ? 4 : 2; }
+constexpr int stream_tn() { return MODE == MOE_QUANT_PTPC_FP8 ? 4 : 2; }
 constexpr int kStreamPF = 4;
 
 // Workgroups of a kernel that fit on the device at once, per device (CACHE:
