@@ -47,6 +47,38 @@ __device__ __forceinline__ void scale_pair(float amax, float& scale, float& inv)
     else { scale = amax / 448.0f; inv = 448.0f / amax; }
 }
 
+// Codes of the vectors c = c0 + lane + 64 i (i < 8, c < nvec) of one row,
+// 8 elements each: GROUP 0 with the row's inverse scale; GROUP 128 forms each
+// 1x128 group's scale from the 16 lanes that hold the group.
+template <int GROUP>
+__device__ __forceinline__ void quant_vecs(const bf16x8 (&v)[8], int c0, int nvec, float inv, uint2* __restrict__ qv,
+                                           float* __restrict__ sr, int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = c0 + lane + 64 * i;
+        if constexpr (GROUP == 0) {
+            if (c < nvec) qv[c] = quant8(v[i], inv);
+        } else {
+            float m = amax8(v[i]);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            float sc, gi;
+            scale_pair(m, sc, gi);
+            if (c < nvec) {
+                qv[c] = quant8(v[i], gi);
+                if ((lane & 15) == 0) sr[c >> 4] = sc;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float amax_vecs(const bf16x8 (&v)[8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, amax8(v[i]));
+    return m;
+}
+
 // One row of x into codes with the wave, in chunks of 4096 elements (8
 // vectors of 8 per lane, all loads of a chunk in flight together).  GROUP 0
 // (one scale per row): amax over the chunks, then codes (a single-chunk row
@@ -72,39 +104,38 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ xr, 
         float m = 0.0f;
         for (int ch = 0; ch < nch; ++ch) {
             load(ch);
-#pragma unroll
-            for (int i = 0; i < CV; ++i) m = fmaxf(m, amax8(v[i]));
+            m = fmaxf(m, amax_vecs(v));
         }
         m = wave_max(m);
         float sc, inv;
         scale_pair(m, sc, inv);
         for (int ch = 0; ch < nch; ++ch) {
             if (nch > 1) load(ch);
-#pragma unroll
-            for (int i = 0; i < CV; ++i) {
-                const int c = ch * 64 * CV + lane + 64 * i;
-                if (c < nvec) qv[c] = quant8(v[i], inv);
-            }
+            quant_vecs<0>(v, ch * 64 * CV, nvec, inv, qv, sr, lane);
         }
         if (lane == 0) sr[0] = sc;
     } else {
         for (int ch = 0; ch < nch; ++ch) {
             load(ch);
-#pragma unroll
-            for (int i = 0; i < CV; ++i) {
-                const int c = ch * 64 * CV + lane + 64 * i;
-                float m = amax8(v[i]);
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-                float sc, inv;
-                scale_pair(m, sc, inv);
-                if (c < nvec) {
-                    qv[c] = quant8(v[i], inv);
-                    if ((lane & 15) == 0) sr[c >> 4] = sc;
-                }
-            }
+            quant_vecs<128>(v, ch * 64 * CV, nvec, 0.0f, qv, sr, lane);
         }
     }
+}
+
+// A row of at most 4096 elements already in registers (v[i] = vector
+// lane + 64 i of the row, zero past its end): the same codes and scales as
+// quant_row_wave.
+template <int GROUP>
+__device__ __forceinline__ void quant_row_regs(const bf16x8 (&v)[8], int K, uint8_t* __restrict__ qr,
+                                               float* __restrict__ sr, int lane) {
+    uint2* qv = reinterpret_cast<uint2*>(qr);
+    float inv = 0.0f;
+    if constexpr (GROUP == 0) {
+        float sc;
+        scale_pair(wave_max(amax_vecs(v)), sc, inv);
+        if (lane == 0) sr[0] = sc;
+    }
+    quant_vecs<GROUP>(v, 0, K >> 3, inv, qv, sr, lane);
 }
 
 // value of an E2M1 code: exponent field 0 is 0 or 0.5, else (1 + m/2) * 2^(e-1)

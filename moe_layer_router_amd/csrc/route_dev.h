@@ -183,4 +183,182 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lr, int E,
 }
 
 
+// ----------------------------------------------------------------------------
+// Four tokens per wave: the token of a 16-lane row (a DPP row) is routed by
+// that row alone, so one instruction stream selects for four tokens.  Lane
+// sub = lane % 16 of the row holds experts e = sub + 16 i, i < EPL
+// (E <= 16 EPL).  The selection is the same as route_token's: `beats` is a
+// total order, so the reduction tree does not change the picks.
+// ----------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ int row_dpp(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float row_dpp_f(float x) {
+    return __builtin_bit_cast(float, row_dpp<CTRL>(__builtin_bit_cast(int, x)));
+}
+
+// One combining step: the partner lane's (value, index, payload) when it
+// beats ours.  Every source of the controls below is inside the row.
+template <int CTRL>
+__device__ __forceinline__ void row_best_step(float& v, int& i, float& s) {
+    const float ov = row_dpp_f<CTRL>(v), os = row_dpp_f<CTRL>(s);
+    const int oi = row_dpp<CTRL>(i);
+    if (beats(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+        s = os;
+    }
+}
+
+// Best (value, index) of the row, with the payload s of the lane that held
+// it, in every lane of the row.  Rotations by 8 and 4 and the quad
+// permutations xor 2 and xor 1 combine disjoint lane sets at each step, so
+// each lane ends with the best of all 16.
+__device__ __forceinline__ void row_argbest(float& v, int& i, float& s) {
+    row_best_step<0x128>(v, i, s);   // row_ror:8
+    row_best_step<0x124>(v, i, s);   // row_ror:4
+    row_best_step<0x4E>(v, i, s);    // quad_perm [2, 3, 0, 1]
+    row_best_step<0xB1>(v, i, s);    // quad_perm [1, 0, 3, 2]
+}
+
+// Largest two values of the row (the same disjoint combining steps).
+template <int CTRL>
+__device__ __forceinline__ void row_top2_step(float& m1, float& m2) {
+    const float a1 = row_dpp_f<CTRL>(m1), a2 = row_dpp_f<CTRL>(m2);
+    const float n1 = fmaxf(m1, a1);
+    const float n2 = fmaxf(fminf(m1, a1), fmaxf(m2, a2));
+    m1 = n1;
+    m2 = n2;
+}
+__device__ __forceinline__ void row_top2(float& m1, float& m2) {
+    row_top2_step<0x128>(m1, m2);
+    row_top2_step<0x124>(m1, m2);
+    row_top2_step<0x4E>(m1, m2);
+    row_top2_step<0xB1>(m1, m2);
+}
+
+// value of lane j of this lane's row
+__device__ __forceinline__ float row_lane_f(float v, int lane, int j) { return __shfl(v, (lane & ~15) + j, 64); }
+__device__ __forceinline__ double row_lane_d(double v, int lane, int j) { return __shfl(v, (lane & ~15) + j, 64); }
+
+// Routes the token of this lane's row (its E logits at lr).  Lane j < k of
+// the row ends with the j-th pick's expert in *id and its weight in *wt.
+// Grouped scoring needs n_groups <= 16 (lane g of the row keeps group g's
+// score).  Every lane of the wave must call it (the steps are cross-lane).
+template <int EPL, int SCORING>
+__device__ __forceinline__ void route_token_row(const float* __restrict__ lr, int E, int k, int n_groups,
+                                                int topk_groups, const float* __restrict__ sel_bias,
+                                                int renormalize, float route_scale, int lane, int* id, float* wt) {
+    const float NEG = -__builtin_inff();
+    const int sub = lane & 15;
+
+    float key[EPL];     // selection keys (-inf: absent or taken)
+    float sc[EPL];      // softmax: logit; sigmoid: unbiased score s
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = sub + 16 * i;
+        const float l = e < E ? lr[e] : 0.0f;
+        if (SCORING == 0) {
+            sc[i] = l;
+            key[i] = e < E ? l : NEG;
+        } else {
+            // sigmoid in fp64, rounded once to fp32
+            const float s = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
+            sc[i] = s;
+            const float b = sel_bias ? (e < E ? sel_bias[e] : 0.0f) : 0.0f;
+            key[i] = e < E ? s + b : NEG;
+        }
+    }
+
+    if (SCORING == 1) {
+        // group score = sum of the two largest keys of each group; keep the
+        // topk_groups best groups (ties to the lower group index)
+        const int gsz = E / n_groups;
+        float mine = NEG;                    // lane g of the row keeps group g's score
+        for (int g = 0; g < n_groups; ++g) {
+            float m1 = NEG, m2 = NEG;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = sub + 16 * i;
+                if (e < E && e / gsz == g) {
+                    const float v = key[i];
+                    if (v > m1) { m2 = m1; m1 = v; } else if (v > m2) { m2 = v; }
+                }
+            }
+            row_top2(m1, m2);
+            if (sub == g) mine = gsz >= 2 ? m1 + m2 : m1;
+        }
+        int r = 0;
+        for (int h = 0; h < n_groups; ++h) {
+            const float other = row_lane_f(mine, lane, h);
+            r += (h != sub) && beats(other, h, mine, sub);
+        }
+        const uint32_t keep =
+            static_cast<uint32_t>(__ballot(sub < n_groups && r < topk_groups) >> (lane & ~15)) & 0xFFFFu;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = sub + 16 * i;
+            if (e < E && !((keep >> (e / gsz)) & 1u)) key[i] = NEG;
+        }
+    }
+
+    // k rounds of arg-best; every lane of the row learns the pick and its
+    // score, and the owner removes it
+    float selv = 0.0f;   // lane j (< k) of the row keeps the j-th pick's score
+    int seli = 0;
+    float vfirst = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bv = NEG, bs = 0.0f;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = sub + 16 * i;
+            if (key[i] != NEG && beats(key[i], e, bv, bi)) { bv = key[i]; bi = e; bs = sc[i]; }
+        }
+        row_argbest(bv, bi, bs);
+        if ((bi & 15) == sub) {
+            const int i = bi >> 4;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q)
+                if (q == i) key[q] = NEG;
+        }
+        if (j == 0) vfirst = bs;
+        if (sub == j) { selv = bs; seli = bi; }
+    }
+
+    // weights in fp64, one rounding to fp32
+    double wj = 0.0, den = 0.0;
+    if (SCORING == 0) {
+        const double lmax = static_cast<double>(vfirst);
+        wj = sub < k ? exp(static_cast<double>(selv) - lmax) : 0.0;
+        if (renormalize) {
+            for (int j = 0; j < k; ++j) den += row_lane_d(wj, lane, j);
+        } else {
+            double part = 0.0;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = sub + 16 * i;
+                if (e < E) part += exp(static_cast<double>(sc[i]) - lmax);
+            }
+            // fixed-order tree over the row
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+            den = part;
+        }
+        wj = wj / den;
+    } else {
+        wj = sub < k ? static_cast<double>(selv) : 0.0;
+        if (renormalize) {
+            for (int j = 0; j < k; ++j) den += row_lane_d(wj, lane, j);
+            wj = wj / den;
+        }
+        wj *= static_cast<double>(route_scale);
+    }
+    *id = seli;
+    *wt = static_cast<float>(wj);
+}
+
 }  // namespace moe

@@ -14,10 +14,11 @@
 //      the logits carry nothing but fp32 accumulation rounding.  The weight
 //      rows are the first operand, so lane (token l % 32) ends with 16
 //      experts of its token per 32-expert tile.
-//   2. The tile's logits go to LDS (and to the logits buffer); each wave then
-//      routes 8 of the tokens with the wave-per-token top-k (route_token).
-//   3. The same tokens' x rows are quantized to FP8 (one scale per row or
-//      per 128 elements), the rows being fresh in L2.
+//   2. The tile's logits go to LDS (and to the logits buffer).  The same
+//      tokens' x rows are quantized to FP8 (one scale per row or per 128
+//      elements; a wave loads two rows of up to 4096 elements at a time).
+//   3. Each wave routes 4 of the tokens, one per 16-lane row
+//      (route_token_row), while the code stores drain.
 // Used by moe_forward for batches above the decode sizes when it is given
 // no logits (large batches spread over T / 32 workgroups), and by
 // moe_router_front.
@@ -111,8 +112,8 @@ __global__ void __launch_bounds__(256) router_prep_kernel(const float* __restric
 // two K steps (128 elements) at a time: the four waves of the half load the
 // 32 rows x 256 bytes with 16 lanes per row (whole lines), the next chunk's
 // loads in flight while the current chunk multiplies.  The prepared weight
-// pieces go straight to registers, the next (step, tile) unit loading while
-// the current one multiplies (a two-deep ring at constant indices).
+// pieces go straight to registers, one or two (step, tile) units loading while
+// the current one multiplies (a ring at constant indices).
 template <int EPT, int EPL, int SCORING, int GROUP>
 __global__ void __launch_bounds__(512) router_front_kernel(const RouterArgs p) {
     constexpr int LD = EPT * 128 + 1;                       // logits row stride (floats)
@@ -174,7 +175,10 @@ __global__ void __launch_bounds__(512) router_front_kernel(const RouterArgs p) {
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[j] = v16f_r{};
 
-    u32x4_r xa[2][4], wa[2][12];
+    // weight ring slots: three (two units ahead) with one expert tile per
+    // wave, two where more tiles' sums leave too few registers for a third
+    constexpr int NSLOT = EPT >= 2 ? 2 : 3;
+    u32x4_r xa[2][4], wa[NSLOT][12];
     auto wload = [&](auto B, int s, int j) {
         constexpr int b = decltype(B)::value;
 #pragma unroll
@@ -195,14 +199,21 @@ __global__ void __launch_bounds__(512) router_front_kernel(const RouterArgs p) {
         }
     };
 
-    using B0 = std::integral_constant<int, 0>;
-    xload(0);
-    xstore(0);
-    wload(B0{}, s_beg, 0);
-    __syncthreads();
-    for (int ch = 0; ch < nchunks; ++ch) {
+    // Weight units (K step, expert tile) in order: unit 2 EPT ch + u is step
+    // s_beg + 2 ch + u / EPT, tile u % EPT.  The ring keeps NSLOT - 1 units
+    // in flight ahead of the one being multiplied (unit U in slot U % NSLOT);
+    // chunks are unrolled by UNR so that every slot index is a constant.
+    // Inside a chunk every load is unconditional (a unit past the end reloads
+    // the last one, unused) so that the compiler's waits count exactly the
+    // loads issued after the one awaited; a conditional load would make it
+    // wait for all of them.  Each half has at least one chunk.
+    constexpr int AHEAD = NSLOT - 1;
+    constexpr int UNR = (2 * EPT) % NSLOT == 0 ? 1 : NSLOT;
+    const int s_end = s_beg + 2 * nchunks;
+    auto chunk = [&](auto CC, int ch) __attribute__((always_inline)) {
+        constexpr int cc = decltype(CC)::value;             // ch % UNR
         const int buf = ch & 1, s = s_beg + 2 * ch;
-        if (ch + 1 < nchunks) xload(ch + 1);                 // in flight during this chunk
+        xload(min(ch + 1, nchunks - 1));                    // in flight during this chunk
         // this chunk's x fragments of both steps
         const uint8_t* xs = s_raw + half * 2 * XBUF + buf * XBUF + r * XROW + kh * 64;
 #pragma unroll
@@ -211,16 +222,34 @@ __global__ void __launch_bounds__(512) router_front_kernel(const RouterArgs p) {
             for (int c = 0; c < 4; ++c) xa[ds][c] = *reinterpret_cast<const u32x4_r*>(xs + ds * 128 + c * 16);
         static_for<2 * EPT>([&](auto U) {
             constexpr int u = decltype(U)::value;
-            constexpr int j = u % EPT, nj = (u + 1) % EPT, nds = (u + 1) / EPT;
-            using Cur = std::integral_constant<int, u & 1>;
-            using Nxt = std::integral_constant<int, (u + 1) & 1>;
+            constexpr int ul = 2 * EPT * cc + u;                // unit within the unrolled chunks
+            constexpr int j = u % EPT;
+            // unit + AHEAD: dch chunks on, position u2 there
+            constexpr int dch = (u + AHEAD) / (2 * EPT), u2 = (u + AHEAD) % (2 * EPT);
+            using Cur = std::integral_constant<int, ul % NSLOT>;
+            using Nxt = std::integral_constant<int, (ul + AHEAD) % NSLOT>;
             using DS = std::integral_constant<int, u / EPT>;
-            if (s + nds < s_beg + 2 * nchunks) wload(Nxt{}, s + nds, nj);
+            wload(Nxt{}, min(s + 2 * dch + u2 / EPT, s_end - 1), u2 % EPT);
             if (tile_on[j]) compute(Cur{}, DS{}, j);
         });
-        if (ch + 1 < nchunks) xstore(buf ^ 1);
+        // the last chunk stores its reloaded x into the idle buffer (read by
+        // no one; the barrier orders it before the buffers' reuse below)
+        xstore(buf ^ 1);
         __syncthreads();
-    }
+    };
+    xload(0);
+    xstore(0);
+    static_for<AHEAD>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        wload(std::integral_constant<int, u>{}, s_beg + u / EPT, u % EPT);
+    });
+    __syncthreads();
+    const int nfull = nchunks - nchunks % UNR;
+    for (int ch0 = 0; ch0 < nfull; ch0 += UNR)
+        static_for<UNR>([&](auto CC) { chunk(CC, ch0 + decltype(CC)::value); });
+    static_for<UNR>([&](auto CC) {
+        if (nfull + decltype(CC)::value < nchunks) chunk(CC, nfull + decltype(CC)::value);
+    });
 
     // second half -> LDS; first half adds it (fixed order) and owns the tile
     if (half) {
@@ -254,26 +283,76 @@ __global__ void __launch_bounds__(512) router_front_kernel(const RouterArgs p) {
     }
     __syncthreads();
 
-    // top-k of each token, one wave per token, from the logits in LDS
-    for (int tt = wave; tt < kRouterTokens; tt += 8) {
-        const int t = t0 + tt;
-        if (t >= p.T) break;
-        int id;
-        float wt;
-        route_token<EPL, SCORING>(&s_lg[tt][0], p.E, p.k, p.n_groups, p.topk_groups, p.sel_bias, p.renormalize,
-                                  p.route_scale, lane, &id, &wt);
-        if (lane < p.k) {
-            p.ids[static_cast<int64_t>(t) * p.k + lane] = id;
-            p.w[static_cast<int64_t>(t) * p.k + lane] = wt;
+    // The tail: the 32 tokens' x rows in the layer's activation format, then
+    // their top-k.  Wave w quantizes rows w, w + 8, w + 16, w + 24; rows of
+    // at most 4096 elements (one scale per row or per 128) are loaded two at
+    // a time, so the wave waits for two round trips, not four, and the code
+    // stores drain while the routing runs.
+    if constexpr (GROUP == 0 || GROUP == 128) {
+        if (p.D <= 4096) {
+            constexpr int XR = 2;   // rows in flight together (four spill registers)
+            const int nvec = p.D >> 3;
+#pragma unroll
+            for (int q0 = 0; q0 < 4; q0 += XR) {
+                bf16x8 xv[XR][8];
+#pragma unroll
+                for (int q = 0; q < XR; ++q) {
+                    const int t = min(t0 + wave + 8 * (q0 + q), p.T - 1);
+                    const bf16x8* xr = reinterpret_cast<const bf16x8*>(p.x + static_cast<int64_t>(t) * p.D);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int c = lane + 64 * i;
+                        xv[q][i] = c < nvec ? ld_once(xr + c) : bf16x8{};
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < XR; ++q) {
+                    const int64_t t = t0 + wave + 8 * (q0 + q);
+                    if (t < p.T)
+                        quant_row_regs<GROUP>(xv[q], p.D, p.xq + t * p.D,
+                                              static_cast<float*>(p.xs) + t * (GROUP == 128 ? p.D / 128 : 1), lane);
+                }
+            }
+        } else {
+            for (int tt = wave; tt < kRouterTokens; tt += 8) {
+                const int t = t0 + tt;
+                if (t >= p.T) break;
+                quant_x_row<GROUP>(p.x, p.D, t, p.xq, p.xs, lane);
+            }
         }
-    }
-
-    // the same tokens' x rows in the layer's activation format
-    if constexpr (GROUP >= 0) {
+    } else if constexpr (GROUP >= 0) {
         for (int tt = wave; tt < kRouterTokens; tt += 8) {
             const int t = t0 + tt;
             if (t >= p.T) break;
             quant_x_row<GROUP>(p.x, p.D, t, p.xq, p.xs, lane);
+        }
+    }
+
+    // top-k from the logits in LDS: four tokens per wave, a 16-lane row
+    // each; grouped scoring with more than 16 groups routes one token per
+    // wave
+    if (SCORING == 0 || p.n_groups <= 16) {
+        const int tt = 4 * wave + (lane >> 4), t = t0 + tt, j = lane & 15;
+        int id;
+        float wt;
+        route_token_row<4 * EPL, SCORING>(&s_lg[tt][0], p.E, p.k, p.n_groups, p.topk_groups, p.sel_bias,
+                                          p.renormalize, p.route_scale, lane, &id, &wt);
+        if (t < p.T && j < p.k) {
+            p.ids[static_cast<int64_t>(t) * p.k + j] = id;
+            p.w[static_cast<int64_t>(t) * p.k + j] = wt;
+        }
+    } else {
+        for (int tt = wave; tt < kRouterTokens; tt += 8) {
+            const int t = t0 + tt;
+            if (t >= p.T) break;
+            int id;
+            float wt;
+            route_token<EPL, SCORING>(&s_lg[tt][0], p.E, p.k, p.n_groups, p.topk_groups, p.sel_bias,
+                                      p.renormalize, p.route_scale, lane, &id, &wt);
+            if (lane < p.k) {
+                p.ids[static_cast<int64_t>(t) * p.k + lane] = id;
+                p.w[static_cast<int64_t>(t) * p.k + lane] = wt;
+            }
         }
     }
 }
