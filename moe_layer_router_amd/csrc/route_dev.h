@@ -7,8 +7,10 @@
 namespace moe {
 
 // (value, index) order: a ranks before b when larger, ties to the lower index.
+// Non-short-circuit operators and the selects below keep the selection
+// code branch-free (one compare chain and v_cndmask per candidate).
 __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+    return (va > vb) | ((va == vb) & (ia < ib));
 }
 
 // One step of a DPP reduction: take (value, index) from the lane the DPP
@@ -19,10 +21,9 @@ __device__ __forceinline__ void dpp_best_step(float& v, int& i) {
         float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
                                            false));
     const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xF, false);
-    if (beats(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-    }
+    const bool take = beats(ov, oi, v, i);
+    v = take ? ov : v;
+    i = take ? oi : i;
 }
 
 // Arg-best of the wave, returned wave-uniform: DPP row shifts by 1, 2, 4, 8
@@ -134,7 +135,9 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lr, int E,
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int e = lane + 64 * i;
-            if (key[i] != NEG && beats(key[i], e, bv, bi)) { bv = key[i]; bi = e; }
+            const bool take = (key[i] != NEG) & beats(key[i], e, bv, bi);
+            bv = take ? key[i] : bv;
+            bi = take ? e : bi;
         }
         wave_argbest(bv, bi);
         // owner fetches the pick's score and removes it
@@ -206,11 +209,10 @@ template <int CTRL>
 __device__ __forceinline__ void row_best_step(float& v, int& i, float& s) {
     const float ov = row_dpp_f<CTRL>(v), os = row_dpp_f<CTRL>(s);
     const int oi = row_dpp<CTRL>(i);
-    if (beats(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-        s = os;
-    }
+    const bool take = beats(ov, oi, v, i);
+    v = take ? ov : v;
+    i = take ? oi : i;
+    s = take ? os : s;
 }
 
 // Best (value, index) of the row, with the payload s of the lane that held
@@ -316,15 +318,15 @@ __device__ __forceinline__ void route_token_row(const float* __restrict__ lr, in
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int e = sub + 16 * i;
-            if (key[i] != NEG && beats(key[i], e, bv, bi)) { bv = key[i]; bi = e; bs = sc[i]; }
+            const bool take = (key[i] != NEG) & beats(key[i], e, bv, bi);
+            bv = take ? key[i] : bv;
+            bi = take ? e : bi;
+            bs = take ? sc[i] : bs;
         }
         row_argbest(bv, bi, bs);
-        if ((bi & 15) == sub) {
-            const int i = bi >> 4;
+        const int own = (bi & 15) == sub ? bi >> 4 : -1;
 #pragma unroll
-            for (int q = 0; q < EPL; ++q)
-                if (q == i) key[q] = NEG;
-        }
+        for (int q = 0; q < EPL; ++q) key[q] = q == own ? NEG : key[q];
         if (j == 0) vfirst = bs;
         if (sub == j) { selv = bs; seli = bi; }
     }
