@@ -263,6 +263,7 @@ def test_quant_weights(quant, layout):
                                           ("qwen3_30b_a3b_ptpc_i384", 64), ("qwen3_30b_a3b_ptpc_i384", 256),
                                           ("deepseek_r1_block_fp8_r", 32), ("deepseek_r1_block_fp8_r", 64),
                                           ("deepseek_r1_block_fp8_r", 128), ("deepseek_r1_block_fp8_r", 256),
+                                          ("deepseek_r1_block_fp8_r", 192),
                                           ("tiny_bf16", 16), ("bf16_small_t20", 16), ("qwen3_235b_decode_ptpc", 16),
                                           ("qwen3_30b_a3b_ptpc", 16), ("qwen3_235b_prefill_ptpc_r", 16),
                                           ("deepseek_r1_block_fp8_r", 16), ("bf16_multi_tile_r", 16),
@@ -304,7 +305,7 @@ def test_gateup_silu_entry(name, block_m):
                                           ("qwen3_30b_a3b_ptpc_i384", 128), ("qwen3_30b_a3b_ptpc_i384", 256),
                                           ("qwen3_30b_a3b_ptpc", 64), ("deepseek_r1_block_fp8_r", 32),
                                           ("deepseek_r1_block_fp8_r", 64), ("deepseek_r1_block_fp8_r", 128),
-                                          ("deepseek_r1_block_fp8_r", 256),
+                                          ("deepseek_r1_block_fp8_r", 256), ("deepseek_r1_block_fp8_r", 192),
                                           ("tiny_bf16", 16), ("qwen3_235b_decode_ptpc", 16),
                                           ("qwen3_235b_decode_ptpc_t64", 16), ("deepseek_r1_block_fp8_small", 16),
                                           ("qwen3_30b_a3b_ptpc", 16), ("qwen3_235b_prefill_ptpc_r", 16)])
@@ -354,6 +355,7 @@ def test_down_entry(name, block_m):
 
 @pytest.mark.parametrize("name,block_m", [("qwen3_235b_prefill_ptpc_r", 256), ("qwen3_235b_prefill_ptpc_r", 128),
                                           ("deepseek_r1_block_fp8_r", 256), ("bf16_multi_tile_r", 256),
+                                          ("deepseek_r1_block_fp8_r", 192),
                                           ("qwen3_30b_a3b_ptpc", 64), ("qwen3_30b_a3b_ptpc", 16),
                                           ("qwen3_235b_prefill_ptpc_r", 16)])
 def test_gemm_counts_skip_pad_tiles(name, block_m):
