@@ -216,8 +216,9 @@ def weight_copies(mlr, layer):
 def time_decode(torch, mlr, synth, steps, warmup):
     """Decode layer (T=32, Zipf-skewed routing): full forward, weights rotated
     over copies so each step streams its experts from HBM.  Timed per call
-    (median, p10, p90), eagerly and replayed from captured HIP graphs (one
-    graph per weight copy; the replayed output must equal the eager one)."""
+    (median, p10, p90), eagerly and replayed from a captured HIP graph of the
+    forwards over every weight copy (per-forward figures; the replayed output
+    must equal the eager one)."""
     w = synth.get("qwen3_235b_decode_ptpc")
     c = Case(mlr, synth, w, keep_masters=False)
     ncopy = 4
@@ -237,21 +238,24 @@ def time_decode(torch, mlr, synth, steps, warmup):
     out = dict(workload=w.name, calls=steps, us_per_step=round(med, 2), p10_us=round(p10, 2), p90_us=round(p90, 2),
                active_experts=int(used), expert_weight_bytes=int(nbytes),
                GBps=round(nbytes / (med * 1e-6) / 1e9, 1), hbm_frac=round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
-    graphs = []
-    for i in range(ncopy):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+    # One graph holds the forwards over the ncopy weight copies in turn (as a
+    # decode step of a model holds its layers): a replay launches ncopy
+    # forwards, so the host's per-launch cost of a graph, larger on this
+    # runtime than one forward's GPU time, is paid once per ncopy forwards.
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(ncopy):
             layers[i].forward(c.x, c.logits, y=y, workspace=ws)
-        graphs.append(g)
     torch.cuda.synchronize()
-    gmed, gp10, gp90 = timed_calls(torch, lambda i: graphs[i % ncopy].replay(), steps, warmup)
+    gsteps = max(1, steps // ncopy)
+    gmed, gp10, gp90 = (v / ncopy for v in timed_calls(torch, lambda i: g.replay(), gsteps, max(1, warmup // ncopy)))
     same = bool(torch.equal(y, y_eager))
     out.update(graph_us_per_step=round(gmed, 2), graph_p10_us=round(gp10, 2), graph_p90_us=round(gp90, 2),
                graph_GBps=round(nbytes / (gmed * 1e-6) / 1e9, 1),
                graph_hbm_frac=round(nbytes / (gmed * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), graph_output_equal=same)
     if not same:
         raise SystemExit("graph replay of the decode forward differs from the eager forward")
-    del graphs, layers, c
+    del g, layers, c
     torch.cuda.empty_cache()
     return out
 
