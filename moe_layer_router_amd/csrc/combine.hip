@@ -86,8 +86,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ o
 template <bool OUT_BF16>
 static void combine_dispatch(dim3 grid, hipStream_t s, const void* out_perm, const int* inv_perm, const float* topk_w,
                              int T, int k, int n_shared, int D, uint16_t* y) {
+    // the rows a token gathers set the registers (all its loads are in
+    // flight at once) and so the waves per SIMD: 9 rows take 82 VGPRs (5
+    // waves), 12 rows (top-10 + shared) 106 (4), 17 rows 146 (3)
     if (k + n_shared <= 9)
         hipLaunchKernelGGL((combine_kernel<OUT_BF16, 9>), grid, dim3(256), 0, s, out_perm, inv_perm, topk_w, T, k,
+                           n_shared, D, y);
+    else if (k + n_shared <= 12)
+        hipLaunchKernelGGL((combine_kernel<OUT_BF16, 12>), grid, dim3(256), 0, s, out_perm, inv_perm, topk_w, T, k,
                            n_shared, D, y);
     else
         hipLaunchKernelGGL((combine_kernel<OUT_BF16, MOE_MAX_TOPK + 1>), grid, dim3(256), 0, s, out_perm, inv_perm,

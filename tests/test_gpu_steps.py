@@ -394,7 +394,9 @@ def test_gemm_counts_skip_pad_tiles(name, block_m):
     assert bool((o1[:total][zp1] == 0).all()) and bool((o0[:total][zp0] == 0).all())
 
 
-@pytest.mark.parametrize("T,k,ns,D,dt", [(64, 2, 0, 256, 0), (300, 8, 1, 1024, 1), (17, 8, 0, 7168, 1)])
+@pytest.mark.parametrize("T,k,ns,D,dt", [(64, 2, 0, 256, 0), (300, 8, 1, 1024, 1), (17, 8, 0, 7168, 1),
+                                         (129, 10, 1, 512, 1), (70, 11, 1, 2048, 1), (40, 12, 1, 512, 1),
+                                         (33, 10, 1, 256, 0)])
 def test_combine_entry(T, k, ns, D, dt):
     say("combine", T, k, ns, D, dt)
     E = 16
