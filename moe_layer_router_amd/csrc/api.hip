@@ -26,6 +26,9 @@ int32_t quant_mx_rows_launch(const uint16_t* x, int64_t M, int K, const int* val
 int32_t quant_wblock_launch(const uint16_t* w, int64_t n_mats, int N, int K, bool blocked, uint8_t* q, float* scale,
                             hipStream_t s);
 bool front_small_ok(int T, int k, int n_shared);
+bool permute_small_ok(int T, int k, int n_shared);
+int32_t permute_small_launch(const int* ids, int T, int k, int E, int n_shared, int block_m, int max_rows,
+                             int* counts, int* offsets, int* sorted, int* bexp, int* inv, hipStream_t s);
 int32_t front_route_quant_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int* ids,
                                  float* w, uint8_t* xq, float* xs, hipStream_t s);
 int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int block_m,
@@ -475,8 +478,9 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
             return st;
     } else {
         // routing and x quantization in one launch (with the router
-        // projection when there are no logits), then the multi-kernel
-        // permutation
+        // projection when there are no logits), then the permutation: one
+        // workgroup up to 256 tokens (the routing's picks are distinct per
+        // token), else the multi-kernel one
         uint8_t* xq = fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr;
         float* xs = fp8 ? static_cast<float*>(at(o.xs)) : nullptr;
         if (fused_router) {
@@ -485,10 +489,13 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
         } else if ((st = front_route_quant_launch(L, x_bf16, logits, T, ids, w, xq, xs, s)) != MOE_OK) {
             return st;
         }
-        if ((st = permute_align_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
-                                       static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, at(o.scratch),
-                                       s)) != MOE_OK)
-            return st;
+        if (permute_small_ok(T, k, L->n_shared))
+            st = permute_small_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
+                                      static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, s);
+        else
+            st = permute_align_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
+                                      static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, at(o.scratch), s);
+        if (st != MOE_OK) return st;
     }
     void* act = at(o.act);
     const int* counts = static_cast<int*>(at(o.counts));

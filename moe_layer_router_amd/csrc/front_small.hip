@@ -12,8 +12,9 @@
 //     spread over T CUs;
 //     (larger batches use it too, followed by the multi-kernel permutation);
 //   permute_small_kernel: one workgroup.  A token's k picks are distinct
-//     experts and T <= 64, so every expert's rows are a 64-bit mask of
-//     tokens (LDS atomicOr); a row's rank in its expert's segment is the
+//     experts and T <= 64 (256 when it runs on its own after the routing of
+//     a larger batch), so every expert's rows are a mask of tokens, 32 per
+//     word (LDS atomicOr); a row's rank in its expert's segment is the
 //     number of mask bits below its token -- the stable ascending order of
 //     flat indices the multi-kernel permutation produces (shared-expert
 //     rows: token order).  Counts, padded offsets, sorted ids, inverse map,
@@ -26,6 +27,9 @@ namespace moe {
 constexpr int kFrontWaves = 16;
 constexpr int kFrontMaxT = 64;
 constexpr int kFrontMaxRows = kFrontMaxT * (MOE_MAX_TOPK + 1);
+// the one-workgroup permutation also serves batches up to this many tokens
+// (routed by the other launches) in place of the three-launch one
+constexpr int kPermSmallMaxT = 256;
 
 struct FrontArgs {
     const float* logits;
@@ -65,35 +69,38 @@ __global__ void __launch_bounds__(128) token_front_kernel(const FrontArgs p) {
     }
 }
 
+// MW: 32-token words of each expert's token mask (T <= 32 MW).
+template <int MW>
 __global__ void __launch_bounds__(kFrontWaves * 64) permute_small_kernel(const FrontArgs p) {
-    __shared__ int s_e[kFrontMaxRows];           // expert of each routed row (-1: no row)
-    __shared__ uint32_t s_mlo[MOE_MAX_EXPERTS];  // tokens 0..31 routed to the expert
-    __shared__ uint32_t s_mhi[MOE_MAX_EXPERTS];  // tokens 32..63
-    __shared__ int s_off[MOE_MAX_EXPERTS + 1];   // padded offsets
+    __shared__ int s_e[32 * MW * (MOE_MAX_TOPK + 1)];   // expert of each routed row (-1: no row)
+    __shared__ uint32_t s_m[MW][MOE_MAX_EXPERTS];      // word w: tokens 32w .. 32w+31 routed to the expert
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];         // padded offsets
     __shared__ int s_wave[kFrontWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int NT = kFrontWaves * 64;
     const int E = p.E, Ep = E + p.n_shared, k = p.k, B = p.block_m, T = p.T;
     const int TK = T * k, A = T * (k + p.n_shared);
 
-    for (int e = tid; e < Ep; e += NT) {
-        s_mlo[e] = 0;
-        s_mhi[e] = 0;
-    }
+    for (int e = tid; e < Ep; e += NT)
+#pragma unroll
+        for (int w = 0; w < MW; ++w) s_m[w][e] = 0;
     __syncthreads();
     for (int f = tid; f < TK; f += NT) {
         const int id = p.ids[f], t = f / k;
         const int e = (id >= 0 && id < E) ? id : -1;             // no valid pick: no row
         s_e[f] = e;
-        if (e >= 0) {
-            if (t < 32) atomicOr(&s_mlo[e], 1u << t);
-            else atomicOr(&s_mhi[e], 1u << (t - 32));
-        }
+        if (e >= 0) atomicOr(&s_m[t >> 5][e], 1u << (t & 31));
     }
     __syncthreads();
+    auto popc_all = [&](int e) {
+        int n = 0;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) n += __popc(s_m[w][e]);
+        return n;
+    };
 
     // counts and padded offsets (one expert per thread, Ep <= 1024)
-    const int c = tid < E ? __popc(s_mlo[tid]) + __popc(s_mhi[tid]) : (tid < Ep ? T : 0);
+    const int c = tid < E ? popc_all(tid) : (tid < Ep ? T : 0);
     const int padded = (c + B - 1) / B * B;
     int inc = wave_incl_scan_i(padded, lane);
     if (lane == 63) s_wave[wave] = inc;
@@ -125,8 +132,10 @@ __global__ void __launch_bounds__(kFrontWaves * 64) permute_small_kernel(const F
                 p.inv[f] = -1;
                 continue;
             }
-            const int below = t < 32 ? __popc(s_mlo[e] & ((1u << t) - 1u))
-                                      : __popc(s_mlo[e]) + __popc(s_mhi[e] & ((1u << (t - 32)) - 1u));
+            int below = __popc(s_m[t >> 5][e] & ((1u << (t & 31)) - 1u));
+#pragma unroll
+            for (int w = 0; w < MW; ++w)
+                if (w < (t >> 5)) below += __popc(s_m[w][e]);
             row = s_off[e] + below;
         } else {
             row = s_off[E] + (f - TK);                                  // shared expert: token order
@@ -136,7 +145,7 @@ __global__ void __launch_bounds__(kFrontWaves * 64) permute_small_kernel(const F
     }
     // pads and block map (one wave per expert), tail past the total
     for (int e = wave; e < Ep; e += kFrontWaves) {
-        const int n = e < E ? __popc(s_mlo[e]) + __popc(s_mhi[e]) : T;
+        const int n = e < E ? popc_all(e) : T;
         const int lo = s_off[e], hi = s_off[e + 1];
         for (int r = lo + n + lane; r < hi; r += 64) p.sorted[r] = A;
         for (int b = lo / B + lane; b < hi / B; b += 64) p.bexp[b] = e;
@@ -228,7 +237,33 @@ int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* 
     a.xq = xq;
     a.xs = xs;
     front_tokens(L, a, s);
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kFrontWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(permute_small_kernel<kFrontMaxT / 32>, dim3(1), dim3(kFrontWaves * 64), 0, s, a);
+    return moe_launch_status();
+}
+
+// The one-workgroup permutation alone, for ids routed by another launch with
+// distinct picks per token (moe_forward's own routing) and T <= 256: one
+// launch in place of the three of the general permutation.
+bool permute_small_ok(int T, int k, int n_shared) {
+    return T >= 1 && T <= kPermSmallMaxT && T * (k + n_shared) <= kPermSmallMaxT * (MOE_MAX_TOPK + 1);
+}
+
+int32_t permute_small_launch(const int* ids, int T, int k, int E, int n_shared, int block_m, int max_rows,
+                             int* counts, int* offsets, int* sorted, int* bexp, int* inv, hipStream_t s) {
+    FrontArgs a{};
+    a.ids = const_cast<int*>(ids);
+    a.T = T;
+    a.E = E;
+    a.k = k;
+    a.n_shared = n_shared;
+    a.block_m = block_m;
+    a.max_rows = max_rows;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.sorted = sorted;
+    a.bexp = bexp;
+    a.inv = inv;
+    hipLaunchKernelGGL(permute_small_kernel<kPermSmallMaxT / 32>, dim3(1), dim3(kFrontWaves * 64), 0, s, a);
     return moe_launch_status();
 }
 
