@@ -1,6 +1,7 @@
-// Per-token top-k routing, shared by the routing kernel and the fused
-// small-batch front end: one wave64 owns one token, holds its E scores in
-// registers and selects with cross-lane reductions.
+// Per-token top-k routing: route_token (one wave64 per token; the routing
+// kernel and the front-end launches) and route_token_row (four tokens per
+// wave, one per 16-lane row; the fused router kernel).  The lanes hold the
+// token's E scores in registers and select with cross-lane reductions.
 #pragma once
 #include "common.h"
 

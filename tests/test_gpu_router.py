@@ -48,8 +48,9 @@ def _route_ref(w, lg):
     return O.route_sigmoid_grouped(lg, w.k, w.n_groups, w.topk_groups, None, w.route_scale)
 
 
-def _front(c, T):
+def _front(c, T, desc=None):
     w = c.w
+    desc = c.layer.desc if desc is None else desc
     fp8 = w.quant != "bf16"
     blk = w.quant == "block128_fp8"
     dev = c.x.device
@@ -58,10 +59,10 @@ def _front(c, T):
     wt = torch.empty((T, w.k), dtype=torch.float32, device=dev)
     xq = torch.empty((T, w.D), dtype=torch.uint8, device=dev) if fp8 else None
     xs = torch.empty((T, w.D // 128) if blk else (T,), dtype=torch.float32, device=dev) if fp8 else None
-    nws = int(L.lib().moe_router_front_workspace_size(ctypes.byref(c.layer.desc)))
+    nws = int(L.lib().moe_router_front_workspace_size(ctypes.byref(desc)))
     assert nws > 0
     ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
-    st = L.lib().moe_router_front(ctypes.byref(c.layer.desc), c.x.data_ptr(), T, lg.data_ptr(), ids.data_ptr(),
+    st = L.lib().moe_router_front(ctypes.byref(desc), c.x.data_ptr(), T, lg.data_ptr(), ids.data_ptr(),
                                   wt.data_ptr(), None if xq is None else xq.data_ptr(),
                                   None if xs is None else xs.data_ptr(), ws.data_ptr(), nws,
                                   torch.cuda.current_stream().cuda_stream)
@@ -102,6 +103,33 @@ def test_router_front(name):
         q, s = O.quant_rows(x_np, 128 if w.quant == "block128_fp8" else 0)
         assert np.array_equal(xq.cpu().numpy(), q)
         assert np.array_equal(xs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,renorm,bias", [("prefill_e128", False, False), ("e512", False, False),
+                                               ("r1_e256", False, True), ("r1_e256", True, True)])
+def test_router_front_routing_options(name, renorm, bias):
+    """The other branches of the four-tokens-per-wave routing: soft-max weights
+    over all experts (not renormalized over the picks) and a selection bias in
+    grouped scoring.  ids bit-exact, weights within one fp32 ulp of the oracle
+    routing the GPU's logits."""
+    w = ROUTED[name]
+    say("router front options", name, renorm, bias)
+    c = build_case(w)
+    desc = L.LayerDesc.from_buffer_copy(c.layer.desc)
+    desc.renormalize = int(renorm)
+    b = synth.gen_normal_f32((w.E,), 0.05, 11, "cuda") if bias else None
+    if b is not None:
+        desc.sel_bias = b.data_ptr()
+    lg, ids, wt, _, _ = _front(c, w.T, desc)
+    lg_np = lg.cpu().numpy()
+    if w.scoring == "softmax":
+        rid, rw = O.route_softmax_topk(lg_np, w.k, renormalize=renorm)
+    else:
+        rid, rw = O.route_sigmoid_grouped(lg_np, w.k, w.n_groups, w.topk_groups,
+                                          None if b is None else b.cpu().numpy(), w.route_scale, renormalize=renorm)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    d = np.abs(wt.cpu().numpy().view(np.int32).astype(np.int64) - rw.view(np.int32).astype(np.int64))
+    assert d.max() <= 1
 
 
 def test_router_front_full_size():
