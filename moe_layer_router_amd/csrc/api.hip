@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued (moe_forward
 // checks the limits of all of its kernels before the first launch).
 #include "common.h"
+#include "perm_dev.h"
 
 #include <atomic>
 #include <mutex>
@@ -31,9 +32,9 @@ int32_t permute_small_launch(const int* ids, int T, int k, int E, int n_shared, 
                              int* counts, int* offsets, int* sorted, int* bexp, int* inv, hipStream_t s);
 int32_t front_route_quant_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int* ids,
                                  float* w, uint8_t* xq, float* xs, hipStream_t s);
-int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int block_m,
-                           int max_rows, int* ids, float* w, int* counts, int* offsets, int* sorted, int* bexp,
-                           int* inv, uint8_t* xq, float* xs, hipStream_t s);
+int32_t stream_gateup_fused_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
+                                   const int* ids, int max_rows, const PermOut& pout, void* act, hipStream_t s);
+bool stream_fused_perm_ok(int T);
 int32_t gemm_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T, int block_m,
                            int64_t max_rows, const int* sorted_ids, const int* block_expert, const int* offsets,
                            const int* counts, void* act, hipStream_t s);
@@ -452,7 +453,7 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     // per-token fp64 router projection first; larger ones route in the fused
     // router kernel (projection on the matrix cores, top-k and x
     // quantization in the same launch).
-    const bool small_front = block_m == 16 && front_small_ok(T, k, L->n_shared);
+    const bool small_front = block_m == 16 && front_small_ok(T, k, L->n_shared) && stream_fused_perm_ok(T);
     const bool fused_router = !logits_or_null && !small_front && router_front_ok(E, L->D);
     float* lg = static_cast<float*>(at(o.logits));
     const float* logits = logits_or_null;
@@ -470,11 +471,11 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     const void* a = fp8 ? at(o.xq) : x_bf16;
     const float* a_scale = fp8 ? static_cast<float*>(at(o.xs)) : nullptr;
     if (small_front) {
-        // small batch: routing, permutation and x quantization in one launch
-        if ((st = front_small_launch(L, x_bf16, logits, T, block_m, static_cast<int>(o.max_rows), ids, w,
-                                     static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv,
-                                     fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr,
-                                     fp8 ? static_cast<float*>(at(o.xs)) : nullptr, s)) != MOE_OK)
+        // small batch: routing and x quantization in one launch; the
+        // weight-streaming gate/up GEMM builds the permutation itself
+        if ((st = front_route_quant_launch(L, x_bf16, logits, T, ids, w,
+                                           fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr,
+                                           fp8 ? static_cast<float*>(at(o.xs)) : nullptr, s)) != MOE_OK)
             return st;
     } else {
         // routing and x quantization in one launch (with the router
@@ -498,10 +499,13 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
         if (st != MOE_OK) return st;
     }
     void* act = at(o.act);
-    const int* counts = static_cast<int*>(at(o.counts));
-    if ((st = gemm_gateup_launch(L, a, a_scale, T, block_m, o.max_rows, sorted, bexp, offsets, counts, act, s)) !=
-        MOE_OK)
-        return st;
+    int* counts = static_cast<int*>(at(o.counts));
+    if (small_front)
+        st = stream_gateup_fused_launch(L, a, a_scale, T, ids, static_cast<int>(o.max_rows),
+                                        PermOut{counts, offsets, sorted, bexp, inv}, act, s);
+    else
+        st = gemm_gateup_launch(L, a, a_scale, T, block_m, o.max_rows, sorted, bexp, offsets, counts, act, s);
+    if (st != MOE_OK) return st;
     const void* act_in = act;
     const float* act_scale = nullptr;
     // the streaming down GEMM reads act codes stored in 16-row x 128-byte

@@ -1,5 +1,5 @@
-// Front end: routing and FP8 quantization of x in one launch (any batch);
-// for small batches (decode) the permutation in a second one.
+// Front end: routing and FP8 quantization of x in one launch (any batch),
+// and the one-workgroup permutation.
 //
 // At a few dozen tokens the routing, the three permutation steps and the FP8
 // quantization of x each move a few KB; as five separate launches they cost
@@ -9,16 +9,13 @@
 //   token_front_kernel: one workgroup of two waves per token; wave 0 routes
 //     the token (route_token, shared with the routing kernel), wave 1
 //     quantizes its x row (the row-quantization arithmetic), in parallel and
-//     spread over T CUs;
-//     (larger batches use it too, followed by the multi-kernel permutation);
-//   permute_small_kernel: one workgroup.  A token's k picks are distinct
-//     experts and T <= 64 (256 when it runs on its own after the routing of
-//     a larger batch), so every expert's rows are a mask of tokens, 32 per
-//     word (LDS atomicOr); a row's rank in its expert's segment is the
-//     number of mask bits below its token -- the stable ascending order of
-//     flat indices the multi-kernel permutation produces (shared-expert
-//     rows: token order).  Counts, padded offsets, sorted ids, inverse map,
-//     pads, block -> expert map and the tail are written exactly as there.
+//     spread over T CUs (every batch size uses it);
+//   permute_small_kernel: the permutation of up to 256 tokens' distinct
+//     picks by one workgroup (perm_dev.h: token masks, ranks by mask bits
+//     below the token) in place of the three launches of the general one.
+//     Up to 64 tokens in the weight-streaming path the gate/up GEMM builds
+//     the same permutation itself and this launch is not needed.
+#include "perm_dev.h"
 #include "quant_dev.h"
 #include "route_dev.h"
 
@@ -72,87 +69,10 @@ __global__ void __launch_bounds__(128) token_front_kernel(const FrontArgs p) {
 // MW: 32-token words of each expert's token mask (T <= 32 MW).
 template <int MW>
 __global__ void __launch_bounds__(kFrontWaves * 64) permute_small_kernel(const FrontArgs p) {
-    __shared__ int s_e[32 * MW * (MOE_MAX_TOPK + 1)];   // expert of each routed row (-1: no row)
-    __shared__ uint32_t s_m[MW][MOE_MAX_EXPERTS];      // word w: tokens 32w .. 32w+31 routed to the expert
-    __shared__ int s_off[MOE_MAX_EXPERTS + 1];         // padded offsets
-    __shared__ int s_wave[kFrontWaves];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    constexpr int NT = kFrontWaves * 64;
-    const int E = p.E, Ep = E + p.n_shared, k = p.k, B = p.block_m, T = p.T;
-    const int TK = T * k, A = T * (k + p.n_shared);
-
-    for (int e = tid; e < Ep; e += NT)
-#pragma unroll
-        for (int w = 0; w < MW; ++w) s_m[w][e] = 0;
-    __syncthreads();
-    for (int f = tid; f < TK; f += NT) {
-        const int id = p.ids[f], t = f / k;
-        const int e = (id >= 0 && id < E) ? id : -1;             // no valid pick: no row
-        s_e[f] = e;
-        if (e >= 0) atomicOr(&s_m[t >> 5][e], 1u << (t & 31));
-    }
-    __syncthreads();
-    auto popc_all = [&](int e) {
-        int n = 0;
-#pragma unroll
-        for (int w = 0; w < MW; ++w) n += __popc(s_m[w][e]);
-        return n;
-    };
-
-    // counts and padded offsets (one expert per thread, Ep <= 1024)
-    const int c = tid < E ? popc_all(tid) : (tid < Ep ? T : 0);
-    const int padded = (c + B - 1) / B * B;
-    int inc = wave_incl_scan_i(padded, lane);
-    if (lane == 63) s_wave[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        const int v = lane < kFrontWaves ? s_wave[lane] : 0;
-        const int sc = wave_incl_scan_i(v, lane);
-        if (lane < kFrontWaves) s_wave[lane] = sc - v;           // exclusive wave bases
-    }
-    __syncthreads();
-    inc += s_wave[wave];
-    if (tid < Ep) {
-        s_off[tid + 1] = inc;
-        p.counts[tid] = c;
-        p.offsets[tid + 1] = inc;
-    }
-    if (tid == 0) {
-        s_off[0] = 0;
-        p.offsets[0] = 0;
-    }
-    __syncthreads();
-
-    // rows: rank of token t in expert e = tokens below t routed to e
-    for (int f = tid; f < A; f += NT) {
-        int row;
-        if (f < TK) {
-            const int e = s_e[f], t = f / k;
-            if (e < 0) {
-                p.inv[f] = -1;
-                continue;
-            }
-            int below = __popc(s_m[t >> 5][e] & ((1u << (t & 31)) - 1u));
-#pragma unroll
-            for (int w = 0; w < MW; ++w)
-                if (w < (t >> 5)) below += __popc(s_m[w][e]);
-            row = s_off[e] + below;
-        } else {
-            row = s_off[E] + (f - TK);                                  // shared expert: token order
-        }
-        p.sorted[row] = f;
-        p.inv[f] = row;
-    }
-    // pads and block map (one wave per expert), tail past the total
-    for (int e = wave; e < Ep; e += kFrontWaves) {
-        const int n = e < E ? popc_all(e) : T;
-        const int lo = s_off[e], hi = s_off[e + 1];
-        for (int r = lo + n + lane; r < hi; r += 64) p.sorted[r] = A;
-        for (int b = lo / B + lane; b < hi / B; b += 64) p.bexp[b] = e;
-    }
-    const int total = s_off[Ep];
-    for (int b = total / B + tid; b < p.max_rows / B; b += NT) p.bexp[b] = -1;
-    for (int r = total + tid; r < p.max_rows; r += NT) p.sorted[r] = A;
+    __shared__ int s_e[32 * MW * MOE_MAX_TOPK];         // expert of each pick (-1: no row)
+    __shared__ PermShared<MW> s_perm;
+    perm_build<MW, kFrontWaves * 64>(p.ids, p.T, p.k, p.E, p.n_shared, p.block_m, p.max_rows, s_perm, s_e, nullptr,
+                                     PermOut{p.counts, p.offsets, p.sorted, p.bexp, p.inv}, true);
 }
 
 template <int EPL, int SCORING>
@@ -206,38 +126,6 @@ int32_t front_route_quant_launch(const moe_layer_desc* L, const void* x, const f
     a.xq = xq;
     a.xs = xs;
     front_tokens(L, a, s);
-    return moe_launch_status();
-}
-
-int32_t front_small_launch(const moe_layer_desc* L, const void* x, const float* logits, int T, int block_m,
-                           int max_rows, int* ids, float* w, int* counts, int* offsets, int* sorted, int* bexp,
-                           int* inv, uint8_t* xq, float* xs, hipStream_t s) {
-    FrontArgs a{};
-    a.logits = logits;
-    a.x = static_cast<const uint16_t*>(x);
-    a.T = T;
-    a.D = L->D;
-    a.E = L->E;
-    a.k = L->top_k;
-    a.n_shared = L->n_shared;
-    a.n_groups = L->n_groups;
-    a.topk_groups = L->topk_groups;
-    a.sel_bias = L->sel_bias;
-    a.renormalize = L->renormalize;
-    a.route_scale = L->route_scale;
-    a.block_m = block_m;
-    a.max_rows = max_rows;
-    a.ids = ids;
-    a.w = w;
-    a.counts = counts;
-    a.offsets = offsets;
-    a.sorted = sorted;
-    a.bexp = bexp;
-    a.inv = inv;
-    a.xq = xq;
-    a.xs = xs;
-    front_tokens(L, a, s);
-    hipLaunchKernelGGL(permute_small_kernel<kFrontMaxT / 32>, dim3(1), dim3(kFrontWaves * 64), 0, s, a);
     return moe_launch_status();
 }
 

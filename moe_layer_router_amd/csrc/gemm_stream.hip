@@ -19,7 +19,9 @@
 //     two v_mfma_f32_16x16x32_bf16), the next step's loads in flight while
 //     the current step multiplies;
 //   - activation rows are tiny and stay in L2.
-#include "common.h"
+#include "perm_dev.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -51,7 +53,22 @@ struct StreamArgs {
     int64_t out_ld;
     int n_exp;                 // E'
     int nslice;                // weight slices (one wave each) per expert
+    // gate_up given the routed ids instead of a permutation (T <= 64, distinct
+    // picks per token): every workgroup builds the permutation in LDS, and
+    // workgroup 0 writes it to `pout` for the launches that follow
+    const int* ids;            // [T, topk] (NULL: sorted_ids, offsets and counts are given)
+    int T, E, n_shared, max_rows;
+    PermOut pout;
 };
+
+// Where an item finds its expert's rows: the given permutation (tok NULL),
+// or the one built in LDS (padded and live offsets, token of each live row).
+struct PermRef {
+    const int* off;
+    const int* live;
+    const int* tok;
+};
+constexpr int kStreamPermMW = 2;           // mask words of the in-kernel permutation (T <= 64)
 
 template <int MODE>
 __device__ __forceinline__ void mfma16(const u32x8& a, const u32x8& b, v4f& acc) {
@@ -94,12 +111,23 @@ __device__ __forceinline__ int src_row(const StreamArgs& p, bool gateup, int row
 // One item: expert E, weight slice SL (COLS_W output columns), rows
 // [R0, R0 + 16*MT) of the expert's segment, on this wave.
 template <int MODE, bool GATEUP, int TN, int MT, int PF>
-__device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, int lane, int r0) {
+__device__ __forceinline__ void stream_item(const StreamArgs& p, const PermRef& pr, int e, int sl, int lane,
+                                            int r0) {
     constexpr bool BLOCKQ = MODE == MOE_QUANT_BLOCK128_FP8;
     constexpr int COLS_W = GATEUP ? TN / 2 * 16 : TN * 16;     // output columns per wave
-    const int row0 = p.offsets[e] + r0;
-    const int cnt = min(p.offsets[e + 1] - row0, 16 * MT);     // padded rows of this chunk
-    const int live = p.counts ? p.offsets[e] + p.counts[e] - row0 : cnt;   // rows before the pads
+    const int row0 = pr.off[e] + r0;
+    const int cnt = min(pr.off[e + 1] - row0, 16 * MT);        // padded rows of this chunk
+    const int nl = pr.tok ? pr.live[e + 1] - pr.live[e] : 0;   // routed rows of the expert (LDS permutation)
+    const int live = pr.tok ? pr.off[e] + nl - row0
+                            : (p.counts ? p.offsets[e] + p.counts[e] - row0 : cnt);   // rows before the pads
+    // token (gate_up) or row (down) of row r of this chunk; v: a routed row
+    auto src_of = [&](int r, bool& v) {
+        if (GATEUP && pr.tok) {
+            v = r0 + r < nl;
+            return v ? pr.tok[pr.live[e] + r0 + r] : 0;
+        }
+        return src_row(p, GATEUP, row0 + r, v);
+    };
     const int c0 = sl * COLS_W;                                 // first output column of this wave
     const int r16 = lane & 15, kq = (lane >> 4) * 16;
 
@@ -122,7 +150,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
     for (int m = 0; m < MT; ++m) {
         const int r = m * 16 + r16;
         bool v = false;
-        const int src = r < cnt ? src_row(p, GATEUP, row0 + r, v) : 0;
+        const int src = r < cnt ? src_of(r, v) : 0;
         const int64_t ar = v ? src : (GATEUP ? 0 : row0);
         ap[m] = p.a_blocked ? p.a + (ar >> 4) * (p.a_ld / 128) * 2048 + blocked_byte(static_cast<int>(ar & 15), kq)
                             : p.a + ar * p.a_ld + kq;
@@ -136,7 +164,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, int e, int sl, 
         for (int i = 0; i < 4; ++i) {
             const int r = m * 16 + (lane >> 4) * 4 + i;
             bool v = false;
-            const int src = r < cnt ? src_row(p, GATEUP, row0 + r, v) : 0;
+            const int src = r < cnt ? src_of(r, v) : 0;
             esrc[m][i] = v ? src : (GATEUP ? 0 : row0);
             emask[m][i] = v && r < live ? 1.0f : 0.0f;
         }
@@ -273,12 +301,25 @@ template <int MODE, bool GATEUP, int TN, int MT, int PF>
 __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
     __shared__ int s_act[MOE_MAX_EXPERTS];
     __shared__ int s_wcnt[4];
+    // the in-kernel permutation (gate_up given routed ids)
+    using PS = typename std::conditional<GATEUP, PermShared<kStreamPermMW>, int>::type;
+    __shared__ PS s_perm;
+    __shared__ int s_e[GATEUP ? 32 * kStreamPermMW * MOE_MAX_TOPK : 1];
+    __shared__ int s_tok[GATEUP ? 32 * kStreamPermMW * (MOE_MAX_TOPK + 1) : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    PermRef pr{p.offsets, nullptr, nullptr};
+    if constexpr (GATEUP) {
+        if (p.ids) {
+            perm_build<kStreamPermMW, 256>(p.ids, p.T, p.topk, p.E, p.n_shared, 16, p.max_rows, s_perm, s_e, s_tok,
+                                           p.pout, blockIdx.x == 0);
+            pr = PermRef{s_perm.off, s_perm.live, s_tok};
+        }
+    }
     // active experts in index order: thread t looks at experts t, t+256, ...
     int base = 0;
     for (int e0 = 0; e0 < p.n_exp; e0 += 256) {
         const int e = e0 + threadIdx.x;
-        const bool act = e < p.n_exp && p.offsets[e + 1] > p.offsets[e];
+        const bool act = e < p.n_exp && pr.off[e + 1] > pr.off[e];
         const uint64_t m = __ballot(act);
         if (lane == 0) s_wcnt[wave] = __popcll(m);
         __syncthreads();
@@ -292,16 +333,16 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
     const int G = gridDim.x;
     for (int i = blockIdx.x + G * wave; i < n_items; i += 4 * G) {
         const int j = i / p.nslice, e = s_act[j], sl = i - j * p.nslice;
-        const int rows = p.offsets[e + 1] - p.offsets[e];
+        const int rows = pr.off[e + 1] - pr.off[e];
         // experts with at most 16 (32) rows take the one-tile (two-tile) path:
         // fewer activation loads, registers and MFMAs; more rows than 16*MT
         // are handled in chunks.  Each path is branch-free inside.
         if (MT > 1 && rows <= 16) {
-            stream_item<MODE, GATEUP, TN, 1, PF>(p, e, sl, lane, 0);
+            stream_item<MODE, GATEUP, TN, 1, PF>(p, pr, e, sl, lane, 0);
         } else if (MT > 2 && rows <= 32) {
-            stream_item<MODE, GATEUP, TN, 2, PF>(p, e, sl, lane, 0);
+            stream_item<MODE, GATEUP, TN, 2, PF>(p, pr, e, sl, lane, 0);
         } else {
-            for (int r0 = 0; r0 < rows; r0 += 16 * MT) stream_item<MODE, GATEUP, TN, MT, PF>(p, e, sl, lane, r0);
+            for (int r0 = 0; r0 < rows; r0 += 16 * MT) stream_item<MODE, GATEUP, TN, MT, PF>(p, pr, e, sl, lane, r0);
         }
     }
 }
@@ -400,6 +441,42 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
     g.out_ld = L->I;
     return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s);
 }
+
+// gate_up from the routed ids (T <= 64, k picks per token distinct): the
+// kernel builds the permutation itself (workgroup 0 writes it to `pout`, for
+// the launches that follow), so no permutation launch precedes it.
+int32_t stream_gateup_fused_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
+                                   const int* ids, int max_rows, const PermOut& pout, void* act, hipStream_t s) {
+    const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    StreamArgs g{};
+    g.a = static_cast<const uint8_t*>(a);
+    g.a_ld = static_cast<int64_t>(L->D) * elem;
+    g.a_scale = a_scale;
+    g.a_scale_ld = L->D / 128;
+    g.topk = L->top_k;
+    g.TK = T * L->top_k;
+    g.sentinel = T * (L->top_k + L->n_shared);
+    g.w = static_cast<const uint8_t*>(L->w13);
+    g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
+    g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
+    g.w_scale = L->w13_scale;
+    g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? 2LL * L->I
+                                                  : static_cast<int64_t>(2 * L->I / 128) * (L->D / 128);
+    g.ws_ld = L->D / 128;
+    g.K = L->D;
+    g.I = L->I;
+    g.out = act;
+    g.out_ld = L->I;
+    g.ids = ids;
+    g.T = T;
+    g.E = L->E;
+    g.n_shared = L->n_shared;
+    g.max_rows = max_rows;
+    g.pout = pout;
+    return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s);
+}
+
+bool stream_fused_perm_ok(int T) { return T >= 1 && T <= 32 * kStreamPermMW; }
 
 int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T,
                            const int* offsets, const int* counts, void* out_perm, hipStream_t s, bool act_blocked) {
