@@ -453,7 +453,9 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     // per-token fp64 router projection first; larger ones route in the fused
     // router kernel (projection on the matrix cores, top-k and x
     // quantization in the same launch).
-    const bool small_front = block_m == 16 && front_small_ok(T, k, L->n_shared) && stream_fused_perm_ok(T);
+    const bool small_front = block_m == 16 && front_small_ok(T, k, L->n_shared);
+    // the weight-streaming gate/up GEMM builds the permutation itself
+    const bool perm_in_gemm = block_m == 16 && stream_fused_perm_ok(T);
     const bool fused_router = !logits_or_null && !small_front && router_front_ok(E, L->D);
     float* lg = static_cast<float*>(at(o.logits));
     const float* logits = logits_or_null;
@@ -470,16 +472,10 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     int* inv = static_cast<int*>(at(o.inv_perm));
     const void* a = fp8 ? at(o.xq) : x_bf16;
     const float* a_scale = fp8 ? static_cast<float*>(at(o.xs)) : nullptr;
-    if (small_front) {
-        // small batch: routing and x quantization in one launch; the
-        // weight-streaming gate/up GEMM builds the permutation itself
-        if ((st = front_route_quant_launch(L, x_bf16, logits, T, ids, w,
-                                           fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr,
-                                           fp8 ? static_cast<float*>(at(o.xs)) : nullptr, s)) != MOE_OK)
-            return st;
-    } else {
+    {
         // routing and x quantization in one launch (with the router
-        // projection when there are no logits), then the permutation: one
+        // projection when there are no logits), then the permutation: inside
+        // the weight-streaming gate/up GEMM up to 256 tokens, else one
         // workgroup up to 256 tokens (the routing's picks are distinct per
         // token), else the multi-kernel one
         uint8_t* xq = fp8 ? static_cast<uint8_t*>(at(o.xq)) : nullptr;
@@ -490,7 +486,9 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
         } else if ((st = front_route_quant_launch(L, x_bf16, logits, T, ids, w, xq, xs, s)) != MOE_OK) {
             return st;
         }
-        if (permute_small_ok(T, k, L->n_shared))
+        if (perm_in_gemm)
+            st = MOE_OK;
+        else if (permute_small_ok(T, k, L->n_shared))
             st = permute_small_launch(ids, T, k, E, L->n_shared, block_m, static_cast<int>(o.max_rows),
                                       static_cast<int*>(at(o.counts)), offsets, sorted, bexp, inv, s);
         else
@@ -500,7 +498,7 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     }
     void* act = at(o.act);
     int* counts = static_cast<int*>(at(o.counts));
-    if (small_front)
+    if (perm_in_gemm)
         st = stream_gateup_fused_launch(L, a, a_scale, T, ids, static_cast<int>(o.max_rows),
                                         PermOut{counts, offsets, sorted, bexp, inv}, act, s);
     else

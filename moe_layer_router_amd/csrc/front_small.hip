@@ -13,8 +13,8 @@
 //   permute_small_kernel: the permutation of up to 256 tokens' distinct
 //     picks by one workgroup (perm_dev.h: token masks, ranks by mask bits
 //     below the token) in place of the three launches of the general one.
-//     Up to 64 tokens in the weight-streaming path the gate/up GEMM builds
-//     the same permutation itself and this launch is not needed.
+//     In the weight-streaming path the gate/up GEMM builds the same
+//     permutation itself and this launch is not needed.
 #include "perm_dev.h"
 #include "quant_dev.h"
 #include "route_dev.h"

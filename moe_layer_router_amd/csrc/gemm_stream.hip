@@ -53,7 +53,7 @@ struct StreamArgs {
     int64_t out_ld;
     int n_exp;                 // E'
     int nslice;                // weight slices (one wave each) per expert
-    // gate_up given the routed ids instead of a permutation (T <= 64, distinct
+    // gate_up given the routed ids instead of a permutation (T <= 256, distinct
     // picks per token): every workgroup builds the permutation in LDS, and
     // workgroup 0 writes it to `pout` for the launches that follow
     const int* ids;            // [T, topk] (NULL: sorted_ids, offsets and counts are given)
@@ -68,7 +68,7 @@ struct PermRef {
     const int* live;
     const int* tok;
 };
-constexpr int kStreamPermMW = 2;           // mask words of the in-kernel permutation (T <= 64)
+constexpr int kStreamPermMW = 8;           // mask words of the in-kernel permutation (T <= 256)
 
 template <int MODE>
 __device__ __forceinline__ void mfma16(const u32x8& a, const u32x8& b, v4f& acc) {
@@ -442,7 +442,7 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
     return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s);
 }
 
-// gate_up from the routed ids (T <= 64, k picks per token distinct): the
+// gate_up from the routed ids (T <= 256, k picks per token distinct): the
 // kernel builds the permutation itself (workgroup 0 writes it to `pout`, for
 // the launches that follow), so no permutation launch precedes it.
 int32_t stream_gateup_fused_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
