@@ -46,9 +46,10 @@ something other than itself -- torch CPU dtype casts and brute-force
 nearest-code search for the codecs, rank-counting brute force for top-k and
 group selection, Python ``sorted`` for the permutation, a dense SwiGLU MLP
 (E=1, top-1) and a per-token pure-Python evaluation for the layer, and
-invariants (identical experts, token-order permutation).  The layer output on
-full-size random inputs has no printed worked example on the pages, so beyond
-those identities it is "parity unpinned".
+invariants (identical experts, token-order permutation).  The pages print no
+worked example of a whole layer; moe_forward is pinned by the per-token
+evaluation and the dense identities at small sizes and runs the same code at
+full size.
 """
 
 from __future__ import annotations
