@@ -413,21 +413,17 @@ static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, 
 }
 
 
-int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
-                             const int* sorted_ids, const int* offsets, const int* counts, void* act,
-                             hipStream_t s) {
+// The gate/up arguments every variant shares.
+static StreamArgs gateup_args(const moe_layer_desc* L, const void* a, const float* a_scale, int T, void* act) {
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
     StreamArgs g{};
     g.a = static_cast<const uint8_t*>(a);
     g.a_ld = static_cast<int64_t>(L->D) * elem;
     g.a_scale = a_scale;
     g.a_scale_ld = L->D / 128;
-    g.sorted_ids = sorted_ids;
     g.topk = L->top_k;
     g.TK = T * L->top_k;
     g.sentinel = T * (L->top_k + L->n_shared);
-    g.offsets = offsets;
-    g.counts = counts;
     g.w = static_cast<const uint8_t*>(L->w13);
     g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
     g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
@@ -439,6 +435,16 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
     g.I = L->I;
     g.out = act;
     g.out_ld = L->I;
+    return g;
+}
+
+int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
+                             const int* sorted_ids, const int* offsets, const int* counts, void* act,
+                             hipStream_t s) {
+    StreamArgs g = gateup_args(L, a, a_scale, T, act);
+    g.sorted_ids = sorted_ids;
+    g.offsets = offsets;
+    g.counts = counts;
     return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s);
 }
 
@@ -447,26 +453,7 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
 // the launches that follow), so no permutation launch precedes it.
 int32_t stream_gateup_fused_launch(const moe_layer_desc* L, const void* a, const float* a_scale, int T,
                                    const int* ids, int max_rows, const PermOut& pout, void* act, hipStream_t s) {
-    const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
-    StreamArgs g{};
-    g.a = static_cast<const uint8_t*>(a);
-    g.a_ld = static_cast<int64_t>(L->D) * elem;
-    g.a_scale = a_scale;
-    g.a_scale_ld = L->D / 128;
-    g.topk = L->top_k;
-    g.TK = T * L->top_k;
-    g.sentinel = T * (L->top_k + L->n_shared);
-    g.w = static_cast<const uint8_t*>(L->w13);
-    g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
-    g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
-    g.w_scale = L->w13_scale;
-    g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? 2LL * L->I
-                                                  : static_cast<int64_t>(2 * L->I / 128) * (L->D / 128);
-    g.ws_ld = L->D / 128;
-    g.K = L->D;
-    g.I = L->I;
-    g.out = act;
-    g.out_ld = L->I;
+    StreamArgs g = gateup_args(L, a, a_scale, T, act);
     g.ids = ids;
     g.T = T;
     g.E = L->E;
