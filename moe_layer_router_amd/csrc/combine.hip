@@ -14,9 +14,10 @@ struct alignas(16) f32x4 { float v[4]; };
 
 // OUT_BF16: out_perm rows are bf16 (else fp32).  Workgroup (t, y) owns
 // columns [2048 y, 2048 y + 2048) of token t, 8 per thread.  The row indices
-// and weights come first (uniform per workgroup), then all of the token's
-// k + n_shared row loads are issued before any is consumed (the kernel is
-// bound by memory latency and bandwidth, not arithmetic).  NR >= k + n_shared.
+// and weights come first (uniform per workgroup), then the token's
+// k + n_shared row loads are issued, up to 9 before any is consumed (the
+// kernel is bound by memory latency and bandwidth, not arithmetic).
+// NR >= k + n_shared.
 template <bool OUT_BF16, int NR>
 __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ out_perm,
                                                       const int* __restrict__ inv_perm,
@@ -37,44 +38,51 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ o
         }
     }
     if (c >= (D >> 3)) return;
-    float o[NR][8];
-#pragma unroll
-    for (int j = 0; j < NR; ++j) {
-        if (r[j] >= 0) {
-            if (OUT_BF16) {
-                // each expert-output row is read once: non-temporal
-                const bf16x8 v = ld_once(reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(out_perm) +
-                                                                         static_cast<int64_t>(r[j]) * D) + c);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) o[j][i] = bf16_to_f32(v.v[i]);
-            } else {
-                const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(out_perm) +
-                                                                static_cast<int64_t>(r[j]) * D) + 2 * c;
-                const f32x4 a = p[0], b = p[1];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { o[j][i] = a.v[i]; o[j][4 + i] = b.v[i]; }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[j][i] = 0.0f;
-        }
-    }
-    // j = 0 .. k-1 (weighted, fused multiply-add), then the shared row
+    // Rows are loaded BATCH at a time (all of them up to 9 rows; in batches
+    // of 6 above, for registers and so waves per SIMD) and summed in index
+    // order: j = 0 .. k-1 weighted (fused multiply-add), then the shared row,
+    // the same order whatever the batch.
+    constexpr int BATCH = NR <= 9 ? NR : 6;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-        if (j < k && r[j] >= 0) {
+    for (int b0 = 0; b0 < NR; b0 += BATCH) {
+        float o[BATCH][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], o[j][i], acc[i]);
+        for (int jj = 0; jj < BATCH; ++jj) {
+            const int j = b0 + jj;
+            if (j < NR && r[j] >= 0) {
+                if (OUT_BF16) {
+                    // each expert-output row is read once: non-temporal
+                    const bf16x8 v = ld_once(reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(out_perm) +
+                                                                             static_cast<int64_t>(r[j]) * D) + c);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) o[jj][i] = bf16_to_f32(v.v[i]);
+                } else {
+                    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(out_perm) +
+                                                                    static_cast<int64_t>(r[j]) * D) + 2 * c;
+                    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { o[jj][i] = a.v[i]; o[jj][4 + i] = b.v[i]; }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[jj][i] = 0.0f;
+            }
         }
-    }
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-        if (j >= k && j < nr && r[j] >= 0) {
+        for (int jj = 0; jj < BATCH; ++jj) {
+            const int j = b0 + jj;
+            if (j < NR && r[j] >= 0) {
+                if (j < k) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += o[j][i];
+                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], o[jj][i], acc[i]);
+                } else if (j < nr) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] += o[jj][i];
+                }
+            }
         }
     }
     bf16x8 out;
