@@ -198,6 +198,73 @@ def timed_calls(torch, call, steps, warmup):
     return pick(0.5), pick(0.1), pick(0.9)
 
 
+def sclk_during(torch, call, seconds=2.0):
+    """The shader clock under the timed workload: `call` runs back to back for
+    `seconds` (after the timed region, which the sampling never overlaps)
+    while a host thread polls the SMU metrics of the GPU at cuda:0's PCI
+    address through amdsmi.  The SMU refreshes them every 100-200 ms (its
+    gfx activity accumulator advances at each refresh): each refresh counts
+    once, the one current when the calls start is dropped, and so is any
+    whose average gfx activity is under 50 %.  A reading is the mean of the
+    XCDs' current gfx clocks.  Without amdsmi or a fresh busy reading the
+    figure is None, with the reason."""
+    import threading
+    try:
+        import amdsmi
+    except Exception as e:                                  # noqa: BLE001 - reported, not fatal
+        return {"mhz_median": None, "reason": f"amdsmi not importable: {e}"}
+    prop = torch.cuda.get_device_properties(0)
+    bdf = f"{prop.pci_domain_id:04x}:{prop.pci_bus_id:02x}:{prop.pci_device_id:02x}"
+    try:
+        amdsmi.amdsmi_init()
+    except Exception as e:                                  # noqa: BLE001
+        return {"mhz_median": None, "reason": f"amdsmi_init: {e}"}
+    try:
+        h = next((h for h in amdsmi.amdsmi_get_processor_handles()
+                  if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(bdf)), None)
+        if h is None:
+            return {"mhz_median": None, "reason": f"no amdsmi device at {bdf}"}
+        seen, readings, errors, stop = set(), [], [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                except Exception as e:                      # noqa: BLE001
+                    errors.append(str(e))
+                    return
+                acc, act, per = m.get("gfx_activity_acc"), m.get("average_gfx_activity"), m.get("current_gfxclks")
+                if acc not in seen:
+                    fresh = bool(seen)
+                    seen.add(acc)
+                    v = [c for c in per if isinstance(c, (int, float)) and c > 0] if isinstance(per, list) else []
+                    if fresh and v and isinstance(act, (int, float)) and act >= 50:
+                        readings.append(sum(v) / len(v))
+                stop.wait(0.01)
+
+        torch.cuda.synchronize()
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            call()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not readings:
+            return {"mhz_median": None, "calls": n,
+                    "reason": errors[0] if errors else "no fresh metrics with the GPU busy"}
+        r = sorted(readings)
+        return {"mhz_median": round(r[len(r) // 2], 1), "mhz_min": round(r[0], 1), "mhz_max": round(r[-1], 1),
+                "readings": len(r), "calls": n, "seconds": seconds,
+                "source": "amdsmi gpu_metrics current_gfxclks (mean over XCDs), fresh SMU refreshes only"}
+    finally:
+        amdsmi.amdsmi_shut_down()
+
+
 def weight_copies(mlr, layer):
     """The layer plus identical copies of its weights when they are under
     1 GiB (part of them could stay in the 256 MB MALL between steps): steps
@@ -422,6 +489,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layers", action="store_true", help="skip the legs of the other layer shapes")
     ap.add_argument("--no-payload", action="store_true", help="skip the expert-parallel payload leg")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip the shader-clock sampling after the timed steps (profiled runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="launch one device-to-device copy of this many MiB (a known-size kernel for "
                          "calibrating HBM byte counters)")
@@ -476,6 +545,8 @@ def main():
     f1.record()
     torch.cuda.synchronize()
     ms = f0.elapsed_time(f1) / args.steps
+    sclk = None if args.no_sclk else sclk_during(torch, fwd)
+    log("sclk", sclk)
 
     # the step entries, HIP events around the grouped GEMMs (over the same
     # weight copies in turn)
@@ -543,6 +614,7 @@ def main():
                   "GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
                   "frac_hbm": round(layer_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "routing": load,
+        "sclk": sclk,
         "step_entries_ms_per_step": round(steps_ms, 4), "step_entries_equal_fused": same,
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
     }
