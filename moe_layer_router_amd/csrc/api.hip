@@ -371,7 +371,7 @@ int32_t moe_unpermute_combine(const void* out_perm, int32_t out_dtype, const int
     MOE_CHECK_ARG(T >= 0 && k > 0 && D > 0 && (n_shared == 0 || n_shared == 1));
     MOE_CHECK_ARG(out_dtype == 0 || out_dtype == 1);
     MOE_CHECK_SUP(D % 8 == 0);
-    MOE_CHECK_SUP(k + n_shared <= MOE_MAX_TOPK + 1);   // rows a token gathers, all loads in flight at once
+    MOE_CHECK_SUP(k + n_shared <= MOE_MAX_TOPK + 1);   // rows a token gathers: the widest kernel instance has 17 row slots
     if (T == 0) return MOE_OK;
     MOE_CHECK_ARG(out_perm && inv_perm && topk_w && y_bf16);
     return combine_launch(out_perm, out_dtype, inv_perm, topk_w, T, k, n_shared, D, static_cast<uint16_t*>(y_bf16),

@@ -23,7 +23,7 @@ REDUCED = {
     "qwen3_235b_decode_ptpc": synth.get("qwen3_235b_decode_ptpc"),
     "deepseek_r1_block_fp8_r": synth.get("deepseek_r1_block_fp8").replace(T=300, D=1024, I=256, E=32),
     "bf16_multi_tile_r": synth.get("tiny_bf16").replace(T=700, D=512, I=256, E=16, k=4),
-    # small batches for the weight-streaming kernels (block_m 16, T <= 64)
+    # small batches for the weight-streaming kernels (block_m 16: T <= 64, or at most 24 rows per expert)
     "deepseek_r1_block_fp8_small": synth.get("deepseek_r1_block_fp8").replace(T=40, D=1024, I=256, E=32),
     "qwen3_235b_decode_ptpc_t64": synth.get("qwen3_235b_decode_ptpc").replace(T=64, D=1024, I=512, E=16),
     "bf16_small_t20": synth.get("tiny_bf16").replace(T=20, D=512, I=256, E=16, k=4),
