@@ -107,8 +107,9 @@ extern "C" {
  *   Microscaling v1.0): activations, weights and the re-quantized act are
  *   all E2M1 with an E8M0 scale 2^e per 32 elements along the reduction
  *   dimension, e = floor(log2(amax)) - 2 clamped to [-127, 127]; the matrix
- *   cores apply both scales.  I % 256 == 0; block_m 32, 64, 128 or 192 (the
- *   LDS-tiled kernels; moe_default_block_m never picks 16 for it).
+ *   cores apply both scales.  I % 256 == 0; block_m 16 (weight streaming,
+ *   the default up to 64 tokens), 32, 64, 128 or 192 (the LDS-tiled
+ *   kernels).
  *   weight_layout: order of the bytes of each [N, K] weight matrix (w13:
  *              N = 2I, K = D; w2: N = D, K = I; K_bytes = K, or K/2 for MXFP4):
  *              MOE_WEIGHTS_ROWS    row-major, K contiguous;
@@ -302,7 +303,7 @@ int32_t moe_quant_weight_fp8(const void* w_bf16, int64_t n_mats, int32_t N, int3
  * kernels; their contents are then unspecified); rows at or past
  * expert_offsets[E'] are not written.  block_m must equal the block_m of moe_permute_align and be one
  * of: 16 (weight-streaming kernels for small batches: each weight byte is
- * read once per 64 rows of its expert; not for MXFP4), 32, 64, 128, 192
+ * read once per 64 rows of its expert), 32, 64, 128, 192
  * (FP8 and MXFP4 only) or 256 (not MXFP4) (LDS-tiled kernels).  Shapes: I % 128 == 0 (MXFP4: 256) and D % 256 == 0.
  */
 int32_t moe_grouped_gemm_gateup_silu(const moe_layer_desc* L, const void* a,

@@ -120,12 +120,11 @@ int act_group(const moe_layer_desc* L) {
     }
 }
 
-// the weight-streaming kernels (block_m 16) cover bf16 and the FP8 modes;
-// MXFP4 runs the LDS-tiled kernels up to 192-row tiles (the 256-row tile's
-// scale words do not fit its registers); 192-row tiles exist for the
-// quantized modes
+// the weight-streaming kernels (block_m 16) cover every mode; MXFP4 runs
+// the LDS-tiled kernels up to 192-row tiles (the 256-row tile's scale words
+// do not fit its registers); 192-row tiles exist for the quantized modes
 bool block_m_ok_for(const moe_layer_desc* L, int block_m) {
-    if (L->quant == MOE_QUANT_MXFP4) return block_m == 32 || block_m == 64 || block_m == 128 || block_m == 192;
+    if (L->quant == MOE_QUANT_MXFP4) return block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128 || block_m == 192;
     if (L->quant == MOE_QUANT_NONE_BF16 && block_m == 192) return false;   // (the 192-row tile: quantized modes)
     return block_m_ok(block_m);
 }
@@ -382,7 +381,10 @@ int32_t moe_default_block_m(const moe_layer_desc* L, int32_t T) {
     if (!L || L->E <= 0 || T < 0) return 64;
     const int64_t rows = static_cast<int64_t>(T) * (L->top_k + L->n_shared);
     const int64_t per_expert = rows / (L->E + L->n_shared);
-    if (T <= kStreamMaxT) return L->quant == MOE_QUANT_MXFP4 ? 32 : 16;
+    // small batches stream the weights in every mode (MXFP4 on the Qwen3-235B
+    // decode shape, T = 16 / 32 / 48 / 64: 100 / 126 / 158 / 160 us with
+    // 32-row tiles, 90 / 115 / 135 / 145 us streaming)
+    if (T <= kStreamMaxT) return 16;
     // A few dozen rows per expert: the weight-streaming kernels (every
     // active expert's weights read once per 64 of its rows) beat 32-row
     // tiles (the Qwen3-30B-A3B-shaped batch, 16 rows per expert:
@@ -514,9 +516,9 @@ int32_t moe_forward(const moe_layer_desc* L, const void* x_bf16, const float* lo
     const bool aq_blocked = fp8 && block_m == 16;
     if (fp8) {
         if (group == 32) {
-            st = quant_mx_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, offsets + Ep, false, sorted,
-                                      T * (k + L->n_shared), static_cast<uint8_t*>(at(o.aq)),
-                                      static_cast<uint8_t*>(at(o.as)), s);
+            st = quant_mx_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, offsets + Ep, aq_blocked,
+                                      block_m == 16 ? nullptr : sorted, T * (k + L->n_shared),
+                                      static_cast<uint8_t*>(at(o.aq)), static_cast<uint8_t*>(at(o.as)), s);
         } else {
             st = quant_rows_launch(static_cast<const uint16_t*>(act), o.max_rows, L->I, group, offsets + Ep,
                                    static_cast<uint8_t*>(at(o.aq)), static_cast<float*>(at(o.as)), s, aq_blocked,

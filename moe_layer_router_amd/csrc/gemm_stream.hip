@@ -16,8 +16,9 @@
 //     filled round of workgroups idles most of the chip;
 //   - no LDS: each lane streams 32 B of a weight row per 128-byte K step
 //     straight into MFMA operand registers (v_mfma_f32_16x16x128_f8f6f4, or
-//     two v_mfma_f32_16x16x32_bf16), the next step's loads in flight while
-//     the current step multiplies;
+//     two v_mfma_f32_16x16x32_bf16, or for MXFP4 two FP4 MFMAs with the
+//     E8M0 block scales as operands), the next step's loads in flight
+//     while the current step multiplies;
 //   - activation rows are tiny and stay in L2.
 #include "perm_dev.h"
 
@@ -47,6 +48,9 @@ struct StreamArgs {
     const float* w_scale;
     int64_t ws_expert;
     int ws_ld;
+    const uint8_t* a_mx;       // MXFP4: E8M0 scales of the activation rows [rows, K/32]
+    const uint8_t* w_mx;       // MXFP4: E8M0 weight scales [E', Nw, K/32]
+    int64_t w_mx_expert;       // MXFP4: scale bytes per expert
     int K;                     // elements
     int I;                     // gate_up act columns
     void* out;
@@ -85,6 +89,22 @@ __device__ __forceinline__ void mfma16(const u32x8& a, const u32x8& b, v4f& acc)
     }
 }
 
+// MXFP4: a lane's 32 bytes of a 128-byte step (256 E2M1 elements per row)
+// are two 16-byte pieces, elements 32q .. 32q+31 and 128+32q .. 128+32q+31
+// of the step (q = lane / 16): the lane's part of two 16x16x128 MFMAs, one
+// per piece C, each an aligned 32-element block with one E8M0 scale.  The
+// step's 8 scale bytes of a row are two dwords; piece C takes byte q of
+// dword C, shifted to byte 0 (operand byte select 0).  Format selectors 4
+// (FP4) for both operands: the MFMA reads the piece's four registers.
+template <int C>
+__device__ __forceinline__ void mfma16_mx(const u32x4_s& a, const u32x4_s& b, uint2 as, uint2 ws, int sh, v4f& acc) {
+    const u32x4_s z = {0u, 0u, 0u, 0u};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        __builtin_bit_cast(v8i_s, __builtin_shufflevector(a, z, 0, 1, 2, 3, 4, 5, 6, 7)),
+        __builtin_bit_cast(v8i_s, __builtin_shufflevector(b, z, 0, 1, 2, 3, 4, 5, 6, 7)), acc, 4, 4, 0,
+        static_cast<int>((C == 0 ? as.x : as.y) >> sh), 0, static_cast<int>((C == 0 ? ws.x : ws.y) >> sh));
+}
+
 // A lane's 32 operand bytes of one 128-byte K step: bytes [16q, 16q+16) and
 // [64+16q, 64+16q+16) of its row, q = lane / 16; the second piece is HI
 // bytes after the first (64 in a row-major row; 1024 in a blocked weight
@@ -114,6 +134,7 @@ template <int MODE, bool GATEUP, int TN, int MT, int PF>
 __device__ __forceinline__ void stream_item(const StreamArgs& p, const PermRef& pr, int e, int sl, int lane,
                                             int r0) {
     constexpr bool BLOCKQ = MODE == MOE_QUANT_BLOCK128_FP8;
+    constexpr bool MX = MODE == MOE_QUANT_MXFP4;
     constexpr int COLS_W = GATEUP ? TN / 2 * 16 : TN * 16;     // output columns per wave
     const int row0 = pr.off[e] + r0;
     const int cnt = min(pr.off[e + 1] - row0, 16 * MT);        // padded rows of this chunk
@@ -132,7 +153,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, const PermRef& 
     const int r16 = lane & 15, kq = (lane >> 4) * 16;
 
     const uint8_t* wexp = p.w + static_cast<int64_t>(e) * p.w_expert_bytes;
-    const int64_t wrow = static_cast<int64_t>(p.K) * (MODE == MOE_QUANT_NONE_BF16 ? 2 : 1);
+    const int64_t wrow = MX ? p.K / 2 : static_cast<int64_t>(p.K) * (MODE == MOE_QUANT_NONE_BF16 ? 2 : 1);
     const uint8_t* bp[TN];
     int wn0[TN];                                                  // first weight row of each tile
 #pragma unroll
@@ -143,6 +164,15 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, const PermRef& 
         bp[t] = p.w_blocked ? wexp + static_cast<int64_t>(wn0[t] >> 4) * (wrow / 128) * 2048 + blocked_byte(r16, kq)
                             : wexp + (wn0[t] + r16) * wrow + kq;
     }
+    // MXFP4: the scale row of the lane's weight row in each tile, and of its
+    // activation row in each M tile (8 bytes per step)
+    const int sld = p.K / 32;
+    const uint8_t* wsp[MX ? TN : 1];
+    const uint8_t* asp[MX ? MT : 1];
+    if constexpr (MX) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) wsp[t] = p.w_mx + e * p.w_mx_expert + static_cast<int64_t>(wn0[t] + r16) * sld;
+    }
     // operand rows: row r16 of each M tile; rows past the segment or on a pad
     // slot read a valid row and are zeroed by the epilogue's row mask
     const uint8_t* ap[MT];
@@ -152,6 +182,7 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, const PermRef& 
         bool v = false;
         const int src = r < cnt ? src_of(r, v) : 0;
         const int64_t ar = v ? src : (GATEUP ? 0 : row0);
+        if constexpr (MX) asp[m] = p.a_mx + ar * sld;
         ap[m] = p.a_blocked ? p.a + (ar >> 4) * (p.a_ld / 128) * 2048 + blocked_byte(static_cast<int>(ar & 15), kq)
                             : p.a + ar * p.a_ld + kq;
     }
@@ -183,17 +214,38 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, const PermRef& 
     // fixed by the item (expert, slice): results stay deterministic.
     const int kbeg = (sl * 5 + e * 3) % nk;
 
-    u32x8 bq[PF][TN], aqr[PF][MT];
+    u32x8 bq[MX ? 1 : PF][TN], aqr[MX ? 1 : PF][MT];
     float asq[PF][MT][4];
+    // MXFP4: the two 16-byte pieces of each operand as separate values (each
+    // is a whole MFMA operand), and the step's scale dwords
+    u32x4_s bq2[MX ? PF : 1][TN][2], aq2[MX ? PF : 1][MT][2];
+    uint2 wsq[MX ? PF : 1][MX ? TN : 1], asx[MX ? PF : 1][MX ? MT : 1];
     auto fill = [&](int j, int s) {
         int ks = s + kbeg;
         ks = ks >= nk ? ks - nk : ks;
         const int64_t ko = static_cast<int64_t>(ks) * (p.a_blocked ? 2048 : 128);   // step offset in the rows
         const int64_t kw = static_cast<int64_t>(ks) * (p.w_blocked ? 2048 : 128);   // step offset in the weights
+        if constexpr (MX) {
 #pragma unroll
-        for (int t = 0; t < TN; ++t) bq[j][t] = ld32(bp[t] + kw, whi);
+            for (int t = 0; t < TN; ++t) {
+                bq2[j][t][0] = *reinterpret_cast<const u32x4_s*>(bp[t] + kw);
+                bq2[j][t][1] = *reinterpret_cast<const u32x4_s*>(bp[t] + kw + whi);
+            }
 #pragma unroll
-        for (int m = 0; m < MT; ++m) aqr[j][m] = ld32(ap[m] + ko, ahi);
+            for (int m = 0; m < MT; ++m) {
+                aq2[j][m][0] = *reinterpret_cast<const u32x4_s*>(ap[m] + ko);
+                aq2[j][m][1] = *reinterpret_cast<const u32x4_s*>(ap[m] + ko + ahi);
+            }
+#pragma unroll
+            for (int t = 0; t < TN; ++t) wsq[j][t] = *reinterpret_cast<const uint2*>(wsp[t] + 8 * ks);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) asx[j][m] = *reinterpret_cast<const uint2*>(asp[m] + 8 * ks);
+        } else {
+#pragma unroll
+            for (int t = 0; t < TN; ++t) bq[j][t] = ld32(bp[t] + kw, whi);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) aqr[j][m] = ld32(ap[m] + ko, ahi);
+        }
         if constexpr (BLOCKQ) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -202,7 +254,21 @@ __device__ __forceinline__ void stream_item(const StreamArgs& p, const PermRef& 
         }
     };
     auto compute = [&](int j, int s) {
-        if constexpr (!BLOCKQ) {
+        if constexpr (MX) {
+            // every tile's first piece, then every tile's second: an
+            // accumulator's two MFMAs of the step are MT*TN MFMAs apart
+            const int sh = 8 * (lane >> 4);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    mfma16_mx<0>(aq2[j][m][0], bq2[j][t][0], asx[j][m], wsq[j][t], sh, acc[m][t]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    mfma16_mx<1>(aq2[j][m][1], bq2[j][t][1], asx[j][m], wsq[j][t], sh, acc[m][t]);
+        } else if constexpr (!BLOCKQ) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -351,8 +417,9 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
 // steps in flight per wave.  In the PTPC mode both GEMMs stream 4 tiles per
 // wave (one wave per SIMD): Qwen3-235B decode step 165.9 -> 163.8 us with 4
 // gate/up tiles instead of 2, then 162.9 -> 161.8 us with 4 down tiles.  The
-// blockwise mode keeps 2 (its per-step scales would not fit the registers),
-// and so does bf16 (4 tiles halve its waves; the 64-token bf16 layer went
+// blockwise mode keeps 2 (its per-step scales would not fit the registers);
+// MXFP4 streams 4 up to 32 rows per launch tile set and 2 beyond (its scale
+// dwords and two-piece operands spill at 4 tiles with 64 rows), and so does bf16 (4 tiles halve its waves; the 64-token bf16 layer went
 // from 0.028 to 0.032 ms).  One tile
 // per wave for down spread its items more evenly over the waves but halved
 // the bytes each wave keeps in flight, and measured slower (178 -> 196 us);
@@ -360,8 +427,8 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
 // 181 us): the waves share HBM bandwidth, and the few that run a last round
 // get more of it.  3 or 6 steps in flight instead of 4 were slower (167.4,
 // 167.3 against 165.9 us).
-template <int MODE, bool GATEUP>
-constexpr int stream_tn() { return MODE == MOE_QUANT_PTPC_FP8 ? 4 : 2; }
+template <int MODE, bool GATEUP, int MT>
+constexpr int stream_tn() { return MODE == MOE_QUANT_PTPC_FP8 || (MODE == MOE_QUANT_MXFP4 && MT <= 2) ? 4 : 2; }
 constexpr int kStreamPF = 4;
 
 // Workgroups of a kernel that fit on the device at once, per device (CACHE:
@@ -382,8 +449,11 @@ static int resident_blocks(Kern kernel, int (&cache)[64]) {
 }
 
 template <int MODE, bool GATEUP, int MT>
-static int32_t stream_launch_mt(const StreamArgs& a, hipStream_t s) {
-    auto kern = stream_gemm_kernel<MODE, GATEUP, stream_tn<MODE, GATEUP>(), MT, kStreamPF>;
+static int32_t stream_launch_mt(StreamArgs a, int ncols, hipStream_t s) {
+    constexpr int TN = stream_tn<MODE, GATEUP, MT>();
+    constexpr int COLS_W = GATEUP ? TN / 2 * 16 : TN * 16;   // output columns per item
+    a.nslice = ncols / COLS_W;
+    auto kern = stream_gemm_kernel<MODE, GATEUP, TN, MT, kStreamPF>;
     static int cache[64];
     // no more workgroups than items could need (E' experts x slices / 4 waves)
     const int wgs = min(resident_blocks(kern, cache),
@@ -394,12 +464,10 @@ static int32_t stream_launch_mt(const StreamArgs& a, hipStream_t s) {
 
 template <int MODE, bool GATEUP>
 static int32_t stream_launch_mode(StreamArgs a, int Ep, int ncols, int T, hipStream_t s) {
-    constexpr int COLS_W = GATEUP ? stream_tn<MODE, GATEUP>() / 2 * 16 : stream_tn<MODE, GATEUP>() * 16;
     a.n_exp = Ep;
-    a.nslice = ncols / COLS_W;
-    if (T <= 16) return stream_launch_mt<MODE, GATEUP, 1>(a, s);
-    if (T <= 32) return stream_launch_mt<MODE, GATEUP, 2>(a, s);
-    return stream_launch_mt<MODE, GATEUP, 4>(a, s);
+    if (T <= 16) return stream_launch_mt<MODE, GATEUP, 1>(a, ncols, s);
+    if (T <= 32) return stream_launch_mt<MODE, GATEUP, 2>(a, ncols, s);
+    return stream_launch_mt<MODE, GATEUP, 4>(a, ncols, s);
 }
 
 template <bool GATEUP>
@@ -408,6 +476,7 @@ static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, 
         case MOE_QUANT_NONE_BF16: return stream_launch_mode<MOE_QUANT_NONE_BF16, GATEUP>(a, Ep, ncols, T, s);
         case MOE_QUANT_PTPC_FP8: return stream_launch_mode<MOE_QUANT_PTPC_FP8, GATEUP>(a, Ep, ncols, T, s);
         case MOE_QUANT_BLOCK128_FP8: return stream_launch_mode<MOE_QUANT_BLOCK128_FP8, GATEUP>(a, Ep, ncols, T, s);
+        case MOE_QUANT_MXFP4: return stream_launch_mode<MOE_QUANT_MXFP4, GATEUP>(a, Ep, ncols, T, s);
     }
     return MOE_ERR_UNSUPPORTED;
 }
@@ -416,9 +485,15 @@ static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, 
 // The gate/up arguments every variant shares.
 static StreamArgs gateup_args(const moe_layer_desc* L, const void* a, const float* a_scale, int T, void* act) {
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    const bool mx = L->quant == MOE_QUANT_MXFP4;   // a_scale: the rows' E8M0 bytes
     StreamArgs g{};
     g.a = static_cast<const uint8_t*>(a);
-    g.a_ld = static_cast<int64_t>(L->D) * elem;
+    g.a_ld = mx ? L->D / 2 : static_cast<int64_t>(L->D) * elem;
+    if (mx) {
+        g.a_mx = reinterpret_cast<const uint8_t*>(a_scale);
+        g.w_mx = reinterpret_cast<const uint8_t*>(L->w13_scale);
+        g.w_mx_expert = 2LL * L->I * (L->D / 32);
+    }
     g.a_scale = a_scale;
     g.a_scale_ld = L->D / 128;
     g.topk = L->top_k;
@@ -426,7 +501,7 @@ static StreamArgs gateup_args(const moe_layer_desc* L, const void* a, const floa
     g.sentinel = T * (L->top_k + L->n_shared);
     g.w = static_cast<const uint8_t*>(L->w13);
     g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
-    g.w_expert_bytes = static_cast<int64_t>(2) * L->I * L->D * elem;
+    g.w_expert_bytes = mx ? static_cast<int64_t>(L->I) * L->D : static_cast<int64_t>(2) * L->I * L->D * elem;
     g.w_scale = L->w13_scale;
     g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? 2LL * L->I
                                                   : static_cast<int64_t>(2 * L->I / 128) * (L->D / 128);
@@ -468,10 +543,16 @@ bool stream_fused_perm_ok(int T) { return T >= 1 && T <= 32 * kStreamPermMW; }
 int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float* act_scale, int T,
                            const int* offsets, const int* counts, void* out_perm, hipStream_t s, bool act_blocked) {
     const int elem = L->quant == MOE_QUANT_NONE_BF16 ? 2 : 1;
+    const bool mx = L->quant == MOE_QUANT_MXFP4;   // act_scale: the rows' E8M0 bytes
     StreamArgs g{};
     g.a = static_cast<const uint8_t*>(act);
-    g.a_ld = static_cast<int64_t>(L->I) * elem;
+    g.a_ld = mx ? L->I / 2 : static_cast<int64_t>(L->I) * elem;
     g.a_blocked = act_blocked && elem == 1;
+    if (mx) {
+        g.a_mx = reinterpret_cast<const uint8_t*>(act_scale);
+        g.w_mx = reinterpret_cast<const uint8_t*>(L->w2_scale);
+        g.w_mx_expert = static_cast<int64_t>(L->D) * (L->I / 32);
+    }
     g.a_scale = act_scale;
     g.a_scale_ld = L->I / 128;
     g.sorted_ids = nullptr;
@@ -479,7 +560,7 @@ int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float
     g.counts = counts;
     g.w = static_cast<const uint8_t*>(L->w2);
     g.w_blocked = L->weight_layout == MOE_WEIGHTS_BLOCKED;
-    g.w_expert_bytes = static_cast<int64_t>(L->D) * L->I * elem;
+    g.w_expert_bytes = mx ? static_cast<int64_t>(L->D) * L->I / 2 : static_cast<int64_t>(L->D) * L->I * elem;
     g.w_scale = L->w2_scale;
     g.ws_expert = L->quant == MOE_QUANT_PTPC_FP8 ? static_cast<int64_t>(L->D)
                                                   : static_cast<int64_t>(L->D / 128) * (L->I / 128);

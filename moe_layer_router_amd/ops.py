@@ -305,7 +305,8 @@ class MoELayer:
         if self.quant == "mxfp4":
             out["xq"] = view("xq", T * D // 2, _U8, (T, D // 2))
             out["xs"] = view("xs", T * D // 32, _U8, (T, D // 32))
-            out["aq"] = view("aq", R * I // 2, _U8, (R, I // 2))
+            aq = view("aq", R * I // 2, _U8, (R, I // 2))
+            out["aq"] = unblock_weights(aq) if B == 16 else aq      # blocked for the streaming down GEMM
             out["as"] = view("as_", R * I // 32, _U8, (R, I // 32))
         elif self.quant != "bf16":
             out["xq"] = view("xq", T * D, _U8, (T, D))

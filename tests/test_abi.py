@@ -126,6 +126,7 @@ def test_layer_validation_and_workspace():
     assert lib.moe_default_block_m(ctypes.byref(_desc(E=128, top_k=8)), 256) == 16
     assert lib.moe_default_block_m(ctypes.byref(_desc(E=128, top_k=8)), 512) == 32
     assert lib.moe_default_block_m(ctypes.byref(_desc(quant=3, I=512, E=128, top_k=8)), 256) == 32
+    assert lib.moe_default_block_m(ctypes.byref(_desc(quant=3, I=512, E=128, top_k=8)), 32) == 16
     assert lib.moe_default_block_m(ctypes.byref(_desc(E=128, top_k=8)), 8192) == 256
     # about 143 rows per expert (the DeepSeek-R1-shaped batch): one 192-row tile; MXFP4 stays at 128
     r1 = dict(E=256, top_k=8, n_shared=1, scoring=1, n_groups=8, topk_groups=4)
