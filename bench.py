@@ -12,7 +12,8 @@ dominant kernel, and checks that both paths give the same bits.
 
 Prints ONE JSON line.  Default workload: the Qwen3-235B-A22B-shaped prefill
 layer (T=8192, D=4096, E=128, top-8, I=1536, PTPC-FP8).  Further legs of the
-same line time the decode batch (T=32) eagerly and from captured graphs, the
+same line time the decode batch (T=32; PTPC-FP8, and MXFP4 as
+``decode_mxfp4``) eagerly and from captured graphs, the
 other layer shapes (tiny bf16, Qwen3-30B-A3B-shaped, DeepSeek-R1-shaped with
 blockwise FP8, 512 experts top-10 plus a shared expert) and the
 expert-parallel payload kernels; ``cpu_baseline`` runs the CPU oracle over
@@ -280,13 +281,13 @@ def weight_copies(mlr, layer):
         for _ in range(ncopy - 1)]
 
 
-def time_decode(torch, mlr, synth, steps, warmup):
+def time_decode(torch, mlr, synth, steps, warmup, name="qwen3_235b_decode_ptpc"):
     """Decode layer (T=32, Zipf-skewed routing): full forward, weights rotated
     over copies so each step streams its experts from HBM.  Timed per call
     (median, p10, p90), eagerly and replayed from a captured HIP graph of the
     forwards over every weight copy (per-forward figures; the replayed output
     must equal the eager one)."""
-    w = synth.get("qwen3_235b_decode_ptpc")
+    w = synth.get(name)
     c = Case(mlr, synth, w, keep_masters=False)
     ncopy = 4
     layers = [c.layer]
@@ -625,6 +626,9 @@ def main():
     if not args.no_decode and w.name != "qwen3_235b_decode_ptpc":
         log("decode leg")
         out["decode"] = time_decode(torch, mlr, synth, max(args.steps, 100), args.warmup)
+        log("decode leg, MXFP4")
+        out["decode_mxfp4"] = time_decode(torch, mlr, synth, max(args.steps, 100), args.warmup,
+                                          name="qwen3_235b_decode_mxfp4")
     if not args.no_cpu_baseline:
         log("cpu baseline: the oracle over the whole batch")
         cb, ok, par = cpu_baseline(case, y_fused)

@@ -108,6 +108,9 @@ WORKLOADS = {
         Workload("deepseek_r1_mxfp4", 9, T=4096, D=7168, E=256, k=8, I=2048,
                  quant="mxfp4", scoring="sigmoid_grouped", n_groups=8,
                  topk_groups=4, route_scale=2.5, n_shared=1),
+        # the 32-token decode batch of the Qwen3-235B shape in MXFP4
+        Workload("qwen3_235b_decode_mxfp4", 10, T=32, D=4096, E=128, k=8, I=1536,
+                 quant="mxfp4", logit_recipe="zipf"),
     ]
 }
 
