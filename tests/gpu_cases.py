@@ -37,7 +37,8 @@ REDUCED = {
     "qwen3_235b_prefill_mxfp4_r": synth.get("qwen3_235b_prefill_mxfp4").replace(T=1000, D=1024, I=512, E=32),
     "deepseek_r1_mxfp4_r": synth.get("deepseek_r1_mxfp4").replace(T=300, D=1024, I=256, E=32),
     "deepseek_r1_mxfp4_small": synth.get("deepseek_r1_mxfp4").replace(T=40, D=1024, I=256, E=32),
-    "qwen3_235b_decode_mxfp4": synth.get("qwen3_235b_decode_ptpc").replace(quant="mxfp4"),
+    # the MXFP4 decode batch (T=32 over 128 experts: the weight-streaming launch of 32 rows per expert)
+    "qwen3_235b_decode_mxfp4_r": synth.get("qwen3_235b_decode_mxfp4").replace(D=1024, I=512),
     # the weight-streaming path's in-kernel permutation at its limits: 256
     # tokens, top-16 plus the shared expert (4352 rows) over 1023 + 1 experts
     "perm_limits_t256_k16": synth.get("e512_top10_shared_ptpc").replace(T=256, D=256, I=128, E=1023, k=16),

@@ -1,7 +1,8 @@
 """GPU parity of the MXFP4 (A4W4) path: the row quantizer for activations
 and weights bit-exact against the oracle (every bf16 value, zero blocks,
-both weight layouts), and moe_forward on reduced MXFP4 layers (and the
-Qwen3-235B decode shape) in every tile size and the weight-streaming path: routing, permutation and x codes bit-exact, act within 2e-3 relative
+both weight layouts), and moe_forward on reduced MXFP4 layers (among them
+a 32-token decode batch over 128 experts) in every tile size and the
+weight-streaming path: routing, permutation and x codes bit-exact, act within 2e-3 relative
 L2 on routed rows, act codes and scales the oracle's quantization of the
 GPU's act, out_perm against the oracle's down GEMM fed those codes, y within
 1e-2 (the quantized paths' bound)."""
@@ -79,7 +80,7 @@ def test_mx_weights(layout):
                                           ("deepseek_r1_mxfp4_r", 32), ("deepseek_r1_mxfp4_r", 128),
                                           ("qwen3_235b_prefill_mxfp4_r", 192), ("deepseek_r1_mxfp4_r", 192),
                                           ("deepseek_r1_mxfp4_small", 0), ("deepseek_r1_mxfp4_small", 16),
-                                          ("qwen3_235b_decode_mxfp4", 16), ("qwen3_235b_prefill_mxfp4_r", 16),
+                                          ("qwen3_235b_decode_mxfp4_r", 16), ("qwen3_235b_decode_mxfp4_r", 0), ("qwen3_235b_prefill_mxfp4_r", 16),
                                           ("deepseek_r1_mxfp4_r", 16)])
 def test_forward_mxfp4(name, block_m):
     w = REDUCED[name]
