@@ -418,6 +418,22 @@ int32_t moe_ep_pack_payload(const void* x_bf16, int32_t T, int32_t D, int32_t fo
 int32_t moe_ep_unpack_payload(const uint8_t* payload, int32_t T, int32_t D, int32_t format,
                               void* x_bf16, void* stream);
 
+/*
+ * Debug validation of a forward's inputs, for callers that switch it on
+ * (moe_forward never calls it; the Python binding does when MOE_VALIDATE=1).
+ * The forward takes such inputs without complaint: a routed id outside
+ * [0, E) gets no row (inv_perm -1), and Inf or NaN go through the
+ * arithmetic as IEEE values.  Writes, on the stream, counts[0] = elements of
+ * x_bf16 [T, D] that are Inf or NaN, counts[1] = the same for logits
+ * [T, E] fp32, counts[2] = ids [T, k] int32 outside [0, E).  Any of x_bf16,
+ * logits, ids may be NULL (its count is 0).  counts: device int32[3],
+ * zeroed by the call; read it once the stream has synchronized.  Errors:
+ * MOE_ERR_INVALID_ARG for counts NULL, T < 0, D <= 0 with x, E <= 0 with
+ * logits or ids, k <= 0 with ids.  Nothing traps: the kernels only count.
+ */
+int32_t moe_validate_inputs(const void* x_bf16, int32_t T, int32_t D, const float* logits, int32_t E,
+                            const int32_t* ids, int32_t k, int32_t* counts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,4 +8,4 @@ from ._lib import MoEError, lib  # noqa: F401
 from .ops import (LayerWeights, MoELayer, ep_pack, ep_payload_bytes, ep_unpack,  # noqa: F401
                   permute_align, permute_max_rows, quant_mxfp4, quant_ptpc_fp8, quant_weight_fp8,
                   quant_weight_mxfp4, route_topk,
-                  router_logits, unblock_weights, unpermute_combine)
+                  router_logits, unblock_weights, unpermute_combine, validate_inputs)

@@ -75,6 +75,8 @@ SIGNATURES = {
     "moe_ep_payload_bytes": (c_int64, [c_int32, c_int32]),
     "moe_ep_pack_payload": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "moe_ep_unpack_payload": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "moe_validate_inputs": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
+                                      c_void_p]),
 }
 
 _LIB = None

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import copy
 import ctypes
+import os
 from dataclasses import dataclass
 from typing import Optional
 
@@ -17,6 +18,11 @@ import torch
 from . import _lib as L
 
 _U8, _BF16, _F32, _I32 = torch.uint8, torch.bfloat16, torch.float32, torch.int32
+
+# MOE_VALIDATE=1 (read once, at import): MoELayer.forward first counts Inf
+# and NaN in x and the logits, and permute_align ids outside [0, E), on the
+# GPU (moe_validate_inputs), and raises ValueError if there are any.
+VALIDATE = os.environ.get("MOE_VALIDATE", "") == "1"
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -43,6 +49,27 @@ def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
 
 
 # ---------------------------------------------------------------- step entries
+
+def validate_inputs(x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                    ids: Optional[torch.Tensor] = None, E: Optional[int] = None) -> dict:
+    """Counts of Inf/NaN in x [T, D] bf16 and logits [T, E] fp32 and of ids
+    [T, k] int32 outside [0, E), taken on the GPU (waits for the stream)."""
+    ref = next(t for t in (x, logits, ids) if t is not None)
+    T = ref.shape[0]
+    E = logits.shape[1] if E is None and logits is not None else E
+    if x is not None:
+        _need(x, _BF16, "x", (T, x.shape[1]))
+    if logits is not None:
+        _need(logits, _F32, "logits", (T, E))
+    if ids is not None:
+        _need(ids, _I32, "ids", (T, ids.shape[1]))
+    counts = _empty((3,), _I32, ref)
+    L.check("moe_validate_inputs", L.lib().moe_validate_inputs(
+        _ptr(x), T, 0 if x is None else x.shape[1], _ptr(logits), E or 0, _ptr(ids), 0 if ids is None else ids.shape[1],
+        _ptr(counts), _stream()))
+    c = counts.tolist()
+    return {"x_nonfinite": c[0], "logits_nonfinite": c[1], "ids_out_of_range": c[2]}
+
 
 def router_logits(x: torch.Tensor, router_w: torch.Tensor) -> torch.Tensor:
     T, D = x.shape
@@ -76,6 +103,10 @@ def permute_max_rows(T: int, k: int, E: int, n_shared: int, block_m: int) -> int
 
 def permute_align(ids: torch.Tensor, E: int, n_shared: int, block_m: int) -> dict:
     T, k = ids.shape
+    if VALIDATE and T > 0:
+        bad = validate_inputs(ids=ids, E=E)
+        if bad["ids_out_of_range"]:
+            raise ValueError(f"MOE_VALIDATE: routed ids outside [0, {E}): {bad['ids_out_of_range']}")
     _need(ids, _I32, "topk_ids")
     R = permute_max_rows(T, k, E, n_shared, block_m)
     Ep = E + n_shared
@@ -273,6 +304,10 @@ class MoELayer:
         _need(x, _BF16, "x", (T, self.D))
         if logits is not None:
             _need(logits, _F32, "logits", (T, self.E))
+        if VALIDATE and T > 0:
+            bad = validate_inputs(x, logits, E=self.E)
+            if bad["x_nonfinite"] or bad["logits_nonfinite"]:
+                raise ValueError(f"MOE_VALIDATE: non-finite forward inputs {bad}")
         if y is None:
             y = _empty((T, self.D), _BF16, x)
         ws = workspace if workspace is not None else self.workspace(T, block_m, x.device)

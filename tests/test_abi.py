@@ -82,6 +82,14 @@ def test_validation_happens_before_any_launch():
     assert lib.moe_unpermute_combine(None, 1, None, None, 4, 16, 1, 256, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_unpermute_combine(None, 1, None, None, 4, 17, 0, 256, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_unpermute_combine(None, 1, None, None, 0, 17, 1, 256, None, None) == L.MOE_ERR_UNSUPPORTED
+    # input validation: argument errors come back before its kernels are enqueued
+    fake = ctypes.c_void_p(256)      # never dereferenced: every call below is refused first
+    assert lib.moe_validate_inputs(None, 4, 256, None, 8, None, 2, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_validate_inputs(None, -1, 256, None, 8, None, 2, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_validate_inputs(fake, 4, 0, None, 8, None, 2, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_validate_inputs(None, 4, 256, fake, 0, None, 2, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_validate_inputs(None, 4, 256, None, 0, fake, 2, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_validate_inputs(None, 4, 256, None, 8, fake, 0, fake, None) == L.MOE_ERR_INVALID_ARG
 
 
 def test_gemm_byte_ranges_are_checked_before_any_launch():
