@@ -15,8 +15,9 @@ layer (T=8192, D=4096, E=128, top-8, I=1536, PTPC-FP8).  Further legs of the
 same line time the decode batch (T=32; PTPC-FP8, and MXFP4 as
 ``decode_mxfp4``) eagerly and from captured graphs, the
 other layer shapes (tiny bf16, Qwen3-30B-A3B-shaped, DeepSeek-R1-shaped with
-blockwise FP8, 512 experts top-10 plus a shared expert) and the
-expert-parallel payload kernels; ``cpu_baseline`` runs the CPU oracle over
+blockwise FP8, 512 experts top-10 plus a shared expert, the Qwen3-235B and
+DeepSeek-R1 shapes in MXFP4, the Qwen3-235B prefill routed by its own router
+gate) and the expert-parallel payload kernels; ``cpu_baseline`` runs the CPU oracle over
 the whole default batch once, on the host's cores, and its output gates the
 GPU number on every token.
 """
