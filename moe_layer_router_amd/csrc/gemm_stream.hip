@@ -417,10 +417,12 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
 // steps in flight per wave.  In the PTPC mode both GEMMs stream 4 tiles per
 // wave (one wave per SIMD): Qwen3-235B decode step 165.9 -> 163.8 us with 4
 // gate/up tiles instead of 2, then 162.9 -> 161.8 us with 4 down tiles.  The
-// blockwise mode keeps 2 (its per-step scales would not fit the registers);
-// MXFP4 streams 4 up to 32 rows per launch tile set and 2 beyond (its scale
-// dwords and two-piece operands spill at 4 tiles with 64 rows), and so does bf16 (4 tiles halve its waves; the 64-token bf16 layer went
-// from 0.028 to 0.032 ms).  One tile
+// blockwise mode keeps 2 (its per-step scales would not fit the registers),
+// and so does bf16 (4 tiles halve its waves; the 64-token bf16 layer went
+// from 0.028 to 0.032 ms).  MXFP4 streams 4 tiles while a launch carries up
+// to 32 rows per expert at a time (Qwen3-235B decode shape 120.3 -> 114.7
+// us against 2 tiles) and 2 with 64 rows, where its scale dwords and
+// two-piece operands would spill at 4.  One tile
 // per wave for down spread its items more evenly over the waves but halved
 // the bytes each wave keeps in flight, and measured slower (178 -> 196 us);
 // so did splitting only the items of the last, partial round (177 ->
