@@ -14,7 +14,7 @@ import torch
 import oracle as O
 import synth
 from tests.gpu_cases import (REDUCED, build_case, dequant_act, pack_nibbles, quant_act_ref, rel_l2, say,
-                             tol_of)
+                             tol_of, zero_pad_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +118,48 @@ def test_forward_mxfp4(name, block_m):
     err = rel_l2(y.float().cpu().numpy(), ref["y"])
     say("y rel_l2", err)
     assert err <= tol_of(w.quant)
+
+
+@pytest.mark.parametrize("name,block_m", [("deepseek_r1_mxfp4_small", 16), ("deepseek_r1_mxfp4_small", 32),
+                                          ("qwen3_235b_decode_mxfp4_r", 16)])
+def test_mxfp4_step_entries(name, block_m):
+    """The gate/up and down step entries on MXFP4 codes from the library's
+    row quantizer (the row-major act codes the public down entry takes; the
+    fused forward hands the streaming down GEMM blocked ones): act against
+    the oracle's act, the act codes the oracle's quantization of it, out_perm
+    against the oracle's down GEMM fed those codes, pad rows written 0."""
+    w = REDUCED[name]
+    say("mxfp4 step entries", name, block_m)
+    c = build_case(w)
+    ids, _ = (mlr.route_topk(c.logits, w.k) if w.scoring == "softmax" else
+              mlr.route_topk(c.logits, w.k, w.scoring, w.n_groups, w.topk_groups, None, True, w.route_scale))
+    perm = mlr.permute_align(ids, w.E, w.n_shared, block_m)
+    xq, xs = mlr.quant_mxfp4(c.x)
+    act = c.layer.gateup_silu(xq, xs, w.T, block_m, perm)
+    torch.cuda.synchronize()
+    ref = O.moe_forward(c.spec, c.bank, c.x_np(), c.logits_np(), block_m=block_m)
+    total = int(perm["offsets"][-1].item())
+    real = perm["sorted_ids"][:total].cpu().numpy() != w.T * (w.k + w.n_shared)
+    got = act[:total].float().cpu().numpy()
+    assert rel_l2(got[real], ref["act"][:total][real]) < 2e-3
+    assert np.all(got[zero_pad_rows(perm, block_m)] == 0)
+
+    aq, sc = mlr.quant_mxfp4(act)
+    out = c.layer.down(aq, sc, w.T, block_m, perm)
+    torch.cuda.synchronize()
+    aq_np, sc_np, out_np = aq.cpu().numpy(), sc.cpu().numpy(), out.float().cpu().numpy()
+    q, s = quant_act_ref("mxfp4", got[real])
+    assert np.array_equal(aq_np[:total][real], q) and np.array_equal(sc_np[:total][real], s)
+    offs, cnts = perm["offsets"].cpu().numpy(), perm["counts"].cpu().numpy()
+    pairs = []
+    for e in range(w.E + w.n_shared):
+        lo, hi = int(offs[e]), int(offs[e]) + int(cnts[e])
+        if hi > lo:
+            a_in = dequant_act("mxfp4", aq_np[lo:hi], sc_np[lo:hi])
+            pairs.append((out_np[lo:hi], O.expert_down(a_in, c.bank.dequantized(e)[1], True)))
+    assert rel_l2(np.concatenate([g for g, _ in pairs]), np.concatenate([r for _, r in pairs])) < 2e-3
+    zp = zero_pad_rows(perm, block_m)
+    assert np.all(out_np[:len(zp)][zp] == 0)
 
 
 def test_mxfp4_rejects_256_row_tiles():
