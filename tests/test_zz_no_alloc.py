@@ -36,7 +36,7 @@ def _noalloc(layer, x, logits, block_m, y):
                                              ("deepseek_r1_block_fp8_small", 0, 3),
                                              ("qwen3_235b_prefill_ptpc_r", 0, 101),
                                              ("deepseek_r1_block_fp8_r", 128, 77),
-                                             ("e512_top10_shared_r", 16, 9)])
+                                             ("e512_top10_shared_r", 16, 9), ("qwen3_235b_decode_mxfp4_r", 0, 7)])
 def test_noalloc_equals_moe_forward(name, block_m, T2):
     w = REDUCED[name]
     say("noalloc", name, block_m, T2)
