@@ -429,9 +429,21 @@ __global__ void __launch_bounds__(256) stream_gemm_kernel(const StreamArgs p) {
 // 181 us): the waves share HBM bandwidth, and the few that run a last round
 // get more of it.  3 or 6 steps in flight instead of 4 were slower (167.4,
 // 167.3 against 165.9 us).
-template <int MODE, bool GATEUP, int MT>
-constexpr int stream_tn() { return MODE == MOE_QUANT_PTPC_FP8 || (MODE == MOE_QUANT_MXFP4 && MT <= 2) ? 4 : 2; }
-constexpr int kStreamPF = 4;
+template <int MODE, bool GATEUP, int MT, bool WIDE>
+constexpr int stream_tn() {
+    return WIDE ? 8 : MODE == MOE_QUANT_PTPC_FP8 || (MODE == MOE_QUANT_MXFP4 && MT <= 2) ? 4 : 2;
+}
+// K steps in flight.  WIDE (the PTPC down GEMM of batches above 32 tokens
+// that route at least 8 rows per expert on average) streams 8 tiles with 2
+// steps in flight: the same bytes in flight per wave as 4 tiles with 4, in
+// items of twice the bytes (the down GEMM's K is I, a few steps, so an
+// item's start latency weighs heavily) and half as many.  Qwen3-30B-A3B-
+// shaped layer (128 active experts, 16 rows each): down GEMM 49.2 -> 46.3
+// us.  Decode batches with few active experts get too few items for the
+// waves: 32 / 64 tokens over 38 / 44 experts measured 156.9 -> 158.0 and
+// 186.7 -> 189.2 us, so they keep 4 tiles.
+template <int MODE, bool GATEUP, int MT, bool WIDE>
+constexpr int stream_pf() { return WIDE ? 2 : 4; }
 
 // Workgroups of a kernel that fit on the device at once, per device (CACHE:
 // one per kernel instantiation).
@@ -450,12 +462,12 @@ static int resident_blocks(Kern kernel, int (&cache)[64]) {
     return n;
 }
 
-template <int MODE, bool GATEUP, int MT>
+template <int MODE, bool GATEUP, int MT, bool WIDE = false>
 static int32_t stream_launch_mt(StreamArgs a, int ncols, hipStream_t s) {
-    constexpr int TN = stream_tn<MODE, GATEUP, MT>();
+    constexpr int TN = stream_tn<MODE, GATEUP, MT, WIDE>();
     constexpr int COLS_W = GATEUP ? TN / 2 * 16 : TN * 16;   // output columns per item
     a.nslice = ncols / COLS_W;
-    auto kern = stream_gemm_kernel<MODE, GATEUP, TN, MT, kStreamPF>;
+    auto kern = stream_gemm_kernel<MODE, GATEUP, TN, MT, stream_pf<MODE, GATEUP, MT, WIDE>()>;
     static int cache[64];
     // no more workgroups than items could need (E' experts x slices / 4 waves)
     const int wgs = min(resident_blocks(kern, cache),
@@ -465,20 +477,23 @@ static int32_t stream_launch_mt(StreamArgs a, int ncols, hipStream_t s) {
 }
 
 template <int MODE, bool GATEUP>
-static int32_t stream_launch_mode(StreamArgs a, int Ep, int ncols, int T, hipStream_t s) {
+static int32_t stream_launch_mode(StreamArgs a, int Ep, int ncols, int T, bool wide, hipStream_t s) {
     a.n_exp = Ep;
     if (T <= 16) return stream_launch_mt<MODE, GATEUP, 1>(a, ncols, s);
     if (T <= 32) return stream_launch_mt<MODE, GATEUP, 2>(a, ncols, s);
+    if constexpr (MODE == MOE_QUANT_PTPC_FP8 && !GATEUP)
+        if (wide) return stream_launch_mt<MODE, GATEUP, 4, true>(a, ncols, s);
     return stream_launch_mt<MODE, GATEUP, 4>(a, ncols, s);
 }
 
 template <bool GATEUP>
-static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, int T, hipStream_t s) {
+static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, int T, hipStream_t s,
+                             bool wide = false) {
     switch (quant) {
-        case MOE_QUANT_NONE_BF16: return stream_launch_mode<MOE_QUANT_NONE_BF16, GATEUP>(a, Ep, ncols, T, s);
-        case MOE_QUANT_PTPC_FP8: return stream_launch_mode<MOE_QUANT_PTPC_FP8, GATEUP>(a, Ep, ncols, T, s);
-        case MOE_QUANT_BLOCK128_FP8: return stream_launch_mode<MOE_QUANT_BLOCK128_FP8, GATEUP>(a, Ep, ncols, T, s);
-        case MOE_QUANT_MXFP4: return stream_launch_mode<MOE_QUANT_MXFP4, GATEUP>(a, Ep, ncols, T, s);
+        case MOE_QUANT_NONE_BF16: return stream_launch_mode<MOE_QUANT_NONE_BF16, GATEUP>(a, Ep, ncols, T, wide, s);
+        case MOE_QUANT_PTPC_FP8: return stream_launch_mode<MOE_QUANT_PTPC_FP8, GATEUP>(a, Ep, ncols, T, wide, s);
+        case MOE_QUANT_BLOCK128_FP8: return stream_launch_mode<MOE_QUANT_BLOCK128_FP8, GATEUP>(a, Ep, ncols, T, wide, s);
+        case MOE_QUANT_MXFP4: return stream_launch_mode<MOE_QUANT_MXFP4, GATEUP>(a, Ep, ncols, T, wide, s);
     }
     return MOE_ERR_UNSUPPORTED;
 }
@@ -571,7 +586,9 @@ int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float
     g.I = L->I;
     g.out = out_perm;
     g.out_ld = L->D;
-    return stream_launch<false>(L->quant, g, L->E + L->n_shared, L->D, T, s);
+    // at least 8 routed rows per expert on average: most experts are active
+    const bool wide = static_cast<int64_t>(T) * L->top_k >= 8LL * (L->E + L->n_shared);
+    return stream_launch<false>(L->quant, g, L->E + L->n_shared, L->D, T, s, wide);
 }
 
 }  // namespace moe
