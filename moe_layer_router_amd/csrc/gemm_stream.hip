@@ -433,15 +433,15 @@ template <int MODE, bool GATEUP, int MT, bool WIDE>
 constexpr int stream_tn() {
     return WIDE ? 8 : MODE == MOE_QUANT_PTPC_FP8 || (MODE == MOE_QUANT_MXFP4 && MT <= 2) ? 4 : 2;
 }
-// K steps in flight.  WIDE (the PTPC down GEMM of batches above 32 tokens
-// that route at least 8 rows per expert on average) streams 8 tiles with 2
-// steps in flight: the same bytes in flight per wave as 4 tiles with 4, in
-// items of twice the bytes (the down GEMM's K is I, a few steps, so an
-// item's start latency weighs heavily) and half as many.  Qwen3-30B-A3B-
-// shaped layer (128 active experts, 16 rows each): down GEMM 49.2 -> 46.3
-// us.  Decode batches with few active experts get too few items for the
-// waves: 32 / 64 tokens over 38 / 44 experts measured 156.9 -> 158.0 and
-// 186.7 -> 189.2 us, so they keep 4 tiles.
+// K steps in flight.  WIDE (the PTPC GEMMs of batches above 32 tokens that
+// route at least 8 rows per expert on average) streams 8 tiles with 2 steps
+// in flight: the same bytes in flight per wave as 4 tiles with 4, in items
+// of twice the bytes and half as many, so each item's start latency is paid
+// half as often.  Qwen3-30B-A3B-shaped layer (128 active experts, 16 rows
+// each): down GEMM 49.2 -> 46.3 us, then gate/up 83.6 -> 80.2 us.  Decode
+// batches with few active experts get too few items for the waves: the
+// down GEMM at 32 / 64 tokens over 38 / 44 experts measured 156.9 -> 158.0
+// and 186.7 -> 189.2 us, so they keep 4 tiles.
 template <int MODE, bool GATEUP, int MT, bool WIDE>
 constexpr int stream_pf() { return WIDE ? 2 : 4; }
 
@@ -481,7 +481,7 @@ static int32_t stream_launch_mode(StreamArgs a, int Ep, int ncols, int T, bool w
     a.n_exp = Ep;
     if (T <= 16) return stream_launch_mt<MODE, GATEUP, 1>(a, ncols, s);
     if (T <= 32) return stream_launch_mt<MODE, GATEUP, 2>(a, ncols, s);
-    if constexpr (MODE == MOE_QUANT_PTPC_FP8 && !GATEUP)
+    if constexpr (MODE == MOE_QUANT_PTPC_FP8)
         if (wide) return stream_launch_mt<MODE, GATEUP, 4, true>(a, ncols, s);
     return stream_launch_mt<MODE, GATEUP, 4>(a, ncols, s);
 }
@@ -498,6 +498,13 @@ static int32_t stream_launch(int quant, const StreamArgs& a, int Ep, int ncols, 
     return MOE_ERR_UNSUPPORTED;
 }
 
+
+// The wide items (8 tiles, 2 steps in flight) for PTPC batches that route
+// at least 8 rows per expert on average: most experts are active, so the
+// items still fill the waves.
+static bool stream_wide(const moe_layer_desc* L, int T) {
+    return static_cast<int64_t>(T) * L->top_k >= 8LL * (L->E + L->n_shared);
+}
 
 // The gate/up arguments every variant shares.
 static StreamArgs gateup_args(const moe_layer_desc* L, const void* a, const float* a_scale, int T, void* act) {
@@ -537,7 +544,7 @@ int32_t stream_gateup_launch(const moe_layer_desc* L, const void* a, const float
     g.sorted_ids = sorted_ids;
     g.offsets = offsets;
     g.counts = counts;
-    return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s);
+    return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s, stream_wide(L, T));
 }
 
 // gate_up from the routed ids (T <= 256, k picks per token distinct): the
@@ -552,7 +559,7 @@ int32_t stream_gateup_fused_launch(const moe_layer_desc* L, const void* a, const
     g.n_shared = L->n_shared;
     g.max_rows = max_rows;
     g.pout = pout;
-    return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s);
+    return stream_launch<true>(L->quant, g, L->E + L->n_shared, L->I, T, s, stream_wide(L, T));
 }
 
 bool stream_fused_perm_ok(int T) { return T >= 1 && T <= 32 * kStreamPermMW; }
@@ -586,9 +593,7 @@ int32_t stream_down_launch(const moe_layer_desc* L, const void* act, const float
     g.I = L->I;
     g.out = out_perm;
     g.out_ld = L->D;
-    // at least 8 routed rows per expert on average: most experts are active
-    const bool wide = static_cast<int64_t>(T) * L->top_k >= 8LL * (L->E + L->n_shared);
-    return stream_launch<false>(L->quant, g, L->E + L->n_shared, L->D, T, s, wide);
+    return stream_launch<false>(L->quant, g, L->E + L->n_shared, L->D, T, s, stream_wide(L, T));
 }
 
 }  // namespace moe
