@@ -15,9 +15,8 @@ struct alignas(16) f32x4 { float v[4]; };
 // OUT_BF16: out_perm rows are bf16 (else fp32).  Workgroup (t, y) owns
 // columns [2048 y, 2048 y + 2048) of token t, 8 per thread.  The row indices
 // and weights come first (uniform per workgroup), then the token's
-// k + n_shared row loads are issued, up to 9 before any is consumed (the
-// kernel is bound by memory latency and bandwidth, not arithmetic).
-// NR >= k + n_shared.
+// k + n_shared rows are loaded a few at a time (the kernel is bound by
+// memory latency and bandwidth, not arithmetic).  NR >= k + n_shared.
 template <bool OUT_BF16, int NR>
 __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ out_perm,
                                                       const int* __restrict__ inv_perm,
@@ -38,11 +37,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ o
         }
     }
     if (c >= (D >> 3)) return;
-    // Rows are loaded BATCH at a time (all of them up to 9 rows; in batches
-    // of 6 above, for registers and so waves per SIMD) and summed in index
-    // order: j = 0 .. k-1 weighted (fused multiply-add), then the shared row,
-    // the same order whatever the batch.
-    constexpr int BATCH = NR <= 9 ? NR : 6;
+    // Rows are loaded BATCH at a time and summed in index order: j = 0 ..
+    // k-1 weighted (fused multiply-add), then the shared row, the same order
+    // whatever the batch.  Small batches keep few registers (52-60 VGPRs, 8
+    // waves per SIMD): with every row of a 9-row token in flight at once (90
+    // VGPRs, 5 waves) the Qwen3-235B-shaped prefill combine took ~10 us more,
+    // and batches of 6 for the 12-row one (76 VGPRs, 6 waves) ~6 us more on
+    // the 512-expert layer than batches of 3 and 4.
+    constexpr int BATCH = NR <= 9 ? 3 : 4;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
